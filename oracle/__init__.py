@@ -1,0 +1,207 @@
+"""any4 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+numpy-level wrappers around ``liboracle.so`` (plain C, see ``any4_oracle.c``).
+Only the test suite, ``__graft_entry__.smoke()`` and the benchmark's CPU
+baseline leg may import this package; the product path (``gemm_any4_amd``)
+never does.
+
+All bf16 data is passed as ``uint16`` bit patterns.  Layouts are dense
+row-major: idx ``[N, K]`` u8, packed ``[N, K/2]`` u8 (byte j holds index 2j in
+bits 0..3 and 2j+1 in bits 4..7), lut ``[N, 16]``, alpha/beta ``[N, K/g]``,
+x ``[M, K]``, w ``[N, K]``.
+
+What each function follows (the pages, by title and section):
+  * the 10100.com any4 explainer, section 二: a row is 4-bit indices plus a
+    16-entry bf16 table; step 1 "分组缩放": contiguous groups of g with a scale
+    alpha and an offset beta; step 2 "E-Step"/"M-Step": weighted k-means with
+    L_q = sum(alpha*w_s*E|x|) / sum(alpha*E|x|);
+  * "any4: Learned 4-bit Numeric Representation for LLMs", abstract: the
+    lookup-table matmul.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.orc_bf16_to_f32.restype = ctypes.c_float
+        lib.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.orc_f32_to_bf16.restype = ctypes.c_uint16
+        lib.orc_f32_to_bf16.argtypes = [ctypes.c_float]
+        lib.orc_f64_to_bf16.restype = ctypes.c_uint16
+        lib.orc_f64_to_bf16.argtypes = [ctypes.c_double]
+        lib.orc_f32_to_bf16_array.restype = None
+        lib.orc_f32_to_bf16_array.argtypes = [P, P, I64]
+        lib.orc_pack.restype = None
+        lib.orc_pack.argtypes = [P, P, I64, I64]
+        lib.orc_unpack.restype = None
+        lib.orc_unpack.argtypes = [P, P, I64, I64]
+        lib.orc_dequant_one.restype = ctypes.c_uint16
+        lib.orc_dequant_one.argtypes = [ctypes.c_uint16] * 3
+        lib.orc_dequant.restype = None
+        lib.orc_dequant.argtypes = [P, P, P, P, P, I64, I64, I64]
+        lib.orc_gemm.restype = None
+        lib.orc_gemm.argtypes = [P, P, P, P, I64, I64, I64, ctypes.c_int]
+        lib.orc_group_scale.restype = None
+        lib.orc_group_scale.argtypes = [P, I64, I64, I64, P, P]
+        lib.orc_kmeans_row.restype = None
+        lib.orc_kmeans_row.argtypes = [P, P, I64, ctypes.c_int, P, P, P]
+        lib.orc_kmeans_quantize.restype = ctypes.c_int
+        lib.orc_kmeans_quantize.argtypes = [P, P, I64, I64, I64, ctypes.c_int, P, P, P, P,
+                                            ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def default_threads() -> int:
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+# --------------------------------------------------------------------------
+# bf16 helpers
+# --------------------------------------------------------------------------
+def bf16_to_f32(h) -> np.ndarray:
+    """Exact widening: bf16 bits are the upper half of the binary32 bits."""
+    h = _c(h, np.uint16)
+    return (h.astype(np.uint32) << 16).view(np.float32)
+
+
+def f32_to_bf16(f) -> np.ndarray:
+    """binary32 -> bf16 bits, round to nearest even (oracle's own C routine)."""
+    f = _c(f, np.float32)
+    out = np.empty(f.shape, np.uint16)
+    _load().orc_f32_to_bf16_array(_ptr(f), _ptr(out), f.size)
+    return out
+
+
+def f64_to_bf16_scalar(d: float) -> int:
+    """binary64 -> bf16 bits with one rounding to nearest even."""
+    return int(_load().orc_f64_to_bf16(float(d)))
+
+
+# --------------------------------------------------------------------------
+# pack / dequant / gemm
+# --------------------------------------------------------------------------
+def pack(idx) -> np.ndarray:
+    idx = _c(idx, np.uint8)
+    N, K = idx.shape
+    assert K % 2 == 0
+    out = np.empty((N, K // 2), np.uint8)
+    _load().orc_pack(_ptr(idx), _ptr(out), N, K)
+    return out
+
+
+def unpack(packed, K: int) -> np.ndarray:
+    packed = _c(packed, np.uint8)
+    N = packed.shape[0]
+    out = np.empty((N, K), np.uint8)
+    _load().orc_unpack(_ptr(packed), _ptr(out), N, K)
+    return out
+
+
+def dequant_one(alpha: int, lut_value: int, beta: int) -> int:
+    return int(_load().orc_dequant_one(alpha, lut_value, beta))
+
+
+def dequant(packed, lut, alpha, beta, g: int) -> np.ndarray:
+    """w[n][k] = bf16(fp32(alpha*LUT[n][idx] + beta)) as bf16 bits [N, K]."""
+    packed = _c(packed, np.uint8)
+    lut = _c(lut, np.uint16)
+    alpha = _c(alpha, np.uint16)
+    beta = _c(beta, np.uint16)
+    N = packed.shape[0]
+    K = packed.shape[1] * 2
+    assert lut.shape == (N, 16)
+    assert K % g == 0 and alpha.shape == (N, K // g) and beta.shape == (N, K // g)
+    w = np.empty((N, K), np.uint16)
+    _load().orc_dequant(_ptr(packed), _ptr(lut), _ptr(alpha), _ptr(beta), _ptr(w), N, K, g)
+    return w
+
+
+def gemm(x, w, nthreads: int = 1):
+    """fp64 reference y[m][n] = sum_k x[m][k]*w[n][k] and sum_k |x*w|.
+
+    x: bf16 bits [M, K]; w: bf16 bits [N, K] (the dequantised weights).
+    Returns (y_ref, absdot), both float64 [M, N]."""
+    x = _c(x, np.uint16)
+    w = _c(w, np.uint16)
+    M, K = x.shape
+    N = w.shape[0]
+    assert w.shape[1] == K
+    y = np.empty((M, N), np.float64)
+    a = np.empty((M, N), np.float64)
+    _load().orc_gemm(_ptr(x), _ptr(w), _ptr(y), _ptr(a), M, N, K, nthreads)
+    return y, a
+
+
+def tolerance(absdot: np.ndarray) -> np.ndarray:
+    """Per-element GEMM bound |y - y_ref| <= 2e-3 * sum_k |x_k w_k| + 1e-3."""
+    return 2e-3 * absdot + 1e-3
+
+
+# --------------------------------------------------------------------------
+# quantiser
+# --------------------------------------------------------------------------
+def group_scale(W, g: int):
+    W = _c(W, np.float64)
+    N, K = W.shape
+    a = np.empty((N, K // g), np.uint16)
+    b = np.empty((N, K // g), np.uint16)
+    _load().orc_group_scale(_ptr(W), N, K, g, _ptr(a), _ptr(b))
+    return a, b
+
+
+def kmeans_row(ws, wt, iters: int, init=None, trace: bool = False):
+    """Weighted k-means of one row in the normalised domain (fp64).
+
+    Returns (L[16] fp64, idx[K] u8) or (L, idx, trace[2*iters])."""
+    ws = _c(ws, np.float64)
+    wt = _c(wt, np.float64)
+    K = ws.size
+    L = _c(np.arange(16) if init is None else init, np.float64).copy()
+    idx = np.empty(K, np.uint8)
+    tr = np.empty(max(1, 2 * iters), np.float64)
+    _load().orc_kmeans_row(_ptr(ws), _ptr(wt), K, iters, _ptr(L), _ptr(idx),
+                           _ptr(tr) if trace else None)
+    if trace:
+        return L, idx, tr[: 2 * iters]
+    return L, idx
+
+
+def kmeans_quantize(W, Ex, g: int, iters: int = 10, nthreads: int | None = None):
+    """any4-quantise W[N, K] (fp64) with channel importance Ex[K] = E|x|.
+
+    Returns (idx u8 [N, K], lut bf16 bits [N, 16], alpha, beta bf16 bits [N, K/g])."""
+    W = _c(W, np.float64)
+    Ex = _c(Ex, np.float64)
+    N, K = W.shape
+    assert Ex.shape == (K,) and K % g == 0
+    idx = np.empty((N, K), np.uint8)
+    lut = np.empty((N, 16), np.uint16)
+    a = np.empty((N, K // g), np.uint16)
+    b = np.empty((N, K // g), np.uint16)
+    rc = _load().orc_kmeans_quantize(_ptr(W), _ptr(Ex), N, K, g, iters, _ptr(idx), _ptr(lut),
+                                     _ptr(a), _ptr(b), nthreads or default_threads())
+    if rc != 0:
+        raise MemoryError("oracle quantiser could not allocate its row buffers")
+    return idx, lut, a, b
