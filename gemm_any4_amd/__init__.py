@@ -1,0 +1,196 @@
+"""Python binding of libany4.so, the MI355X any4 dequantize-GEMM.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+in ``include/any4.h``.  PyTorch provides device memory and the current HIP
+stream.  There is no CPU fallback: if the library is missing or a call fails,
+a ``RuntimeError`` is raised.
+
+Tensors
+  idx     uint8  [N, K]     values 0..15
+  packed  uint8  [N, K/2]   byte j: index 2j in bits 0..3, 2j+1 in bits 4..7
+  lut     bf16   [N, 16]    per-row table
+  alpha   bf16   [N, K/g]   per-group scale
+  beta    bf16   [N, K/g]   per-group offset
+  x       bf16   [M, K]     M = 1..16
+  y       bf16   [M, N]
+  w       bf16   [N, K]
+(bf16 tensors may also be given as int16/uint16 bit patterns.)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libany4.so")
+
+ANY4_OK = 0
+_STATUS_NAMES = {0: "ANY4_OK", 1: "ANY4_E_NULL", 2: "ANY4_E_SHAPE", 3: "ANY4_E_ALIGN",
+                 4: "ANY4_E_WORKSPACE", 5: "ANY4_E_HIP"}
+
+# every symbol include/any4.h declares
+EXPORTS = ("any4_pack", "any4_dequant", "any4_gemm_workspace_size", "any4_gemm",
+           "any4_status_string")
+
+_lib = None
+
+
+class Any4Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libany4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "or python -m gemm_any4_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        L.any4_pack.restype = ctypes.c_int
+        L.any4_pack.argtypes = [P, P, I64, I64, P]
+        L.any4_dequant.restype = ctypes.c_int
+        L.any4_dequant.argtypes = [P, P, P, P, P, I64, I64, I64, P]
+        L.any4_gemm_workspace_size.restype = SZ
+        L.any4_gemm_workspace_size.argtypes = [I64, I64, I64, I64]
+        L.any4_gemm.restype = ctypes.c_int
+        L.any4_gemm.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P, SZ, P]
+        L.any4_status_string.restype = ctypes.c_char_p
+        L.any4_status_string.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().any4_status_string(s).decode()
+
+
+def check(s: int) -> None:
+    if s != ANY4_OK:
+        raise Any4Error(s, status_string(s))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None or t.numel() == 0:
+        return None
+    return t.data_ptr()
+
+
+def _u8(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must be uint8, got {t.dtype}")
+    return _dev(t, name)
+
+
+def _b16(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must be bfloat16 (or 16-bit bit patterns), got {t.dtype}")
+    return _dev(t, name)
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+# --------------------------------------------------------------------------
+# raw C-ABI calls (device pointers as ints)
+# --------------------------------------------------------------------------
+def pack_raw(idx_ptr, packed_ptr, N, K, stream=None) -> int:
+    return lib().any4_pack(idx_ptr, packed_ptr, N, K, _stream(stream))
+
+
+def dequant_raw(packed_ptr, lut_ptr, alpha_ptr, beta_ptr, w_ptr, N, K, g, stream=None) -> int:
+    return lib().any4_dequant(packed_ptr, lut_ptr, alpha_ptr, beta_ptr, w_ptr, N, K, g,
+                              _stream(stream))
+
+
+def workspace_size(M: int, N: int, K: int, g: int) -> int:
+    return int(lib().any4_gemm_workspace_size(M, N, K, g))
+
+
+def gemm_raw(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
+             ws_ptr=None, ws_bytes=0, stream=None) -> int:
+    return lib().any4_gemm(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
+                           ws_ptr, ws_bytes, _stream(stream))
+
+
+# --------------------------------------------------------------------------
+# tensor API
+# --------------------------------------------------------------------------
+def pack(idx: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """idx uint8 [N, K] -> packed uint8 [N, K/2]."""
+    _u8(idx, "idx")
+    N, K = idx.shape
+    if out is None:
+        out = torch.empty((N, K // 2), dtype=torch.uint8, device=idx.device)
+    _u8(out, "packed")
+    if out.shape != (N, K // 2):
+        raise ValueError("packed must be [N, K/2]")
+    check(pack_raw(_ptr(idx), _ptr(out), N, K, stream))
+    return out
+
+
+def dequant(packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+            g: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Materialise the bf16 weights w [N, K]."""
+    _u8(packed, "packed")
+    _b16(lut, "lut"), _b16(alpha, "alpha"), _b16(beta, "beta")
+    N, K2 = packed.shape
+    K = 2 * K2
+    if lut.shape != (N, 16):
+        raise ValueError("lut must be [N, 16]")
+    if g <= 0 or K % g or alpha.shape != (N, K // g) or beta.shape != (N, K // g):
+        raise ValueError("alpha/beta must be [N, K/g]")
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=packed.device)
+    _b16(out, "w")
+    if out.shape != (N, K):
+        raise ValueError("w must be [N, K]")
+    check(dequant_raw(_ptr(packed), _ptr(lut), _ptr(alpha), _ptr(beta), _ptr(out), N, K, g,
+                      stream))
+    return out
+
+
+def gemm(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor,
+         beta: torch.Tensor, g: int, out: torch.Tensor | None = None,
+         workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y [M, N] = x [M, K] * W^T with W the any4 weights."""
+    _b16(x, "x"), _u8(packed, "packed")
+    _b16(lut, "lut"), _b16(alpha, "alpha"), _b16(beta, "beta")
+    M, K = x.shape
+    N = packed.shape[0]
+    if packed.shape != (N, K // 2) or lut.shape != (N, 16):
+        raise ValueError("packed must be [N, K/2] and lut [N, 16]")
+    if g <= 0 or K % g or alpha.shape != (N, K // g) or beta.shape != (N, K // g):
+        raise ValueError("alpha/beta must be [N, K/g]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _b16(out, "y")
+    if out.shape != (M, N):
+        raise ValueError("y must be [M, N]")
+    need = workspace_size(M, N, K, g)
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(gemm_raw(_ptr(x), _ptr(packed), _ptr(lut), _ptr(alpha), _ptr(beta), _ptr(out), M, N, K,
+                   g, ws_ptr, ws_bytes, stream))
+    return out

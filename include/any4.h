@@ -1,0 +1,127 @@
+/*
+ * any4.h -- C ABI of libany4.so, the MI355X (gfx950) any4 dequantize-GEMM.
+ *
+ * any4 (the 10100.com any4 explainer, section 二) stores each weight of a
+ * row as a 4-bit index into that row's 16-entry bf16 lookup table; each
+ * contiguous group of g weights of a row also has a scale alpha and an offset
+ * beta (step 1, "分组缩放": g = 128 typical, accuracy holds to g = 1024).  A
+ * weight is w = alpha * LUT_row[idx] + beta.  The matmul y = x * W^T runs at
+ * the decode batch sizes M = 1..16 that the same page's section 三 targets.
+ *
+ * Conventions shared by every call
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing, keeps no per-call state and may be called from several
+ *     host threads.  Buffers must stay alive until the work on `stream`
+ *     completes.
+ *   - bf16 values travel as uint16_t bit patterns.  Arrays are dense and
+ *     row-major:
+ *         idx     [N][K]    uint8, values 0..15 (only the low 4 bits are read)
+ *         packed  [N][K/2]  uint8, byte j of a row holds index 2j in bits 0..3
+ *                           and index 2j+1 in bits 4..7
+ *         lut     [N][16]   bf16, lut[n][i] is the value of index i in row n
+ *         alpha   [N][K/g]  bf16, scale of weights k in [j*g, (j+1)*g) of row n
+ *         beta    [N][K/g]  bf16, offset of the same group
+ *         x       [M][K]    bf16 activations
+ *         y       [M][N]    bf16 output
+ *         w       [N][K]    bf16 dequantised weights
+ *   - Calls are asynchronous on `stream` (0 = the default stream).  They
+ *     return before the GPU work finishes; device faults show up at the
+ *     caller's next synchronisation.
+ *   - Arguments are checked before anything is launched.  On any error
+ *     nothing is launched and every output is left untouched.
+ *   - Outputs must not overlap inputs.  They are fully overwritten (no
+ *     accumulate mode).
+ *   - Group size: g must be a positive multiple of 128 and divide K
+ *     (K = 0 is allowed where stated).  This covers g = 128 .. 1024.
+ *   - Alignment: x, packed, lut and w need 16-byte aligned base pointers;
+ *     idx needs 16 bytes as well; alpha, beta and y need 2 bytes.
+ */
+#ifndef ANY4_H
+#define ANY4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum any4_status {
+    ANY4_OK = 0,
+    ANY4_E_NULL = 1,      /* a required pointer is NULL                               */
+    ANY4_E_SHAPE = 2,     /* a size is negative, K is odd, g is not a positive multiple
+                             of 128, K % g != 0, or M > 16 (any4_gemm)                */
+    ANY4_E_ALIGN = 3,     /* a base pointer misses the alignment stated above          */
+    ANY4_E_WORKSPACE = 4, /* workspace smaller than any4_gemm_workspace_size()         */
+    ANY4_E_HIP = 5        /* the HIP runtime refused a query or a launch               */
+} any4_status;
+
+/*
+ * any4_pack -- pack 4-bit indices two per byte (the layout above).
+ * The offline step before inference, the counterpart of the "weights laid out
+ * ahead of time" that the explainer's section 三 describes for its kernel.
+ *   idx     device, [N][K] uint8, read-only; bits 4..7 of each byte are ignored.
+ *   packed  device, [N][K/2] uint8, written.
+ *   N, K    N >= 0, K >= 0 and even.  N*K == 0 is a no-op.
+ * Errors: ANY4_E_SHAPE, ANY4_E_NULL, ANY4_E_ALIGN (idx or packed not 16-byte
+ * aligned), ANY4_E_HIP.
+ */
+any4_status any4_pack(const uint8_t* idx, uint8_t* packed, int64_t N, int64_t K,
+                      hipStream_t stream);
+
+/*
+ * any4_dequant -- materialise the bf16 weights (the explainer, section 二:
+ * a lookup in the row's table; step 1: group scale and offset):
+ *     w[n][k] = bf16_rne( fp32( alpha[n][k/g] * lut[n][idx[n][k]] + beta[n][k/g] ) )
+ * The bf16 x bf16 product is exact in fp32, so the inner value is one fp32
+ * rounding (nearest even) of the exact sum; the result is then rounded to bf16
+ * (nearest even).  Bit-exact: there is one correct answer.
+ *   packed, lut, alpha, beta  device, read-only, layouts above.
+ *   w                         device, [N][K] bf16, written.
+ *   N >= 0, K >= 0, g as above.  N*K == 0 is a no-op.
+ * Errors: ANY4_E_SHAPE, ANY4_E_NULL, ANY4_E_ALIGN, ANY4_E_HIP.
+ */
+any4_status any4_dequant(const uint8_t* packed, const uint16_t* lut, const uint16_t* alpha,
+                         const uint16_t* beta, uint16_t* w, int64_t N, int64_t K, int64_t g,
+                         hipStream_t stream);
+
+/*
+ * any4_gemm_workspace_size -- bytes of device workspace any4_gemm needs for
+ * this shape (0 when it needs none).  Returns 0 for shapes any4_gemm rejects.
+ */
+size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
+
+/*
+ * any4_gemm -- y = x * W^T with W the any4 weights above, for M = 1..16
+ * (the explainer's section 三: decode batches of 1..16):
+ *     y[m][n] = bf16_rne( sum_k x[m][k] * (alpha[n][k/g] * lut[n][idx[n][k]] + beta[n][k/g]) )
+ * The weights are never written out: each group contributes
+ * alpha * sum_k x*lut[idx] + beta * sum_k x, accumulated in fp32.  Any
+ * summation order is allowed; the result is within
+ *     |y - y_ref| <= 2e-3 * sum_k |x[m][k] * w[n][k]| + 1e-3
+ * of the fp64 product with the bf16 dequantised weights for the workloads this
+ * library is tested on.  Runs are deterministic (same inputs, same bits).
+ *   x                         device, [M][K] bf16, read-only.
+ *   packed, lut, alpha, beta  device, read-only.
+ *   y                         device, [M][N] bf16, written.
+ *   M in 0..16, N >= 0, K >= 0 with K % g == 0.  M*N == 0 is a no-op;
+ *   K == 0 writes y = 0 (x, packed, alpha and beta may then be NULL).
+ *   workspace, workspace_bytes  device scratch of at least
+ *       any4_gemm_workspace_size(M, N, K, g) bytes (NULL/0 when that is 0);
+ *       its contents on entry do not matter.
+ * Errors: ANY4_E_SHAPE, ANY4_E_NULL, ANY4_E_ALIGN, ANY4_E_WORKSPACE, ANY4_E_HIP.
+ */
+any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
+                      const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
+                      int64_t N, int64_t K, int64_t g, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* A static, human-readable name for a status code (never NULL). */
+const char* any4_status_string(any4_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ANY4_H */

@@ -1,0 +1,84 @@
+"""The C-ABI library loads, exports what include/any4.h declares, and rejects bad
+arguments before touching the GPU (CPU only: no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gemm_any4_amd as any4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "any4.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(any4_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared_functions() == sorted(any4.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(any4.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for s, name in any4._STATUS_NAMES.items():
+        assert any4.status_string(s).startswith(name)
+    assert "unknown" in any4.status_string(99)
+
+
+# Every call below fails validation, so nothing reaches the HIP runtime.
+A = 1 << 20          # a 16-byte aligned fake address (never dereferenced)
+
+
+@pytest.mark.parametrize("M,N,K,g", [(17, 16, 128, 128), (-1, 16, 128, 128), (1, -1, 128, 128),
+                                     (1, 16, 128, 64), (1, 16, 256, 96), (1, 16, 384, 256),
+                                     (1, 16, -128, 128), (1, 16, 128, 0)])
+def test_gemm_shape_errors(M, N, K, g):
+    assert any4.gemm_raw(A, A, A, A, A, A, M, N, K, g, stream=0) == 2
+
+
+def test_gemm_null_errors():
+    assert any4.gemm_raw(None, A, A, A, A, A, 1, 16, 128, 128, stream=0) == 1
+    assert any4.gemm_raw(A, None, A, A, A, A, 1, 16, 128, 128, stream=0) == 1
+    assert any4.gemm_raw(A, A, None, A, A, A, 1, 16, 128, 128, stream=0) == 1
+    assert any4.gemm_raw(A, A, A, A, A, None, 1, 16, 128, 128, stream=0) == 1
+
+
+def test_gemm_alignment_errors():
+    assert any4.gemm_raw(A + 2, A, A, A, A, A, 1, 16, 128, 128, stream=0) == 3
+    assert any4.gemm_raw(A, A + 8, A, A, A, A, 1, 16, 128, 128, stream=0) == 3
+    assert any4.gemm_raw(A, A, A + 4, A, A, A, 1, 16, 128, 128, stream=0) == 3
+    assert any4.gemm_raw(A, A, A, A + 1, A, A, 1, 16, 128, 128, stream=0) == 3
+    assert any4.gemm_raw(A, A, A, A, A, A + 1, 1, 16, 128, 128, stream=0) == 3
+
+
+def test_empty_calls_are_no_ops():
+    # nothing to do: success without touching pointers or the runtime
+    assert any4.gemm_raw(None, None, None, None, None, None, 0, 16, 128, 128, stream=0) == 0
+    assert any4.gemm_raw(None, None, None, None, None, None, 4, 0, 128, 128, stream=0) == 0
+    assert any4.dequant_raw(None, None, None, None, None, 0, 128, 128, stream=0) == 0
+    assert any4.pack_raw(None, None, 0, 64, stream=0) == 0
+    assert any4.pack_raw(None, None, 8, 0, stream=0) == 0
+
+
+def test_pack_and_dequant_errors():
+    assert any4.pack_raw(A, A, 4, 7, stream=0) == 2
+    assert any4.pack_raw(None, A, 4, 8, stream=0) == 1
+    assert any4.pack_raw(A + 1, A, 4, 8, stream=0) == 3
+    assert any4.dequant_raw(A, A, A, A, A, 4, 256, 192, stream=0) == 2
+    assert any4.dequant_raw(A, A, None, A, A, 4, 256, 128, stream=0) == 1
+    assert any4.dequant_raw(A, A, A, A, A + 2, 4, 256, 128, stream=0) == 3
+
+
+def test_workspace_size_is_defined_for_all_shapes():
+    for M in (1, 2, 4, 8, 16):
+        assert any4.workspace_size(M, 14336, 4096, 128) >= 0
+    assert any4.workspace_size(17, 16, 128, 128) == 0

@@ -1,0 +1,277 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+  * pack and dequant: bit-exact on every config at full size and on ragged
+    shapes;
+  * gemm: every output within |y - y_ref| <= 2e-3 * sum|x w| + 1e-3 of the
+    oracle's fp64 product, for configs 0-3 at every batch size (all outputs)
+    and config 4 (70B decoder-layer shapes from the oracle's k-means) on
+    sampled rows;
+  * invariants on the device: identity table returns the indices, one-hot x
+    returns a column of the dequantised W bit-exactly, permuting the table
+    with its indices leaves y bit-identical, x = 0 gives 0, runs are
+    deterministic, nothing is written outside y, the call honours a
+    non-default stream, empty shapes are no-ops and K = 0 gives zeros.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import gemm_any4_amd as any4
+import oracle
+import workloads
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    gu.require_gpu()
+    any4.lib()
+
+
+# --------------------------------------------------------------------------
+# pack
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_pack_bitexact_configs(cfg):
+    L = gu.config_layer(cfg)
+    idx = gu.dev_u8(L.inp.idx)
+    packed = any4.pack(idx)
+    torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy(), L.packed_host)
+
+
+@pytest.mark.parametrize("N,K", [(1, 2), (3, 30), (7, 34), (5, 1000), (64, 4098), (1, 32)])
+def test_pack_ragged(N, K):
+    rng = np.random.default_rng(N * 1000 + K)
+    idx = rng.integers(0, 256, size=(N, K), dtype=np.uint8)   # high bits must be ignored
+    packed = any4.pack(gu.dev_u8(idx))
+    torch.cuda.synchronize()
+    assert np.array_equal(packed.cpu().numpy(), oracle.pack(idx))
+
+
+# --------------------------------------------------------------------------
+# dequant
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_dequant_bitexact_configs(cfg):
+    L = gu.config_layer(cfg)
+    w = any4.dequant(L.packed, L.lut, L.alpha, L.beta, L.g)
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.host_b16(w), L.w_ref())
+
+
+@pytest.mark.parametrize("N,K,g", [(1, 128, 128), (3, 384, 128), (33, 640, 128), (7, 2048, 1024),
+                                   (5, 1536, 512), (129, 128, 128)])
+def test_dequant_ragged(N, K, g):
+    inp = workloads.generic(N + K + g, 1, N, K, g)
+    L = gu.Layer(inp)
+    w = any4.dequant(L.packed, L.lut, L.alpha, L.beta, g)
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.host_b16(w), L.w_ref())
+
+
+def test_identity_table_returns_indices():
+    """pack + in-kernel decode: LUT[i] = i, alpha = 1, beta = 0 gives idx exactly."""
+    N, K, g = 40, 512, 128
+    rng = np.random.default_rng(77)
+    idx = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    lut = np.tile(workloads.to_bf16_bits(np.arange(16.0)), (N, 1))
+    one = workloads.to_bf16_bits(np.ones((N, K // g)))
+    zero = np.zeros((N, K // g), np.uint16)
+    packed = any4.pack(gu.dev_u8(idx))
+    w = any4.dequant(packed, gu.dev_b16(lut), gu.dev_b16(one), gu.dev_b16(zero), g)
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.host_f64(w), idx.astype(np.float64))
+
+
+def test_dequant_rounding_ties_on_device():
+    """alpha*L exactly half way between two bf16 values (beta = 0): nearest even."""
+    N, K, g = 16, 256, 128
+    rng = np.random.default_rng(5)
+    a = rng.integers(0x3F80, 0x3FFF, size=(N, K // g)).astype(np.uint16)
+    lut = rng.integers(0x3F80, 0x3FFF, size=(N, 16)).astype(np.uint16)
+    idx = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    zero = np.zeros((N, K // g), np.uint16)
+    inp = workloads.Any4Inputs(N, K, g, idx, lut, a, zero, np.zeros((1, K), np.uint16))
+    L = gu.Layer(inp)
+    w = any4.dequant(L.packed, L.lut, L.alpha, L.beta, g)
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.host_b16(w), L.w_ref())
+
+
+# --------------------------------------------------------------------------
+# gemm against the oracle
+# --------------------------------------------------------------------------
+CONFIG_MS = [(0, 1), (1, 1), (2, 1), (2, 2), (2, 4), (2, 8), (2, 16), (3, 1), (3, 16)]
+
+
+@pytest.mark.parametrize("cfg,M", CONFIG_MS)
+def test_gemm_configs(cfg, M):
+    L = gu.config_layer(cfg)
+    y = any4.gemm(L.x[:M], L.packed, L.lut, L.alpha, L.beta, L.g)
+    torch.cuda.synchronize()
+    y_ref, ad = gu.config_ref(cfg, M)
+    r = gu.assert_within_bound(y, y_ref, ad, f"config {cfg} M={M}")
+    print(f"config {cfg} M={M}: max err/tol = {r:.3e}", flush=True)
+
+
+@functools.lru_cache(maxsize=1)
+def _config4(name):
+    raw = workloads.raw_layer(name)
+    idx, lut, a, b = oracle.kmeans_quantize(raw.W, raw.Ex, raw.g, workloads.CONFIG4_ITERS)
+    del raw.W
+    inp = workloads.Any4Inputs(raw.N, raw.K, raw.g, idx, lut, a, b, raw.x)
+    return gu.Layer(inp)
+
+
+@pytest.mark.parametrize("name", ["qkvo", "up_gate", "down"])
+def test_gemm_config4_sampled_rows(name):
+    L = _config4(name)
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([[0, L.N - 1], rng.choice(L.N, 254, replace=False)]))
+    w_rows = oracle.dequant(L.packed_host[rows], L.inp.lut[rows], L.inp.alpha[rows],
+                            L.inp.beta[rows], L.g)
+    for M in workloads.CONFIG4_MS:
+        y = any4.gemm(L.x[:M], L.packed, L.lut, L.alpha, L.beta, L.g)
+        torch.cuda.synchronize()
+        y_ref, ad = oracle.gemm(L.inp.x[:M], w_rows, nthreads=oracle.default_threads())
+        r = gu.assert_within_bound(y[:, torch.from_numpy(rows).to(gu.DEV)], y_ref, ad,
+                                   f"config 4 {name} M={M}")
+        print(f"config 4 {name} M={M}: max err/tol = {r:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("M,N,K,g", [(1, 17, 128, 128), (3, 50, 384, 128), (5, 1, 256, 256),
+                                     (7, 33, 1024, 512), (16, 15, 128, 128), (9, 100, 2048, 1024),
+                                     (12, 272, 640, 128), (2, 4097, 256, 128)])
+def test_gemm_ragged(M, N, K, g):
+    inp = workloads.generic(M * 7 + N + K, M, N, K, g)
+    L = gu.Layer(inp)
+    y = any4.gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g)
+    torch.cuda.synchronize()
+    y_ref, ad = oracle.gemm(inp.x, L.w_ref())
+    gu.assert_within_bound(y, y_ref, ad, f"ragged {M}x{N}x{K} g{g}")
+
+
+# --------------------------------------------------------------------------
+# invariants on the device
+# --------------------------------------------------------------------------
+def test_one_hot_x_returns_dequantised_columns():
+    inp = workloads.generic(31, 16, 64, 1024, 256)
+    L = gu.Layer(inp)
+    w_ref = L.w_ref()
+    one = workloads.to_bf16_bits(np.array([1.0]))[0]
+    ks = [0, 1, 2, 31, 32, 127, 128, 255, 256, 511, 777, 1023]
+    x = np.zeros((len(ks), 1024), np.uint16)
+    for m, k in enumerate(ks):
+        x[m, k] = one
+    y = any4.gemm(gu.dev_b16(x), L.packed, L.lut, L.alpha, L.beta, 256)
+    torch.cuda.synchronize()
+    yb = gu.host_b16(y)
+    for m, k in enumerate(ks):
+        assert np.array_equal(yb[m], w_ref[:, k]), k
+
+
+def test_permutation_gives_bitwise_identical_y():
+    inp = workloads.generic(32, 16, 96, 1024, 128)
+    rng = np.random.default_rng(32)
+    lut2, idx2 = inp.lut.copy(), inp.idx.copy()
+    for n in range(inp.N):
+        pi = rng.permutation(16)
+        lut2[n, pi] = inp.lut[n]
+        idx2[n] = pi[inp.idx[n]]
+    L1 = gu.Layer(inp)
+    L2 = gu.Layer(workloads.Any4Inputs(inp.N, inp.K, inp.g, idx2, lut2, inp.alpha, inp.beta,
+                                       inp.x))
+    for M in (1, 4, 16):
+        y1 = any4.gemm(L1.x[:M], L1.packed, L1.lut, L1.alpha, L1.beta, 128)
+        y2 = any4.gemm(L2.x[:M], L2.packed, L2.lut, L2.alpha, L2.beta, 128)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_constant_table_rank1():
+    N, K, g = 64, 1024, 128
+    inp = workloads.generic(33, 16, N, K, g)
+    c = workloads.to_bf16_bits(np.linspace(-2, 2, N))
+    lut = np.repeat(c[:, None], 16, axis=1)
+    a = np.repeat(inp.alpha[:, :1], K // g, axis=1)
+    b = np.repeat(inp.beta[:, :1], K // g, axis=1)
+    L = gu.Layer(workloads.Any4Inputs(N, K, g, inp.idx, lut, a, b, inp.x))
+    y = any4.gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g)
+    torch.cuda.synchronize()
+    w_ref = L.w_ref()
+    wn = workloads.bf16_bits_to_f64(w_ref[:, 0])
+    X = workloads.bf16_bits_to_f64(inp.x)
+    closed = np.outer(X.sum(axis=1), wn)
+    _, ad = oracle.gemm(inp.x, w_ref)
+    gu.assert_within_bound(y, closed, ad, "rank-1")
+
+
+def test_zero_x_gives_exact_zero():
+    L = gu.config_layer(0)
+    x = torch.zeros((16, L.K), dtype=torch.bfloat16, device=gu.DEV)
+    y = any4.gemm(x, L.packed, L.lut, L.alpha, L.beta, L.g)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y.float()) == 0
+
+
+def test_deterministic():
+    L = gu.config_layer(1)
+    y1 = any4.gemm(L.x[:1], L.packed, L.lut, L.alpha, L.beta, L.g)
+    y2 = any4.gemm(L.x[:1], L.packed, L.lut, L.alpha, L.beta, L.g)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_no_writes_outside_y():
+    inp = workloads.generic(34, 5, 37, 512, 128)
+    L = gu.Layer(inp)
+    pad = 4096
+    buf = torch.full((pad + 5 * 37 + pad,), -12345, dtype=torch.int16, device=gu.DEV)
+    y = buf[pad:pad + 5 * 37].view(5, 37)
+    any4.gemm(L.x, L.packed, L.lut, L.alpha, L.beta, 128, out=y.view(torch.bfloat16))
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == -12345) and torch.all(buf[pad + 5 * 37:] == -12345)
+    y_ref, ad = oracle.gemm(inp.x, L.w_ref())
+    gu.assert_within_bound(y.view(torch.bfloat16), y_ref, ad, "guarded")
+
+
+def test_non_default_stream():
+    L = gu.config_layer(2)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y = any4.gemm(L.x[:4], L.packed, L.lut, L.alpha, L.beta, L.g)
+        w = any4.dequant(L.packed, L.lut, L.alpha, L.beta, L.g)
+    s.synchronize()
+    y_ref, ad = gu.config_ref(2, 4)
+    gu.assert_within_bound(y, y_ref, ad, "stream")
+    assert np.array_equal(gu.host_b16(w), L.w_ref())
+
+
+def test_empty_and_k0():
+    L = gu.config_layer(0)
+    y = torch.empty((0, L.N), dtype=torch.bfloat16, device=gu.DEV)
+    any4.gemm(L.x[:0], L.packed, L.lut, L.alpha, L.beta, L.g, out=y)
+    # K = 0: an empty sum
+    x0 = torch.empty((3, 0), dtype=torch.bfloat16, device=gu.DEV)
+    p0 = torch.empty((L.N, 0), dtype=torch.uint8, device=gu.DEV)
+    ab0 = torch.empty((L.N, 0), dtype=torch.bfloat16, device=gu.DEV)
+    y0 = torch.full((3, L.N), 7.0, dtype=torch.bfloat16, device=gu.DEV)
+    any4.gemm(x0, p0, L.lut, ab0, ab0, 128, out=y0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y0.float()) == 0
+
+
+def test_misaligned_pointer_is_rejected():
+    L = gu.config_layer(0)
+    xs = torch.zeros(L.K + 8, dtype=torch.bfloat16, device=gu.DEV)
+    y = torch.zeros((1, L.N), dtype=torch.bfloat16, device=gu.DEV)
+    s = any4.gemm_raw(xs.data_ptr() + 2, L.packed.data_ptr(), L.lut.data_ptr(),
+                      L.alpha.data_ptr(), L.beta.data_ptr(), y.data_ptr(), 1, L.N, L.K, L.g)
+    assert s == 3
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y.float()) == 0
