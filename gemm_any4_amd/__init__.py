@@ -6,8 +6,9 @@ stream.  There is no CPU fallback: if the library is missing or a call fails,
 a ``RuntimeError`` is raised.
 
 Tensors
-  idx     uint8  [N, K]     values 0..15
-  packed  uint8  [N, K/2]   byte j: index 2j in bits 0..3, 2j+1 in bits 4..7
+  idx     uint8  [N, K]     values 0..15, K a multiple of 128
+  packed  uint8  [packed_bytes(N, K)]  the indices in the library's tile layout
+                            (16 rows x 128 k per 1 KB tile; include/any4.h)
   lut     bf16   [N, 16]    per-row table
   alpha   bf16   [N, K/g]   per-group scale
   beta    bf16   [N, K/g]   per-group offset
@@ -31,8 +32,8 @@ _STATUS_NAMES = {0: "ANY4_OK", 1: "ANY4_E_NULL", 2: "ANY4_E_SHAPE", 3: "ANY4_E_A
                  4: "ANY4_E_WORKSPACE", 5: "ANY4_E_HIP"}
 
 # every symbol include/any4.h declares
-EXPORTS = ("any4_pack", "any4_dequant", "any4_gemm_workspace_size", "any4_gemm",
-           "any4_status_string")
+EXPORTS = ("any4_packed_bytes", "any4_pack", "any4_dequant", "any4_gemm_workspace_size",
+           "any4_gemm", "any4_status_string")
 
 _lib = None
 
@@ -52,6 +53,8 @@ def lib() -> ctypes.CDLL:
                                "or python -m gemm_any4_amd.build")
         L = ctypes.CDLL(LIB_PATH)
         P, I64, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        L.any4_packed_bytes.restype = SZ
+        L.any4_packed_bytes.argtypes = [I64, I64]
         L.any4_pack.restype = ctypes.c_int
         L.any4_pack.argtypes = [P, P, I64, I64, P]
         L.any4_dequant.restype = ctypes.c_int
@@ -125,6 +128,10 @@ def workspace_size(M: int, N: int, K: int, g: int) -> int:
     return int(lib().any4_gemm_workspace_size(M, N, K, g))
 
 
+def packed_bytes(N: int, K: int) -> int:
+    return int(lib().any4_packed_bytes(N, K))
+
+
 def gemm_raw(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
              ws_ptr=None, ws_bytes=0, stream=None) -> int:
     return lib().any4_gemm(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
@@ -135,31 +142,40 @@ def gemm_raw(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
 # tensor API
 # --------------------------------------------------------------------------
 def pack(idx: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """idx uint8 [N, K] -> packed uint8 [N, K/2]."""
+    """idx uint8 [N, K] -> packed uint8 [packed_bytes(N, K)] (tile layout)."""
     _u8(idx, "idx")
     N, K = idx.shape
+    nbytes = packed_bytes(N, K)
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
     if out is None:
-        out = torch.empty((N, K // 2), dtype=torch.uint8, device=idx.device)
+        out = torch.empty((nbytes,), dtype=torch.uint8, device=idx.device)
     _u8(out, "packed")
-    if out.shape != (N, K // 2):
-        raise ValueError("packed must be [N, K/2]")
+    if out.numel() != nbytes:
+        raise ValueError(f"packed must hold {nbytes} bytes")
     check(pack_raw(_ptr(idx), _ptr(out), N, K, stream))
     return out
 
 
+def _check_packed(packed: torch.Tensor, N: int, K: int) -> None:
+    _u8(packed, "packed")
+    if packed.numel() != packed_bytes(N, K):
+        raise ValueError(f"packed must hold packed_bytes({N}, {K}) = {packed_bytes(N, K)} bytes")
+
+
 def dequant(packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
             g: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Materialise the bf16 weights w [N, K]."""
-    _u8(packed, "packed")
+    """Materialise the bf16 weights w [N, K] (N from lut, K = alpha.shape[1] * g)."""
     _b16(lut, "lut"), _b16(alpha, "alpha"), _b16(beta, "beta")
-    N, K2 = packed.shape
-    K = 2 * K2
-    if lut.shape != (N, 16):
+    if lut.dim() != 2 or lut.shape[1] != 16:
         raise ValueError("lut must be [N, 16]")
-    if g <= 0 or K % g or alpha.shape != (N, K // g) or beta.shape != (N, K // g):
+    N = lut.shape[0]
+    if g <= 0 or alpha.dim() != 2 or alpha.shape[0] != N or beta.shape != alpha.shape:
         raise ValueError("alpha/beta must be [N, K/g]")
+    K = alpha.shape[1] * g
+    _check_packed(packed, N, K)
     if out is None:
-        out = torch.empty((N, K), dtype=torch.bfloat16, device=packed.device)
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=lut.device)
     _b16(out, "w")
     if out.shape != (N, K):
         raise ValueError("w must be [N, K]")
@@ -168,29 +184,48 @@ def dequant(packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor, beta: 
     return out
 
 
+# One zeroed workspace per (device, stream): calls on one stream run one after
+# another, and each call leaves its workspace zeroed again.
+_workspaces: dict = {}
+
+
+def _workspace(need: int, device: torch.device, stream_handle: int) -> torch.Tensor:
+    key = (device.index, stream_handle)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(max(need, 1 << 16), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
 def gemm(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor,
          beta: torch.Tensor, g: int, out: torch.Tensor | None = None,
          workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """y [M, N] = x [M, K] * W^T with W the any4 weights."""
-    _b16(x, "x"), _u8(packed, "packed")
-    _b16(lut, "lut"), _b16(alpha, "alpha"), _b16(beta, "beta")
+    """y [M, N] = x [M, K] * W^T with W the any4 weights (N from lut).
+
+    workspace: optional uint8 device tensor of at least workspace_size(M, N, K, g)
+    bytes, all zero before its first use (each call leaves it zeroed).  By
+    default a workspace kept per device and stream is used."""
+    _b16(x, "x"), _b16(lut, "lut"), _b16(alpha, "alpha"), _b16(beta, "beta")
     M, K = x.shape
-    N = packed.shape[0]
-    if packed.shape != (N, K // 2) or lut.shape != (N, 16):
-        raise ValueError("packed must be [N, K/2] and lut [N, 16]")
+    if lut.dim() != 2 or lut.shape[1] != 16:
+        raise ValueError("lut must be [N, 16]")
+    N = lut.shape[0]
     if g <= 0 or K % g or alpha.shape != (N, K // g) or beta.shape != (N, K // g):
         raise ValueError("alpha/beta must be [N, K/g]")
+    _check_packed(packed, N, K)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _b16(out, "y")
     if out.shape != (M, N):
         raise ValueError("y must be [M, N]")
+    sh = _stream(stream)
     need = workspace_size(M, N, K, g)
     ws_ptr, ws_bytes = None, 0
     if need:
         if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+            workspace = _workspace(need, x.device, sh)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     check(gemm_raw(_ptr(x), _ptr(packed), _ptr(lut), _ptr(alpha), _ptr(beta), _ptr(out), M, N, K,
-                   g, ws_ptr, ws_bytes, stream))
+                   g, ws_ptr, ws_bytes, sh))
     return out

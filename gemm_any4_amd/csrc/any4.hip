@@ -6,26 +6,19 @@
 // w = alpha * LUT_row[idx] + beta; the matmul y = x * W^T runs at decode batch
 // sizes 1..16 (section 三).  The C ABI is declared in include/any4.h.
 //
+// Packed tile layout (written by k_pack, read by k_dequant and k_gemm)
+//   The weights are cut into tiles of 16 rows x 128 k.  A tile is 1 KB and is
+//   one 16-byte load per lane of a wave64: lane l holds row (l % 16) of the
+//   tile, k in [32*(l/16), 32*(l/16) + 32), two indices per byte, the even k
+//   in the low nibble.  Tiles are stored row-block major: tile (b, c) of row
+//   block b (rows 16b..16b+15) and k-chunk c (k 128c..128c+127) starts at byte
+//   (b * K/128 + c) * 1024.  Rows past N are zero padding.
+//
 // Kernels
-//   k_pack     nibble packing, 32 index bytes -> 16 packed bytes per thread.
-//   k_dequant  w = bf16(fma(alpha, LUT[idx], beta)), 16 weights per thread.
-//   k_gemm     y = x * W^T on the bf16 MFMA units:
-//     * A 16-row tile of W is the B operand of v_mfma_f32_16x16x32_bf16, x is
-//       the A operand (rows m >= M are zero), so one MFMA covers 16 weight rows
-//       x 32 k for every m of the batch.
-//     * Lookup: each packed byte (two indices) selects one dword of a per-lane
-//       LDS table holding the bf16 pair (LUT[lo], LUT[hi]), which is exactly one
-//       dword of the MFMA operand.  The table has 256 entries x 64 slots, one
-//       slot per lane, laid out entry-major, so a lane always reads bank
-//       (lane mod 64): the gather is free of bank conflicts.  The byte address
-//       entry*256 + lane*4 is one v_perm_b32 of the packed dword.
-//     * Scale and offset stay out of the per-weight work: a group contributes
-//       alpha * (sum_k x*LUT[idx]) + beta * (sum_k x); the first sum is an MFMA
-//       chain, alpha is one FMA per accumulator, and the beta term is an MFMA
-//       against a constant operand filled with beta.
-//     * The waves of a workgroup share one tile and split its K; their partial
-//       sums meet in LDS in a fixed order (deterministic), then are rounded to
-//       bf16 and stored.
+//   k_pack     idx[N][K] u8 -> tiles, 16 output bytes per thread.
+//   k_dequant  w = bf16(fma(alpha, LUT[idx], beta)), one tile slot per thread.
+//   k_gemm     y = x * W^T with v_mfma_f32_16x16x32_bf16; see the comment above
+//              the kernel.
 #include <hip/hip_runtime.h>
 
 #include "any4.h"
@@ -36,16 +29,42 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+constexpr int TILE_ROWS = 16;
+constexpr int TILE_K = 128;
+constexpr int TILE_BYTES = TILE_ROWS * TILE_K / 2;   // 1024
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t h)
 {
     return __uint_as_float(h << 16);
 }
 
-// fp32 -> bf16 with the hardware conversion (v_cvt_pk_bf16_f32, round to
-// nearest even).
+// fp32 -> bf16 with the hardware conversion (round to nearest even).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f)
 {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// ---------------------------------------------------------------------------
+// bounds-checked buffer loads
+// ---------------------------------------------------------------------------
+constexpr uint32_t OOR = 0x80000000u;   // an offset past every buffer this library reads
+
+// Raw buffer resource over [base, base + bytes): a load at an offset >= bytes
+// returns zero and touches no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t load2(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -63,207 +82,375 @@ __device__ __forceinline__ uint32_t pack8(uint32_t lo4, uint32_t hi4)
     return __builtin_amdgcn_perm(u, t, 0x06040200u);
 }
 
+// One thread per 16-byte tile slot: tile q/64, lane q%64.
 __global__ __launch_bounds__(PACK_THREADS) void k_pack(const uint8_t* __restrict__ idx,
-                                                       uint8_t* __restrict__ packed,
-                                                       size_t nout)
+                                                       uint8_t* __restrict__ packed, int N,
+                                                       int K, uint32_t slots)
 {
-    const size_t o = (static_cast<size_t>(blockIdx.x) * PACK_THREADS + threadIdx.x) * 16;
-    if (o + 16 <= nout) {
-        const uint4* src = reinterpret_cast<const uint4*>(idx + 2 * o);
-        const uint4 a = src[0], b = src[1];
-        uint4 r;
-        r.x = pack8(a.x, a.y);
-        r.y = pack8(a.z, a.w);
-        r.z = pack8(b.x, b.y);
-        r.w = pack8(b.z, b.w);
-        *reinterpret_cast<uint4*>(packed + o) = r;
-    } else if (o < nout) {
-        for (size_t j = o; j < nout; ++j)
-            packed[j] = static_cast<uint8_t>((idx[2 * j] & 15u) | ((idx[2 * j + 1] & 15u) << 4));
+    const uint32_t q = blockIdx.x * PACK_THREADS + threadIdx.x;
+    if (q >= slots)
+        return;
+    const int Kc = K / TILE_K;
+    const uint32_t tile = q >> 6, l = q & 63;
+    const int b = tile / Kc, c = tile % Kc;
+    const int n = b * TILE_ROWS + (l & 15);
+    u32x4_t out = {0u, 0u, 0u, 0u};
+    if (n < N) {
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
+            idx + static_cast<size_t>(n) * K + c * TILE_K + (l >> 4) * 32);
+        const u32x4_t a = src[0], bb = src[1];
+        out[0] = pack8(a[0], a[1]);
+        out[1] = pack8(a[2], a[3]);
+        out[2] = pack8(bb[0], bb[1]);
+        out[3] = pack8(bb[2], bb[3]);
     }
+    *reinterpret_cast<u32x4_t*>(packed + static_cast<size_t>(q) * 16) = out;
 }
 
 // ---------------------------------------------------------------------------
 // dequant
 // ---------------------------------------------------------------------------
-constexpr int DQ_THREADS = 256;
-constexpr int DQ_PER_THREAD = 16;                         // weights per thread
-constexpr int DQ_PER_BLOCK = DQ_THREADS * DQ_PER_THREAD;  // 4096
-constexpr int DQ_MAX_ROWS = DQ_PER_BLOCK / 128 + 1;       // K >= 128
+constexpr int DQ_WAVES = 4;   // one tile per wave; a workgroup covers 4 chunks of one row block
 
-__global__ __launch_bounds__(DQ_THREADS) void k_dequant(const uint8_t* __restrict__ packed,
-                                                        const uint16_t* __restrict__ lut,
-                                                        const uint16_t* __restrict__ alpha,
-                                                        const uint16_t* __restrict__ beta,
-                                                        uint16_t* __restrict__ w, int64_t K,
-                                                        int64_t g, size_t units)
+// w[n][k] = bf16(fma(alpha, LUT[idx], beta)).  The workgroup's 16 table rows
+// are widened to fp32 in LDS; each lane decodes its 32 weights and writes 64
+// contiguous bytes of w.
+__global__ __launch_bounds__(64 * DQ_WAVES) void k_dequant(const uint8_t* __restrict__ packed,
+                                                          const uint16_t* __restrict__ lut,
+                                                          const uint16_t* __restrict__ alpha,
+                                                          const uint16_t* __restrict__ beta,
+                                                          uint16_t* __restrict__ w, int N, int K,
+                                                          int g)
 {
-    __shared__ float slut[DQ_MAX_ROWS * 16];
-    const size_t u0 = static_cast<size_t>(blockIdx.x) * DQ_THREADS;
-    const size_t ulast = min(u0 + DQ_THREADS, units) - 1;
-    const int64_t n_first = static_cast<int64_t>(u0 * DQ_PER_THREAD / K);
-    const int64_t n_last = static_cast<int64_t>(ulast * DQ_PER_THREAD / K);
-    const int nrows = static_cast<int>(n_last - n_first + 1);
-    for (int t = threadIdx.x; t < nrows * 16; t += DQ_THREADS)
-        slut[t] = bf16_to_f32(lut[n_first * 16 + t]);
-    __syncthreads();
-
-    const size_t u = u0 + threadIdx.x;
-    if (u >= units)
-        return;
-    const size_t e0 = u * DQ_PER_THREAD;                 // flat weight index
-    const int64_t n = static_cast<int64_t>(e0 / K);
-    const int64_t k0 = static_cast<int64_t>(e0 % K);
-    const int64_t G = K / g;
-    const float a = bf16_to_f32(alpha[n * G + k0 / g]);
-    const float b = bf16_to_f32(beta[n * G + k0 / g]);
-    const float* L = slut + (n - n_first) * 16;
-    const uint2 p = *reinterpret_cast<const uint2*>(packed + e0 / 2);
-    const uint32_t pw[2] = {p.x, p.y};
-    uint32_t out[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const uint32_t byte = (pw[q >> 2] >> (8 * (q & 3))) & 0xFFu;
-        const float lo = fmaf(a, L[byte & 15u], b);
-        const float hi = fmaf(a, L[byte >> 4], b);
-        out[q] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    __shared__ float sl[TILE_ROWS * 16];
+    const int Kc = K / TILE_K;
+    const int cgroups = (Kc + DQ_WAVES - 1) / DQ_WAVES;
+    const int b = blockIdx.x / cgroups;
+    const int c = (blockIdx.x % cgroups) * DQ_WAVES + (threadIdx.x >> 6);
+    {
+        const int t = threadIdx.x;   // 256 threads: row t/16, entry t%16
+        const int n = b * TILE_ROWS + (t >> 4);
+        sl[t] = n < N ? bf16_to_f32(lut[static_cast<size_t>(n) * 16 + (t & 15)]) : 0.f;
     }
-    uint4* dst = reinterpret_cast<uint4*>(w + e0);
-    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+    __syncthreads();
+    const int l = threadIdx.x & 63;
+    const int j = l & 15;
+    const int n = b * TILE_ROWS + j;
+    if (c >= Kc || n >= N)
+        return;
+    const int k0 = c * TILE_K + (l >> 4) * 32;
+    const int G = K / g;
+    const float a = bf16_to_f32(alpha[static_cast<size_t>(n) * G + k0 / g]);
+    const float bt = bf16_to_f32(beta[static_cast<size_t>(n) * G + k0 / g]);
+    const u32x4_t p = *reinterpret_cast<const u32x4_t*>(
+        packed + (static_cast<size_t>(b) * Kc + c) * TILE_BYTES + l * 16);
+    const float* L = sl + j * 16;
+    u32x4_t out[4];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const uint32_t byte = (p[q >> 2] >> (8 * (q & 3))) & 0xFFu;
+        const float lo = fmaf(a, L[byte & 15u], bt);
+        const float hi = fmaf(a, L[byte >> 4], bt);
+        out[q >> 2][q & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    }
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(w + static_cast<size_t>(n) * K + k0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        dst[q] = out[q];
 }
 
 // ---------------------------------------------------------------------------
 // gemm
 // ---------------------------------------------------------------------------
-constexpr int GEMM_WAVES = 8;
-constexpr int GEMM_THREADS = 64 * GEMM_WAVES;
-constexpr int TILE_N = 16;       // weight rows per tile (MFMA N)
-constexpr int CHUNK_K = 128;     // k per chunk: a lane reads 16 packed bytes = 32 k
-constexpr int TAB_SLOTS = 64;    // one table copy per lane
-constexpr int TAB_WORDS = 256 * TAB_SLOTS;
 
-// Byte address of table entry `byte j of d` in this lane's slot:
-// (d.byte[j] << 8) | (lane * 4).
+// y = 0 (the K = 0 case: every sum is empty).  A kernel rather than a memset,
+// so that the call can be captured in a HIP graph.
+__global__ __launch_bounds__(256) void k_zero(uint16_t* __restrict__ y, size_t n)
+{
+    const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n)
+        y[i] = 0;
+}
+
+// Work split.  A workgroup has 8 waves and stays resident for the whole call
+// (the grid is about one workgroup per CU).  K is cut into S parts of 8*C
+// chunks; wave w of a workgroup always works on the same C chunks of its
+// part, so the x operands of those chunks are loaded once, into VGPRs, and
+// reused for every row block.  The workgroup walks row blocks r, r+Gp, r+2Gp,
+// ... (Gp workgroups per part); for each block its 8 waves decode their chunks
+// and their partial sums meet in LDS.  With S > 1 the parts of a block are
+// summed by whichever workgroup finishes that block last (counter in the
+// workspace), in part order, so results do not depend on timing.
+//
+// Decode.  A packed byte (two indices) selects one dword of a pair table in
+// LDS: entry (hi << 4 | lo) holds (LUT[lo], LUT[hi]) as two bf16, which is
+// exactly one dword of an MFMA B operand.  The table of a row block has 32
+// slots per entry (slot = lane % 32, row = slot % 16); a wave64 LDS read is
+// served as two halves of 32 lanes, so every lane reads its own bank: no
+// conflicts.  Entry e of buffer q sits at byte e*256 + q*128, so the read
+// address is one v_perm of the packed dword.  Two buffers let the waves build
+// the next block's table while they decode the current one.
+//
+// Scale and offset.  Per 128-k chunk a lane accumulates sum_k x*LUT[idx] with
+// four MFMAs, then adds alpha times that sum and beta times sum_k x (the chunk
+// sums of x are computed once, with MFMAs against ones).
+//
+// Memory.  Each wave keeps the next D tiles of its sequence (plus their alpha
+// and beta) in flight in a register ring, and loads the tables LR blocks
+// ahead.  Every load is a bounds-checked buffer load; where there is nothing
+// to read (past the wave's work, x rows m >= M) its offset is pushed out of
+// range, so no branch guards a load and no traffic is made.
+constexpr int GW = 8;                   // waves per workgroup
+constexpr int GT = 64 * GW;
+constexpr int TAB_BYTES = 256 * 256;    // 256 entries x 2 buffers x 32 slots x 4 B
+constexpr int RED_BYTES = 2 * GW * 64 * 16;
+
+struct GemmArgs {
+    const uint16_t* x;
+    const uint8_t* packed;
+    const uint16_t* lut;
+    const uint16_t* alpha;
+    const uint16_t* beta;
+    uint16_t* y;
+    float* part;        // [S][NB][64][VC] partial sums (S > 1)
+    uint32_t* count;    // [NB] arrival counters, zero between calls (S > 1)
+    int M, N, K, g;
+    int S, Gp;
+};
+
+// Byte address of table entry `byte j of d` in the lane's slot: (d.byte[j] << 8) | slot4.
 __device__ __forceinline__ uint32_t tab_addr(uint32_t d, uint32_t slot4, int j)
 {
     return __builtin_amdgcn_perm(d, slot4, 0x0C0C0000u | ((4u + j) << 8));
 }
 
-__device__ __forceinline__ uint32_t tab_read(const uint32_t* tab, uint32_t byte_addr)
+__device__ __forceinline__ uint32_t lds_word(const uint8_t* smem, uint32_t byte_addr)
 {
-    return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(tab) + byte_addr);
+    return *reinterpret_cast<const uint32_t*>(smem + byte_addr);
 }
 
-template <int MT>
-__global__ __launch_bounds__(GEMM_THREADS) void k_gemm(const uint16_t* __restrict__ x,
-                                                       const uint8_t* __restrict__ packed,
-                                                       const uint16_t* __restrict__ lut,
-                                                       const uint16_t* __restrict__ alpha,
-                                                       const uint16_t* __restrict__ beta,
-                                                       uint16_t* __restrict__ y, int M, int N,
-                                                       int K, int g)
+template <int MT, int C, int D, int LR>
+__global__ __launch_bounds__(GT) void k_gemm(const GemmArgs args)
 {
-    __shared__ uint32_t tab[TAB_WORDS];   // 64 KB pair table, then the reduction buffer
+    static_assert(D % C == 0 && (D / C) % LR == 0, "ring sizes");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[TAB_BYTES + RED_BYTES];
     constexpr int VC = MT < 4 ? MT : 4;   // accumulator rows that can hold a real m
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int j = lane & 15;              // weight row in the tile, and x row m
-    const int kq = lane >> 4;             // which 32-k quarter of a chunk
-    const int nchunks = K / CHUNK_K;
+    const int M = args.M, N = args.N, K = args.K, g = args.g;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15;      // tile row of this lane (B operand), x row m (A operand)
+    const int kq = lane >> 4;     // 32-k quarter of a chunk
+    const int Kc = K / TILE_K;
+    const int NB = (N + TILE_ROWS - 1) / TILE_ROWS;
     const int G = K / g;
-    const int cpg = g / CHUNK_K;
-    const int c_begin = nchunks * wave / GEMM_WAVES;
-    const int c_end = nchunks * (wave + 1) / GEMM_WAVES;
-    const int ntiles = (N + TILE_N - 1) / TILE_N;
-    const bool has_x = j < M;
-    const uint32_t slot4 = static_cast<uint32_t>(lane) * 4u;
+    const int s = blockIdx.x / args.Gp;
+    const int r = blockIdx.x % args.Gp;
+    const int nblk = r < NB ? (NB - 1 - r) / args.Gp + 1 : 0;
+    const int T = nblk * C;                 // tiles in this wave's sequence
+    const int cbase = s * (GW * C) + wave * C;
 
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int n0 = tile * TILE_N;
-        const int nr = min(n0 + j, N - 1);   // rows past N read row N-1, never stored
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc(args.packed, static_cast<uint32_t>(NB) * Kc * TILE_BYTES);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(args.lut, static_cast<uint32_t>(N) * 32);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(args.alpha, static_cast<uint32_t>(N) * G * 2);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(args.beta, static_cast<uint32_t>(N) * G * 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(args.x, static_cast<uint32_t>(M) * K * 2);
 
-        __syncthreads();   // the previous tile's reduction reads are done
-        {
-            const uint4* lp = reinterpret_cast<const uint4*>(lut + static_cast<size_t>(nr) * 16);
-            const uint4 q0 = lp[0], q1 = lp[1];
-            const uint32_t Lw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-            constexpr int HPW = 16 / GEMM_WAVES;
+    // ---- table rows: thread tid builds slot st (row st % 16), entries lo + 16*hi
+    const int st = tid & 31;
+    const int lo = tid >> 5;   // 0..15
+    u32x4_t lq0[LR], lq1[LR];
+    uint32_t llo[LR];
+    auto lut_load = [&](int i, u32x4_t& q0, u32x4_t& q1, uint32_t& ll) {
+        const uint32_t row = static_cast<uint32_t>(r + i * args.Gp) * TILE_ROWS + (st & 15);
+        const uint32_t off = i < nblk ? row * 32u : OOR;
+        q0 = load16(rl, off);
+        q1 = load16(rl, off + 16);
+        ll = load2(rl, off + 2 * lo);
+    };
+    auto tab_build = [&](int buf, const u32x4_t& q0, const u32x4_t& q1, uint32_t ll) {
+        const uint32_t Lw[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+        uint32_t* tw = reinterpret_cast<uint32_t*>(smem) + lo * 64 + buf * 32 + st;
 #pragma unroll
-            for (int h = 0; h < HPW; ++h) {
-                const int hi = wave * HPW + h;
-                const uint32_t Lhi = lut[static_cast<size_t>(nr) * 16 + hi];
+        for (int hi = 0; hi < 16; ++hi)
+            tw[hi * 16 * 64] = __builtin_amdgcn_perm(Lw[hi >> 1], ll,
+                                                     (hi & 1) ? 0x07060100u : 0x05040100u);
+    };
+
+    // ---- tile ring
+    u32x4_t pb[D];
+    uint32_t ab[D], bbv[D];
+    const uint32_t tile_lane = static_cast<uint32_t>(lane) * 16;
+    auto issue = [&](int u, int t) {
+        const int i = t / C;
+        const int c = cbase + t % C;
+        const bool live = t < T && c < Kc;
+        const int b = r + i * args.Gp;
+        const uint32_t toff = static_cast<uint32_t>(b * Kc + c) * TILE_BYTES + tile_lane;
+        const uint32_t goff =
+            (static_cast<uint32_t>(b * TILE_ROWS + j) * G + (c * TILE_K) / g) * 2;
+        pb[u] = load16(rp, live ? toff : OOR);
+        ab[u] = load2(ra, live ? goff : OOR);
+        bbv[u] = load2(rb, live ? goff : OOR);
+    };
+
+    // ---- prologue: table of block 0, x operands, the first D tiles, tables 1..LR
+    lut_load(0, lq0[0], lq1[0], llo[0]);
+    u32x4_t xr[C][4];
 #pragma unroll
-                for (int lo = 0; lo < 16; ++lo)
-                    tab[(hi * 16 + lo) * TAB_SLOTS + lane] = __builtin_amdgcn_perm(
-                        Lhi, Lw[lo >> 1], (lo & 1) ? 0x05040302u : 0x05040100u);
+    for (int ci = 0; ci < C; ++ci) {
+        const int c = cbase + ci;
+        const bool live = j < M && c < Kc;
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+            xr[ci][s4] = load16(rx, live ? static_cast<uint32_t>(
+                                               (j * K + c * TILE_K + kq * 32 + s4 * 8) * 2)
+                                         : OOR);
+    }
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+        issue(u, u);
+    tab_build(0, lq0[0], lq1[0], llo[0]);
+#pragma unroll
+    for (int q = 1; q <= LR; ++q)
+        lut_load(q, lq0[q % LR], lq1[q % LR], llo[q % LR]);
+
+    // chunk sums of x: lane l gets sum_k x[4*(l/16) + v][k] in xs[ci][v]
+    f32x4_t xs[C];
+    {
+        const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+        for (int ci = 0; ci < C; ++ci) {
+            xs[ci] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+                xs[ci] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, xr[ci][s4]), __builtin_bit_cast(bf16x8_t, ones),
+                    xs[ci], 0, 0, 0);
+        }
+    }
+    __syncthreads();
+
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem + TAB_BYTES);
+    const bool split = args.S > 1;
+
+    // The body is straight-line apart from uniform branches that skip the
+    // decode of tiles past the sequence: every load is issued on every path, so
+    // the in-flight ring survives the loop (no register copies, no early waits).
+    for (int t0 = 0; t0 < T; t0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int t = t0 + u;
+            const int ci = u % C;
+            const int i = t / C;   // block number in this workgroup's sequence
+            if (ci == 0) {
+                // start of block i: build the table of block i+1, then fetch the
+                // table rows of block i+1+LR into the slot just used.
+                const int q = (u / C + 1) % LR;
+                tab_build((i + 1) & 1, lq0[q], lq1[q], llo[q]);
+                lut_load(i + 1 + LR, lq0[q], lq1[q], llo[q]);
+            }
+            if (t < T) {
+                // decode tile t
+                const u32x4_t p = pb[u];
+                const float a = bf16_to_f32(ab[u]);
+                const float bt = bf16_to_f32(bbv[u]);
+                const uint32_t slot4 = static_cast<uint32_t>((i & 1) * 128 + (lane & 31) * 4);
+                f32x4_t ag = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    u32x4_t bw;
+                    bw[0] = lds_word(smem, tab_addr(p[s4], slot4, 0));
+                    bw[1] = lds_word(smem, tab_addr(p[s4], slot4, 1));
+                    bw[2] = lds_word(smem, tab_addr(p[s4], slot4, 2));
+                    bw[3] = lds_word(smem, tab_addr(p[s4], slot4, 3));
+                    ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, xr[ci][s4]), __builtin_bit_cast(bf16x8_t, bw),
+                        ag, 0, 0, 0);
+                }
+#pragma unroll
+                for (int v = 0; v < VC; ++v)
+                    acc[v] = fmaf(a, ag[v], fmaf(bt, xs[ci][v], acc[v]));
+            }
+            issue(u, t + D);
+            if (ci == C - 1) {
+                // end of block i: partial sums of the 8 waves meet in LDS
+                red[((i & 1) * GW + wave) * 64 + lane] = acc;
+                acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                __syncthreads();
+                if (wave == i % GW && i < nblk) {
+                    f32x4_t tot = red[((i & 1) * GW) * 64 + lane];
+#pragma unroll
+                    for (int w = 1; w < GW; ++w) {
+                        const f32x4_t o = red[((i & 1) * GW + w) * 64 + lane];
+#pragma unroll
+                        for (int v = 0; v < VC; ++v)
+                            tot[v] += o[v];
+                    }
+                    const int b = r + i * args.Gp;
+                    if (!split) {
+                        const int n = b * TILE_ROWS + j;
+#pragma unroll
+                        for (int v = 0; v < VC; ++v) {
+                            const int m = kq * 4 + v;
+                            if (m < M && n < N)
+                                args.y[static_cast<size_t>(m) * N + n] =
+                                    static_cast<uint16_t>(f32_to_bf16(tot[v]));
+                        }
+                    } else {
+                        float* pp =
+                            args.part + ((static_cast<size_t>(s) * NB + b) * 64 + lane) * VC;
+#pragma unroll
+                        for (int v = 0; v < VC; ++v)
+                            pp[v] = tot[v];
+                    }
+                }
             }
         }
-        __syncthreads();
+    }
 
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        const uint8_t* prow = packed + static_cast<size_t>(nr) * (K / 2) + kq * 16;
-        const uint16_t* xr = x + static_cast<size_t>(has_x ? j : 0) * K + kq * 32;
-        const uint16_t* arow = alpha + static_cast<size_t>(nr) * G;
-        const uint16_t* brow = beta + static_cast<size_t>(nr) * G;
-        for (int c = c_begin; c < c_end; ++c) {
-            const uint4 p = *reinterpret_cast<const uint4*>(prow + static_cast<size_t>(c) * 64);
-            u32x4_t xa[4];
-            if (has_x) {
-                const uint4* xp = reinterpret_cast<const uint4*>(xr + static_cast<size_t>(c) * CHUNK_K);
+    if (!split)
+        return;
+    // ---- split K: the last workgroup to finish a block sums its S parts in order.
+    for (int i = wave; i < nblk; i += GW) {
+        const int b = r + i * args.Gp;
+        __threadfence();
+        uint32_t old = 0;
+        if (lane == 0)
+            old = atomicAdd(args.count + b, 1u);
+        old = __builtin_amdgcn_readfirstlane(old);
+        if (old != static_cast<uint32_t>(args.S - 1))
+            continue;
+        __threadfence();
+        float tot[VC];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const uint4 v = xp[s];
-                    xa[s] = u32x4_t{v.x, v.y, v.z, v.w};
-                }
-            } else {
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    xa[s] = u32x4_t{0u, 0u, 0u, 0u};
-            }
-            const uint32_t pd[4] = {p.x, p.y, p.z, p.w};
-            f32x4_t accg = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                u32x4_t b;
-                b[0] = tab_read(tab, tab_addr(pd[s], slot4, 0));
-                b[1] = tab_read(tab, tab_addr(pd[s], slot4, 1));
-                b[2] = tab_read(tab, tab_addr(pd[s], slot4, 2));
-                b[3] = tab_read(tab, tab_addr(pd[s], slot4, 3));
-                accg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, xa[s]), __builtin_bit_cast(bf16x8_t, b), accg,
-                    0, 0, 0);
-            }
-            const int grp = c / cpg;
-            const float a = bf16_to_f32(arow[grp]);
-            const uint32_t bb = brow[grp];
-            const uint32_t b2 = bb | (bb << 16);
-            const u32x4_t bv = {b2, b2, b2, b2};
+        for (int v = 0; v < VC; ++v)
+            tot[v] = 0.f;
+        for (int sp = 0; sp < args.S; ++sp) {
+            const float* pp = args.part + ((static_cast<size_t>(sp) * NB + b) * 64 + lane) * VC;
 #pragma unroll
             for (int v = 0; v < VC; ++v)
-                acc[v] = fmaf(a, accg[v], acc[v]);
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, xa[s]), __builtin_bit_cast(bf16x8_t, bv), acc, 0,
-                    0, 0);
+                tot[v] += __builtin_nontemporal_load(pp + v);
         }
-
-        __syncthreads();   // every wave is done with the table
-        f32x4_t* red = reinterpret_cast<f32x4_t*>(tab);
-        red[wave * 64 + lane] = acc;
-        __syncthreads();
-        for (int t = threadIdx.x; t < TILE_N * MT; t += GEMM_THREADS) {
-            const int m = t >> 4, jj = t & 15;
-            const int l = ((m >> 2) << 4) | jj, v = m & 3;
-            float s = 0.f;
+        const int n = b * TILE_ROWS + j;
 #pragma unroll
-            for (int w = 0; w < GEMM_WAVES; ++w)
-                s += red[w * 64 + l][v];
-            if (m < M && n0 + jj < N)
-                y[static_cast<size_t>(m) * N + n0 + jj] = static_cast<uint16_t>(f32_to_bf16(s));
+        for (int v = 0; v < VC; ++v) {
+            const int m = kq * 4 + v;
+            if (m < M && n < N)
+                args.y[static_cast<size_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16(tot[v]));
         }
+        // leave this block's part of the workspace zero again, counter included
+        for (int sp = 0; sp < args.S; ++sp) {
+            float* pp = args.part + ((static_cast<size_t>(sp) * NB + b) * 64 + lane) * VC;
+#pragma unroll
+            for (int v = 0; v < VC; ++v)
+                pp[v] = 0.f;
+        }
+        if (lane == 0)
+            args.count[b] = 0u;
     }
 }
 
@@ -277,34 +464,72 @@ bool aligned(const void* p, uintptr_t a)
 
 bool group_ok(int64_t K, int64_t g)
 {
-    return g > 0 && g % 128 == 0 && K >= 0 && K % g == 0;
+    return g > 0 && g % TILE_K == 0 && K >= 0 && K % g == 0;
 }
 
-constexpr int MAX_DEVICES = 64;
-int g_cu_count[MAX_DEVICES];   // 0 = not queried yet
-
-any4_status cu_count(int* out)
+int64_t row_blocks(int64_t N)
 {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return ANY4_E_HIP;
-    if (dev >= 0 && dev < MAX_DEVICES && g_cu_count[dev] > 0) {
-        *out = g_cu_count[dev];
-        return ANY4_OK;
-    }
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        return ANY4_E_HIP;
-    if (dev >= 0 && dev < MAX_DEVICES)
-        g_cu_count[dev] = cus;
-    *out = cus;
-    return ANY4_OK;
+    return (N + TILE_ROWS - 1) / TILE_ROWS;
 }
 
 any4_status launched()
 {
     return hipGetLastError() == hipSuccess ? ANY4_OK : ANY4_E_HIP;
+}
+
+// How a GEMM is split: C chunks per wave, S parts of K, Gp workgroups per part.
+struct Plan {
+    int C, S, Gp;
+};
+
+constexpr int PLAN_CUS = 256;   // the split is planned for a full MI355X
+
+Plan plan_for(int64_t N, int64_t K)
+{
+    const int64_t Kc = K / TILE_K, NB = row_blocks(N);
+    Plan best{4, 1, 1};
+    double best_cost = 1e30;
+    for (int C : {4, 2, 1}) {
+        const int64_t S = (Kc + GW * C - 1) / (GW * C);
+        int64_t Gp = PLAN_CUS / S;
+        if (Gp < 1)
+            Gp = 1;
+        if (Gp > NB)
+            Gp = NB;
+        const int64_t rounds = (NB + Gp - 1) / Gp;
+        // time of one workgroup: rounds x (C tiles + table build and barrier);
+        // a split adds the partial-sum traffic and the final sum.
+        const double cost = rounds * (C + 0.5) + (S > 1 ? 1.0 : 0.0);
+        if (cost < best_cost - 1e-9) {
+            best_cost = cost;
+            best = Plan{C, static_cast<int>(S), static_cast<int>(Gp)};
+        }
+    }
+    return best;
+}
+
+size_t split_bytes(int64_t M, int64_t N, const Plan& p, size_t* count_off)
+{
+    if (p.S <= 1) {
+        *count_off = 0;
+        return 0;
+    }
+    const int64_t NB = row_blocks(N);
+    const int64_t VC = M < 4 ? M : 4;
+    const size_t part = static_cast<size_t>(p.S) * NB * 64 * VC * sizeof(float);
+    *count_off = (part + 255) & ~static_cast<size_t>(255);
+    return *count_off + static_cast<size_t>(NB) * sizeof(uint32_t);
+}
+
+template <int MT>
+void launch_gemm(const Plan& p, const GemmArgs& a, hipStream_t stream)
+{
+    const dim3 grid(static_cast<unsigned>(p.S * p.Gp)), block(GT);
+    switch (p.C) {
+    case 4: hipLaunchKernelGGL((k_gemm<MT, 4, 8, 2>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_gemm<MT, 2, 8, 2>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((k_gemm<MT, 1, 8, 2>), grid, block, 0, stream, a); break;
+    }
 }
 
 }  // namespace
@@ -319,8 +544,9 @@ const char* any4_status_string(any4_status s)
     switch (s) {
     case ANY4_OK: return "ANY4_OK: success";
     case ANY4_E_NULL: return "ANY4_E_NULL: a required pointer is NULL";
-    case ANY4_E_SHAPE: return "ANY4_E_SHAPE: unsupported sizes (negative size, odd K, g not a "
-                              "positive multiple of 128, K % g != 0, or M > 16)";
+    case ANY4_E_SHAPE: return "ANY4_E_SHAPE: unsupported sizes (negative size, K not a multiple "
+                              "of 128, g not a positive multiple of 128, K % g != 0, M > 16, "
+                              "or buffers of 2 GiB or more)";
     case ANY4_E_ALIGN: return "ANY4_E_ALIGN: a base pointer is not aligned as required";
     case ANY4_E_WORKSPACE: return "ANY4_E_WORKSPACE: workspace too small";
     case ANY4_E_HIP: return "ANY4_E_HIP: the HIP runtime reported an error";
@@ -328,25 +554,32 @@ const char* any4_status_string(any4_status s)
     return "any4: unknown status";
 }
 
+size_t any4_packed_bytes(int64_t N, int64_t K)
+{
+    if (N < 0 || K < 0 || K % TILE_K != 0)
+        return 0;
+    return static_cast<size_t>(row_blocks(N)) * TILE_ROWS * static_cast<size_t>(K / 2);
+}
+
 any4_status any4_pack(const uint8_t* idx, uint8_t* packed, int64_t N, int64_t K,
                       hipStream_t stream)
 {
-    if (N < 0 || K < 0 || K % 2 != 0)
+    if (N < 0 || K < 0 || K % TILE_K != 0)
         return ANY4_E_SHAPE;
     if (N == 0 || K == 0)
         return ANY4_OK;
+    if (any4_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31) ||
+        static_cast<size_t>(N) * K >= (static_cast<size_t>(1) << 40))
+        return ANY4_E_SHAPE;
     if (!idx || !packed)
         return ANY4_E_NULL;
     if (!aligned(idx, 16) || !aligned(packed, 16))
         return ANY4_E_ALIGN;
-    const size_t nout = static_cast<size_t>(N) * static_cast<size_t>(K / 2);
-    const size_t threads = (nout + 15) / 16;
-    const size_t blocks = (threads + PACK_THREADS - 1) / PACK_THREADS;
-    if (blocks > 0x7FFFFFFFu)
-        return ANY4_E_SHAPE;
+    const uint32_t slots = static_cast<uint32_t>(any4_packed_bytes(N, K) / 16);
+    const uint32_t blocks = (slots + PACK_THREADS - 1) / PACK_THREADS;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(k_pack, dim3(static_cast<unsigned>(blocks)), dim3(PACK_THREADS), 0, stream,
-                       idx, packed, nout);
+    hipLaunchKernelGGL(k_pack, dim3(blocks), dim3(PACK_THREADS), 0, stream, idx, packed,
+                       static_cast<int>(N), static_cast<int>(K), slots);
     return launched();
 }
 
@@ -358,28 +591,30 @@ any4_status any4_dequant(const uint8_t* packed, const uint16_t* lut, const uint1
         return ANY4_E_SHAPE;
     if (N == 0 || K == 0)
         return ANY4_OK;
+    if (any4_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31))
+        return ANY4_E_SHAPE;
     if (!packed || !lut || !alpha || !beta || !w)
         return ANY4_E_NULL;
-    if (!aligned(packed, 16) || !aligned(lut, 16) || !aligned(w, 16) || !aligned(alpha, 2) ||
+    if (!aligned(packed, 16) || !aligned(w, 16) || !aligned(lut, 2) || !aligned(alpha, 2) ||
         !aligned(beta, 2))
         return ANY4_E_ALIGN;
-    const size_t units = static_cast<size_t>(N) * static_cast<size_t>(K) / DQ_PER_THREAD;
-    const size_t blocks = (units + DQ_THREADS - 1) / DQ_THREADS;
-    if (blocks > 0x7FFFFFFFu)
-        return ANY4_E_SHAPE;
+    const int64_t Kc = K / TILE_K;
+    const int64_t blocks = row_blocks(N) * ((Kc + DQ_WAVES - 1) / DQ_WAVES);
     (void)hipGetLastError();
-    hipLaunchKernelGGL(k_dequant, dim3(static_cast<unsigned>(blocks)), dim3(DQ_THREADS), 0, stream,
-                       packed, lut, alpha, beta, w, K, g, units);
+    hipLaunchKernelGGL(k_dequant, dim3(static_cast<unsigned>(blocks)), dim3(64 * DQ_WAVES), 0,
+                       stream, packed, lut, alpha, beta, w, static_cast<int>(N),
+                       static_cast<int>(K), static_cast<int>(g));
     return launched();
 }
 
 size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g)
 {
-    (void)M;
-    (void)N;
-    (void)K;
-    (void)g;
-    return 0;
+    if (M <= 0 || M > 16 || N <= 0 || K <= 0 || !group_ok(K, g))
+        return 0;
+    if (any4_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31))
+        return 0;
+    size_t off = 0;
+    return split_bytes(M, N, plan_for(N, K), &off);
 }
 
 any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
@@ -387,43 +622,59 @@ any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* 
                       int64_t N, int64_t K, int64_t g, void* workspace, size_t workspace_bytes,
                       hipStream_t stream)
 {
-    (void)workspace;
     if (M < 0 || M > 16 || N < 0 || !group_ok(K, g))
         return ANY4_E_SHAPE;
-    if (N > 0x7FFFFFFF / 16 || K > 0x7FFFFFFF / 2 || N * (K / g) > 0x7FFFFFFF)
+    if (any4_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31) ||
+        static_cast<size_t>(M) * K * 2 >= (static_cast<size_t>(1) << 31))
         return ANY4_E_SHAPE;
     if (M == 0 || N == 0)
         return ANY4_OK;
-    if (!lut || !y || (K > 0 && (!x || !packed || !alpha || !beta)))
+    if (!y || (K > 0 && (!x || !packed || !lut || !alpha || !beta)))
         return ANY4_E_NULL;
-    if (!aligned(lut, 16) || !aligned(y, 2) ||
-        (K > 0 && (!aligned(x, 16) || !aligned(packed, 16) || !aligned(alpha, 2) ||
-                   !aligned(beta, 2))))
+    if (!aligned(y, 2) || (K > 0 && (!aligned(x, 16) || !aligned(packed, 16) ||
+                                     !aligned(lut, 16) || !aligned(alpha, 2) ||
+                                     !aligned(beta, 2))))
         return ANY4_E_ALIGN;
-    if (workspace_bytes < any4_gemm_workspace_size(M, N, K, g))
-        return ANY4_E_WORKSPACE;
-    int cus = 0;
-    if (cu_count(&cus) != ANY4_OK)
-        return ANY4_E_HIP;
-    const int ntiles = static_cast<int>((N + TILE_N - 1) / TILE_N);
-    const int grid = ntiles < 2 * cus ? ntiles : 2 * cus;   // 64 KB of LDS: 2 per CU
     (void)hipGetLastError();
-    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K),
-              gg = static_cast<int>(g);
-#define ANY4_LAUNCH(MT)                                                                         \
-    hipLaunchKernelGGL(k_gemm<MT>, dim3(grid), dim3(GEMM_THREADS), 0, stream, x, packed, lut,    \
-                       alpha, beta, y, m, n, k, gg)
+    if (K == 0) {
+        const size_t n = static_cast<size_t>(M) * N;
+        hipLaunchKernelGGL(k_zero, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                           stream, y, n);
+        return launched();
+    }
+    const Plan p = plan_for(N, K);
+    size_t count_off = 0;
+    const size_t need = split_bytes(M, N, p, &count_off);
+    if (workspace_bytes < need)
+        return ANY4_E_WORKSPACE;
+    if (need > 0 && (!workspace || !aligned(workspace, 256)))
+        return workspace ? ANY4_E_ALIGN : ANY4_E_NULL;
+    GemmArgs a;
+    a.x = x;
+    a.packed = packed;
+    a.lut = lut;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.y = y;
+    a.part = need ? static_cast<float*>(workspace) : nullptr;
+    a.count = need ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + count_off)
+                   : nullptr;
+    a.M = static_cast<int>(M);
+    a.N = static_cast<int>(N);
+    a.K = static_cast<int>(K);
+    a.g = static_cast<int>(g);
+    a.S = p.S;
+    a.Gp = p.Gp;
     if (M == 1)
-        ANY4_LAUNCH(1);
+        launch_gemm<1>(p, a, stream);
     else if (M == 2)
-        ANY4_LAUNCH(2);
+        launch_gemm<2>(p, a, stream);
     else if (M <= 4)
-        ANY4_LAUNCH(4);
+        launch_gemm<4>(p, a, stream);
     else if (M <= 8)
-        ANY4_LAUNCH(8);
+        launch_gemm<8>(p, a, stream);
     else
-        ANY4_LAUNCH(16);
-#undef ANY4_LAUNCH
+        launch_gemm<16>(p, a, stream);
     return launched();
 }
 

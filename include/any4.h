@@ -10,20 +10,30 @@
  *
  * Conventions shared by every call
  *   - All data pointers are DEVICE pointers owned by the caller.  The library
- *     allocates nothing, keeps no per-call state and may be called from several
+ *     allocates nothing, keeps no global state and may be called from several
  *     host threads.  Buffers must stay alive until the work on `stream`
  *     completes.
- *   - bf16 values travel as uint16_t bit patterns.  Arrays are dense and
- *     row-major:
+ *   - bf16 values travel as uint16_t bit patterns.  Dense row-major arrays:
  *         idx     [N][K]    uint8, values 0..15 (only the low 4 bits are read)
- *         packed  [N][K/2]  uint8, byte j of a row holds index 2j in bits 0..3
- *                           and index 2j+1 in bits 4..7
  *         lut     [N][16]   bf16, lut[n][i] is the value of index i in row n
  *         alpha   [N][K/g]  bf16, scale of weights k in [j*g, (j+1)*g) of row n
  *         beta    [N][K/g]  bf16, offset of the same group
  *         x       [M][K]    bf16 activations
  *         y       [M][N]    bf16 output
  *         w       [N][K]    bf16 dequantised weights
+ *   - packed: the indices, two per byte, in tiles of 16 rows x 128 k
+ *     (any4_packed_bytes(N, K) bytes; the tile layout is the library's, made
+ *     so that one tile is one 16-byte load per lane of a 64-lane wave):
+ *         tile (b, c) covers rows 16b..16b+15 and k 128c..128c+127 and starts
+ *         at byte (b * K/128 + c) * 1024;
+ *         byte 16*l + i of a tile (lane l = 0..63, i = 0..15) holds, for row
+ *         n = 16b + (l % 16) and k = 128c + 32*(l / 16) + 2i,
+ *             idx[n][k] in bits 0..3 and idx[n][k+1] in bits 4..7;
+ *         rows n >= N (the last block when N % 16 != 0) are zero bytes.
+ *     Equivalently: take the row-major nibble packing P[n][j] = idx[n][2j] |
+ *     idx[n][2j+1] << 4, pad N up to a multiple of 16 with zero rows, view it
+ *     as [N/16][16][K/128][4][16] and store it transposed to
+ *     [N/16][K/128][4][16][16].
  *   - Calls are asynchronous on `stream` (0 = the default stream).  They
  *     return before the GPU work finishes; device faults show up at the
  *     caller's next synchronisation.
@@ -31,10 +41,12 @@
  *     nothing is launched and every output is left untouched.
  *   - Outputs must not overlap inputs.  They are fully overwritten (no
  *     accumulate mode).
- *   - Group size: g must be a positive multiple of 128 and divide K
- *     (K = 0 is allowed where stated).  This covers g = 128 .. 1024.
- *   - Alignment: x, packed, lut and w need 16-byte aligned base pointers;
- *     idx needs 16 bytes as well; alpha, beta and y need 2 bytes.
+ *   - K must be a multiple of 128.  Group size: g must be a positive multiple
+ *     of 128 that divides K (g = 128 .. 1024 are the sizes tested).  Every
+ *     buffer must be smaller than 2 GiB.
+ *   - Alignment: x, idx, packed and w need 16-byte aligned base pointers;
+ *     lut needs 16 bytes for any4_gemm and 2 for any4_dequant; alpha, beta and
+ *     y need 2 bytes; the any4_gemm workspace needs 256 bytes.
  */
 #ifndef ANY4_H
 #define ANY4_H
@@ -50,20 +62,27 @@ extern "C" {
 typedef enum any4_status {
     ANY4_OK = 0,
     ANY4_E_NULL = 1,      /* a required pointer is NULL                               */
-    ANY4_E_SHAPE = 2,     /* a size is negative, K is odd, g is not a positive multiple
-                             of 128, K % g != 0, or M > 16 (any4_gemm)                */
+    ANY4_E_SHAPE = 2,     /* a size is negative, K is not a multiple of 128, g is not a
+                             positive multiple of 128, K % g != 0, M > 16 (any4_gemm),
+                             or a buffer would be 2 GiB or larger                     */
     ANY4_E_ALIGN = 3,     /* a base pointer misses the alignment stated above          */
     ANY4_E_WORKSPACE = 4, /* workspace smaller than any4_gemm_workspace_size()         */
     ANY4_E_HIP = 5        /* the HIP runtime refused a query or a launch               */
 } any4_status;
 
 /*
- * any4_pack -- pack 4-bit indices two per byte (the layout above).
+ * any4_packed_bytes -- size in bytes of the packed tiles of an N x K weight
+ * matrix: ceil(N/16) * 16 * K/2.  Returns 0 when N < 0, K < 0 or K % 128 != 0.
+ */
+size_t any4_packed_bytes(int64_t N, int64_t K);
+
+/*
+ * any4_pack -- pack 4-bit indices two per byte into the tile layout above.
  * The offline step before inference, the counterpart of the "weights laid out
  * ahead of time" that the explainer's section 三 describes for its kernel.
  *   idx     device, [N][K] uint8, read-only; bits 4..7 of each byte are ignored.
- *   packed  device, [N][K/2] uint8, written.
- *   N, K    N >= 0, K >= 0 and even.  N*K == 0 is a no-op.
+ *   packed  device, any4_packed_bytes(N, K) bytes, written (padding included).
+ *   N, K    N >= 0, K >= 0, K % 128 == 0.  N*K == 0 is a no-op.
  * Errors: ANY4_E_SHAPE, ANY4_E_NULL, ANY4_E_ALIGN (idx or packed not 16-byte
  * aligned), ANY4_E_HIP.
  */
@@ -89,6 +108,8 @@ any4_status any4_dequant(const uint8_t* packed, const uint16_t* lut, const uint1
 /*
  * any4_gemm_workspace_size -- bytes of device workspace any4_gemm needs for
  * this shape (0 when it needs none).  Returns 0 for shapes any4_gemm rejects.
+ * The workspace holds per-part partial sums and one arrival counter per
+ * 16-row block for the shapes where K is split across workgroups.
  */
 size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
 
@@ -96,20 +117,24 @@ size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
  * any4_gemm -- y = x * W^T with W the any4 weights above, for M = 1..16
  * (the explainer's section 三: decode batches of 1..16):
  *     y[m][n] = bf16_rne( sum_k x[m][k] * (alpha[n][k/g] * lut[n][idx[n][k]] + beta[n][k/g]) )
- * The weights are never written out: each group contributes
- * alpha * sum_k x*lut[idx] + beta * sum_k x, accumulated in fp32.  Any
- * summation order is allowed; the result is within
+ * The weights are never written out: each 128-k chunk of a group contributes
+ * alpha * sum_k x*lut[idx] + beta * sum_k x, accumulated in fp32.  The result
+ * is within
  *     |y - y_ref| <= 2e-3 * sum_k |x[m][k] * w[n][k]| + 1e-3
  * of the fp64 product with the bf16 dequantised weights for the workloads this
- * library is tested on.  Runs are deterministic (same inputs, same bits).
+ * library is tested on.  Runs are deterministic (same inputs, same bits): the
+ * summation order depends only on the shape.
  *   x                         device, [M][K] bf16, read-only.
  *   packed, lut, alpha, beta  device, read-only.
  *   y                         device, [M][N] bf16, written.
  *   M in 0..16, N >= 0, K >= 0 with K % g == 0.  M*N == 0 is a no-op;
- *   K == 0 writes y = 0 (x, packed, alpha and beta may then be NULL).
+ *   K == 0 writes y = 0 (x, packed, lut, alpha and beta may then be NULL).
  *   workspace, workspace_bytes  device scratch of at least
- *       any4_gemm_workspace_size(M, N, K, g) bytes (NULL/0 when that is 0);
- *       its contents on entry do not matter.
+ *       any4_gemm_workspace_size(M, N, K, g) bytes (NULL/0 when that is 0).
+ *       It must be all zero bytes before its first use; every call that
+ *       completes leaves it all zero again, so one zeroed workspace serves any
+ *       number of calls.  Calls that may run at the same time need separate
+ *       workspaces.
  * Errors: ANY4_E_SHAPE, ANY4_E_NULL, ANY4_E_ALIGN, ANY4_E_WORKSPACE, ANY4_E_HIP.
  */
 any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,

@@ -8,7 +8,9 @@ never does.
 All bf16 data is passed as ``uint16`` bit patterns.  Layouts are dense
 row-major: idx ``[N, K]`` u8, packed ``[N, K/2]`` u8 (byte j holds index 2j in
 bits 0..3 and 2j+1 in bits 4..7), lut ``[N, 16]``, alpha/beta ``[N, K/g]``,
-x ``[M, K]``, w ``[N, K]``.
+x ``[M, K]``, w ``[N, K]``.  ``tile``/``untile`` convert the row-major
+packing to and from the GPU library's tile layout, written here from the
+layout's written specification (include/any4.h), not from the kernels.
 
 What each function follows (the pages, by title and section):
   * the 10100.com any4 explainer, section 二: a row is 4-bit indices plus a
@@ -117,6 +119,44 @@ def unpack(packed, K: int) -> np.ndarray:
     out = np.empty((N, K), np.uint8)
     _load().orc_unpack(_ptr(packed), _ptr(out), N, K)
     return out
+
+
+# --------------------------------------------------------------------------
+# the GPU library's tile layout (16 rows x 128 k per 1 KB tile)
+# --------------------------------------------------------------------------
+TILE_ROWS = 16
+TILE_K = 128
+
+
+def tiled_bytes(N: int, K: int) -> int:
+    """Bytes of the tile layout: rows padded to a multiple of 16, K/2 bytes each."""
+    return -(-N // TILE_ROWS) * TILE_ROWS * (K // 2)
+
+
+def tile(packed) -> np.ndarray:
+    """Row-major packed [N, K/2] -> tile layout (flat uint8).
+
+    Pad the rows with zero rows to a multiple of 16, view the bytes as
+    [N/16 blocks][16 rows][K/128 chunks][4 quarters][16 bytes] and store them
+    in the order [blocks][chunks][quarters][rows][bytes]."""
+    packed = _c(packed, np.uint8)
+    N, K2 = packed.shape
+    K = 2 * K2
+    assert K % TILE_K == 0
+    NB = -(-N // TILE_ROWS)
+    P = np.zeros((NB * TILE_ROWS, K2), np.uint8)
+    P[:N] = packed
+    t = P.reshape(NB, TILE_ROWS, K // TILE_K, 4, 16).transpose(0, 2, 3, 1, 4)
+    return np.ascontiguousarray(t).reshape(-1)
+
+
+def untile(t, N: int, K: int) -> np.ndarray:
+    """Inverse of tile: tile layout -> row-major packed [N, K/2] (padding dropped)."""
+    t = _c(t, np.uint8)
+    NB = -(-N // TILE_ROWS)
+    assert t.size == NB * TILE_ROWS * (K // 2)
+    P = t.reshape(NB, K // TILE_K, 4, TILE_ROWS, 16).transpose(0, 3, 1, 2, 4)
+    return np.ascontiguousarray(P).reshape(NB * TILE_ROWS, K // 2)[:N].copy()
 
 
 def dequant_one(alpha: int, lut_value: int, beta: int) -> int:

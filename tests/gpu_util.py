@@ -41,8 +41,10 @@ class Layer:
     def __init__(self, inp: workloads.Any4Inputs, packed_host=None):
         self.inp = inp
         self.N, self.K, self.g = inp.N, inp.K, inp.g
+        # row-major packing for the oracle; the device gets the same bytes in
+        # the library's tile layout, both produced by the oracle
         self.packed_host = oracle.pack(inp.idx) if packed_host is None else packed_host
-        self.packed = dev_u8(self.packed_host)
+        self.packed = dev_u8(oracle.tile(self.packed_host))
         self.lut = dev_b16(inp.lut)
         self.alpha = dev_b16(inp.alpha)
         self.beta = dev_b16(inp.beta)

@@ -65,17 +65,34 @@ def test_empty_calls_are_no_ops():
     assert any4.gemm_raw(None, None, None, None, None, None, 0, 16, 128, 128, stream=0) == 0
     assert any4.gemm_raw(None, None, None, None, None, None, 4, 0, 128, 128, stream=0) == 0
     assert any4.dequant_raw(None, None, None, None, None, 0, 128, 128, stream=0) == 0
-    assert any4.pack_raw(None, None, 0, 64, stream=0) == 0
+    assert any4.pack_raw(None, None, 0, 128, stream=0) == 0
     assert any4.pack_raw(None, None, 8, 0, stream=0) == 0
 
 
 def test_pack_and_dequant_errors():
     assert any4.pack_raw(A, A, 4, 7, stream=0) == 2
-    assert any4.pack_raw(None, A, 4, 8, stream=0) == 1
-    assert any4.pack_raw(A + 1, A, 4, 8, stream=0) == 3
+    assert any4.pack_raw(A, A, 4, 64, stream=0) == 2      # K must be a multiple of 128
+    assert any4.pack_raw(None, A, 4, 128, stream=0) == 1
+    assert any4.pack_raw(A + 1, A, 4, 128, stream=0) == 3
     assert any4.dequant_raw(A, A, A, A, A, 4, 256, 192, stream=0) == 2
     assert any4.dequant_raw(A, A, None, A, A, 4, 256, 128, stream=0) == 1
     assert any4.dequant_raw(A, A, A, A, A + 2, 4, 256, 128, stream=0) == 3
+
+
+def test_packed_bytes():
+    assert any4.packed_bytes(16, 128) == 1024
+    assert any4.packed_bytes(17, 128) == 2048        # rows padded to a multiple of 16
+    assert any4.packed_bytes(14336, 4096) == 14336 * 2048
+    assert any4.packed_bytes(5, 100) == 0            # K not a multiple of 128
+    assert any4.packed_bytes(-1, 128) == 0
+
+
+def test_gemm_workspace_errors():
+    # a shape that splits K needs a workspace: none given -> ANY4_E_WORKSPACE
+    need = any4.workspace_size(1, 64, 16384, 128)
+    assert need > 0
+    assert any4.gemm_raw(A, A, A, A, A, A, 1, 64, 16384, 128, None, 0, stream=0) == 4
+    assert any4.gemm_raw(A, A, A, A, A, A, 1, 64, 16384, 128, A + 16, need, stream=0) == 3
 
 
 def test_workspace_size_is_defined_for_all_shapes():

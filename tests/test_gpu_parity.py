@@ -41,16 +41,19 @@ def test_pack_bitexact_configs(cfg):
     idx = gu.dev_u8(L.inp.idx)
     packed = any4.pack(idx)
     torch.cuda.synchronize()
-    assert np.array_equal(packed.cpu().numpy(), L.packed_host)
+    assert np.array_equal(packed.cpu().numpy(), oracle.tile(L.packed_host))
 
 
-@pytest.mark.parametrize("N,K", [(1, 2), (3, 30), (7, 34), (5, 1000), (64, 4098), (1, 32)])
+@pytest.mark.parametrize("N,K", [(1, 128), (3, 256), (7, 384), (17, 1024), (64, 4096),
+                                 (33, 128), (1000, 640)])
 def test_pack_ragged(N, K):
     rng = np.random.default_rng(N * 1000 + K)
     idx = rng.integers(0, 256, size=(N, K), dtype=np.uint8)   # high bits must be ignored
-    packed = any4.pack(gu.dev_u8(idx))
+    # the padding rows of the last block must come out zero, whatever was there
+    packed = torch.full((any4.packed_bytes(N, K),), 0xA5, dtype=torch.uint8, device=gu.DEV)
+    any4.pack(gu.dev_u8(idx), out=packed)
     torch.cuda.synchronize()
-    assert np.array_equal(packed.cpu().numpy(), oracle.pack(idx))
+    assert np.array_equal(packed.cpu().numpy(), oracle.tile(oracle.pack(idx)))
 
 
 # --------------------------------------------------------------------------
@@ -156,6 +159,43 @@ def test_gemm_ragged(M, N, K, g):
     gu.assert_within_bound(y, y_ref, ad, f"ragged {M}x{N}x{K} g{g}")
 
 
+# K split over workgroups: each 16-row block is summed from several parts by
+# whichever workgroup finishes it last, through the zeroed workspace.
+@pytest.mark.parametrize("M,N,K,g", [(1, 64, 16384, 128), (16, 100, 8192, 1024),
+                                     (4, 300, 14336, 1024), (2, 17, 28672, 128),
+                                     (16, 4096, 14336, 1024)])
+def test_gemm_split_k(M, N, K, g):
+    assert any4.workspace_size(M, N, K, g) > 0, "shape expected to split K"
+    inp = workloads.generic(M * 3 + N + K, M, N, K, g)
+    L = gu.Layer(inp)
+    y_ref, ad = oracle.gemm(inp.x, L.w_ref(), nthreads=oracle.default_threads())
+    ws = torch.zeros(any4.workspace_size(M, N, K, g), dtype=torch.uint8, device=gu.DEV)
+    ys = []
+    for _ in range(3):   # the counters must come back to zero after every call
+        ys.append(any4.gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g, workspace=ws))
+    torch.cuda.synchronize()
+    for y in ys:
+        gu.assert_within_bound(y, y_ref, ad, f"split {M}x{N}x{K} g{g}")
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+    assert torch.count_nonzero(ws) == 0   # partial sums and counters cleared again
+
+
+def test_workspace_shared_across_shapes():
+    """One workspace serves calls of different split shapes in any order."""
+    shapes = [(16, 4096, 14336, 1024), (1, 300, 8192, 128), (8, 64, 16384, 128),
+              (16, 4096, 14336, 1024)]
+    need = max(any4.workspace_size(*s) for s in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device=gu.DEV)
+    for i, (M, N, K, g) in enumerate(shapes):
+        inp = workloads.generic(900 + i, M, N, K, g)
+        L = gu.Layer(inp)
+        y = any4.gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g, workspace=ws)
+        torch.cuda.synchronize()
+        y_ref, ad = oracle.gemm(inp.x, L.w_ref(), nthreads=oracle.default_threads())
+        gu.assert_within_bound(y, y_ref, ad, f"shared workspace {M}x{N}x{K} g{g}")
+        assert torch.count_nonzero(ws) == 0
+
+
 # --------------------------------------------------------------------------
 # invariants on the device
 # --------------------------------------------------------------------------
@@ -258,7 +298,7 @@ def test_empty_and_k0():
     any4.gemm(L.x[:0], L.packed, L.lut, L.alpha, L.beta, L.g, out=y)
     # K = 0: an empty sum
     x0 = torch.empty((3, 0), dtype=torch.bfloat16, device=gu.DEV)
-    p0 = torch.empty((L.N, 0), dtype=torch.uint8, device=gu.DEV)
+    p0 = torch.empty((0,), dtype=torch.uint8, device=gu.DEV)
     ab0 = torch.empty((L.N, 0), dtype=torch.bfloat16, device=gu.DEV)
     y0 = torch.full((3, L.N), 7.0, dtype=torch.bfloat16, device=gu.DEV)
     any4.gemm(x0, p0, L.lut, ab0, ab0, 128, out=y0)

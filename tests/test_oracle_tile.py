@@ -1,0 +1,59 @@
+"""Pins of the oracle's tile layout (CPU only).
+
+The tile layout is the GPU library's own (its header states it); the oracle
+restates it with a reshape and a transpose.  Here it is checked against the
+per-byte definition, written out with plain loops, on small inputs."""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _tile_by_definition(idx: np.ndarray) -> np.ndarray:
+    """byte 16*l + i of tile (b, c) = idx[n][k] | idx[n][k+1] << 4 with
+    n = 16b + l % 16 and k = 128c + 32*(l // 16) + 2i; zero for n >= N."""
+    N, K = idx.shape
+    NB, Kc = -(-N // 16), K // 128
+    out = np.zeros(NB * Kc * 1024, np.uint8)
+    for b in range(NB):
+        for c in range(Kc):
+            for l in range(64):
+                n = 16 * b + l % 16
+                if n >= N:
+                    continue
+                for i in range(16):
+                    k = 128 * c + 32 * (l // 16) + 2 * i
+                    lo = int(idx[n, k]) & 15
+                    hi = int(idx[n, k + 1]) & 15
+                    out[(b * Kc + c) * 1024 + 16 * l + i] = lo | (hi << 4)
+    return out
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (16, 128), (17, 256), (37, 384), (48, 512)])
+def test_tile_matches_the_per_byte_definition(N, K):
+    rng = np.random.default_rng(N * 131 + K)
+    idx = rng.integers(0, 256, size=(N, K), dtype=np.uint8)   # high bits are ignored
+    t = oracle.tile(oracle.pack(idx))
+    assert t.size == oracle.tiled_bytes(N, K)
+    assert np.array_equal(t, _tile_by_definition(idx))
+
+
+@pytest.mark.parametrize("N,K", [(5, 128), (33, 640), (64, 1024)])
+def test_untile_inverts_tile(N, K):
+    rng = np.random.default_rng(N + K)
+    p = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    assert np.array_equal(oracle.untile(oracle.tile(p), N, K), p)
+
+
+def test_one_tile_is_contiguous_per_lane():
+    """Lane l of tile (0, 0) holds 32 consecutive k of row l % 16: the first
+    byte pairs indices 32*(l//16) and 32*(l//16)+1."""
+    N, K = 16, 128
+    idx = np.zeros((N, K), np.uint8)
+    for n in range(N):
+        for k in range(K):
+            idx[n, k] = (n + k) % 16
+    t = oracle.tile(oracle.pack(idx))
+    for l in range(64):
+        n, k = l % 16, 32 * (l // 16)
+        assert t[16 * l] == ((n + k) % 16) | (((n + k + 1) % 16) << 4)
