@@ -62,9 +62,10 @@ __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t off
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t load2(__amdgpu_buffer_rsrc_t r, uint32_t off)
+// The same with the non-temporal hint, for data read exactly once (weights).
+__device__ __forceinline__ u32x4_t load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
 }
 
 // ---------------------------------------------------------------------------
@@ -172,38 +173,44 @@ __global__ __launch_bounds__(256) void k_zero(uint16_t* __restrict__ y, size_t n
         y[i] = 0;
 }
 
-// Work split.  A workgroup has 8 waves and stays resident for the whole call
-// (the grid is about one workgroup per CU).  K is cut into S parts of 8*C
-// chunks; wave w of a workgroup always works on the same C chunks of its
-// part, so the x operands of those chunks are loaded once, into VGPRs, and
-// reused for every row block.  The workgroup walks row blocks r, r+Gp, r+2Gp,
-// ... (Gp workgroups per part); for each block its 8 waves decode their chunks
-// and their partial sums meet in LDS.  With S > 1 the parts of a block are
-// summed by whichever workgroup finishes that block last (counter in the
-// workspace), in part order, so results do not depend on timing.
+// Two kernels compute y = x * W^T; both work on 16-row blocks of W, with the
+// 8 waves of a workgroup splitting the block's K and meeting in LDS.
+//
+//   k_gemm_res  (K <= 4096) persistent: about one workgroup per CU walks row
+//               blocks r, r+G, r+2G, ...; wave w always decodes the same 4
+//               chunks of 128 k, so their x operands are loaded once, into
+//               VGPRs, and reused for every block.
+//   k_gemm_str  (any K) one workgroup per row block; a wave decodes K/8 of
+//               the block and loads the x operand of each chunk with the
+//               chunk's tile.
 //
 // Decode.  A packed byte (two indices) selects one dword of a pair table in
 // LDS: entry (hi << 4 | lo) holds (LUT[lo], LUT[hi]) as two bf16, which is
 // exactly one dword of an MFMA B operand.  The table of a row block has 32
 // slots per entry (slot = lane % 32, row = slot % 16); a wave64 LDS read is
 // served as two halves of 32 lanes, so every lane reads its own bank: no
-// conflicts.  Entry e of buffer q sits at byte e*256 + q*128, so the read
-// address is one v_perm of the packed dword.  Two buffers let the waves build
-// the next block's table while they decode the current one.
+// conflicts.  Entry e of table buffer q sits at byte e*256 + q*128, so the
+// read address is one v_perm of the packed dword.
 //
 // Scale and offset.  Per 128-k chunk a lane accumulates sum_k x*LUT[idx] with
-// four MFMAs, then adds alpha times that sum and beta times sum_k x (the chunk
-// sums of x are computed once, with MFMAs against ones).
+// four MFMAs, then adds alpha times that sum, plus beta times sum_k x.
 //
-// Memory.  Each wave keeps the next D tiles of its sequence (plus their alpha
-// and beta) in flight in a register ring, and loads the tables LR blocks
-// ahead.  Every load is a bounds-checked buffer load; where there is nothing
-// to read (past the wave's work, x rows m >= M) its offset is pushed out of
-// range, so no branch guards a load and no traffic is made.
+// Staging.  The table rows (16 x 32 B) and the block's alpha and beta
+// (16 x K/g bf16 each, contiguous in [N][K/g]) are fetched with coalesced
+// 16-byte loads and written to LDS, alpha and beta interleaved as
+// (alpha | beta << 16) dwords, so a lane reads both with one ds_read_b32.
+//
+// Memory.  Each wave keeps the next D tiles of its sequence in flight in a
+// register ring.  Every load is a bounds-checked buffer load whose offset is
+// pushed out of range where there is nothing to read (past the wave's work,
+// x rows m >= M), so no branch guards a load and no traffic is made.  The
+// loop bodies are straight-line apart from uniform branches that skip the
+// decode of tiles past the sequence, so the ring survives the loop.
 constexpr int GW = 8;                   // waves per workgroup
 constexpr int GT = 64 * GW;
 constexpr int TAB_BYTES = 256 * 256;    // 256 entries x 2 buffers x 32 slots x 4 B
-constexpr int RED_BYTES = 2 * GW * 64 * 16;
+constexpr int RES_MAX_K = 4096;         // k_gemm_res: K covered by one workgroup
+constexpr int STR_MAX_G = 512;          // k_gemm_str: K/g up to 512 (two staging rounds)
 
 struct GemmArgs {
     const uint16_t* x;
@@ -212,10 +219,7 @@ struct GemmArgs {
     const uint16_t* alpha;
     const uint16_t* beta;
     uint16_t* y;
-    float* part;        // [S][NB][64][VC] partial sums (S > 1)
-    uint32_t* count;    // [NB] arrival counters, zero between calls (S > 1)
     int M, N, K, g;
-    int S, Gp;
 };
 
 // Byte address of table entry `byte j of d` in the lane's slot: (d.byte[j] << 8) | slot4.
@@ -224,17 +228,152 @@ __device__ __forceinline__ uint32_t tab_addr(uint32_t d, uint32_t slot4, int j)
     return __builtin_amdgcn_perm(d, slot4, 0x0C0C0000u | ((4u + j) << 8));
 }
 
-__device__ __forceinline__ uint32_t lds_word(const uint8_t* smem, uint32_t byte_addr)
+template <typename T>
+__device__ __forceinline__ T& lds_at(uint8_t* smem, uint32_t byte_addr)
 {
-    return *reinterpret_cast<const uint32_t*>(smem + byte_addr);
+    return *reinterpret_cast<T*>(smem + byte_addr);
 }
 
-template <int MT, int C, int D, int LR>
-__global__ __launch_bounds__(GT) void k_gemm(const GemmArgs args)
+// Build table buffer `buf` of one row block from its 16 LUT rows, staged in
+// LDS at `lut_off` as [16 rows][16] bf16.  Thread t of the W*64 writes slot
+// t % 32 (row (t % 32) % 16) of the entries lo + 16*hi, lo = (t / 32) % 16,
+// for its share of the 16 hi.
+template <int W>
+__device__ __forceinline__ void build_table(uint8_t* smem, uint32_t lut_off, int buf, int tid)
 {
-    static_assert(D % C == 0 && (D / C) % LR == 0, "ring sizes");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[TAB_BYTES + RED_BYTES];
-    constexpr int VC = MT < 4 ? MT : 4;   // accumulator rows that can hold a real m
+    constexpr int HPT = 128 / W;   // hi values per thread
+    const int st = tid & 31;
+    const int lo = (tid >> 5) & 15;
+    const int h0 = (tid >> 9) * HPT;
+    const uint32_t row = lut_off + (st & 15) * 32;
+    const u32x4_t q0 = lds_at<u32x4_t>(smem, row);
+    const u32x4_t q1 = lds_at<u32x4_t>(smem, row + 16);
+    const uint32_t ll = lds_at<uint16_t>(smem, row + 2 * lo);
+    const uint32_t Lw[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+    uint32_t* tw = reinterpret_cast<uint32_t*>(smem) + lo * 64 + buf * 32 + st;
+    if constexpr (HPT == 16) {
+#pragma unroll
+        for (int hi = 0; hi < 16; ++hi)
+            tw[hi * 16 * 64] =
+                __builtin_amdgcn_perm(Lw[hi >> 1], ll, (hi & 1) ? 0x07060100u : 0x05040100u);
+    } else {
+#pragma unroll
+        for (int hh = 0; hh < HPT; ++hh) {
+            const int hi = h0 + hh;
+            uint32_t v = Lw[0];
+#pragma unroll
+            for (int q = 1; q < 8; ++q)
+                if (hi >> 1 == q)
+                    v = Lw[q];
+            tw[hi * 16 * 64] = __builtin_amdgcn_perm(v, ll, (hi & 1) ? 0x07060100u : 0x05040100u);
+        }
+    }
+}
+
+// Interleave 8 alpha and 8 beta values (elements 8q .. 8q+7 of the block's
+// [16][G] arrays) into (alpha | beta << 16) dwords stored as [group][row]:
+// the 16 rows of a group are 16 consecutive dwords, so the 16 rows' lanes
+// read 16 different banks.
+__device__ __forceinline__ void store_pairs(uint8_t* smem, uint32_t base, int q, int G,
+                                            const u32x4_t& qa, const u32x4_t& qb)
+{
+    int row = (8 * q) / G;
+    int grp = 8 * q - row * G;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        lds_at<uint32_t>(smem, base + (grp * 16 + row) * 4) =
+            __builtin_amdgcn_perm(qb[i >> 1], qa[i >> 1], sel);
+        if (++grp == G) {
+            grp = 0;
+            ++row;
+        }
+    }
+}
+
+// sum_k x*LUT[idx] over one tile: four MFMAs, B operands looked up in the
+// table through `slot4` (buffer and slot of this lane).
+__device__ __forceinline__ f32x4_t tile_dot(const uint8_t* smem, uint32_t slot4, const u32x4_t& p,
+                                            const u32x4_t (&xa)[4])
+{
+    f32x4_t ag = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+        u32x4_t bw;
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+            bw[jb] = *reinterpret_cast<const uint32_t*>(smem + tab_addr(p[s4], slot4, jb));
+        ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[s4]),
+                                                     __builtin_bit_cast(bf16x8_t, bw), ag, 0, 0,
+                                                     0);
+    }
+    return ag;
+}
+
+// The 8 waves' partial sums of one block, left by each wave in red[wave][lane],
+// summed in wave order; lane l holds y[4*(l/16) + v][n0 + l%16].
+template <int MT, int W>
+__device__ __forceinline__ void store_block(const f32x4_t* red, uint16_t* y, int lane, int M,
+                                            int N, int n0)
+{
+    constexpr int VC = MT < 4 ? MT : 4;
+    f32x4_t tot = red[lane];
+#pragma unroll
+    for (int w = 1; w < W; ++w) {
+        const f32x4_t o = red[w * 64 + lane];
+#pragma unroll
+        for (int v = 0; v < VC; ++v)
+            tot[v] += o[v];
+    }
+    const int n = n0 + (lane & 15);
+#pragma unroll
+    for (int v = 0; v < VC; ++v) {
+        const int m = (lane >> 4) * 4 + v;
+        if (m < M && n < N)
+            y[static_cast<size_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16(tot[v]));
+    }
+}
+
+// ---- k_gemm_res: persistent, x resident in VGPRs (K <= 4096) -------------
+//
+// W waves of C chunks each cover K <= W*C*128 = 4096.  LDS: [0, 64K) tables
+// (2 buffers), red[2][W][64] f32x4, alpha/beta pairs [2][G <= 32][16] dwords,
+// LUT rows [2][16][16] bf16, then (M <= XRMAX) x staging [W][M][C*256 B].
+// Pipeline at the start of block i (all waves), parity P = i & 1 known at
+// compile time (the loop body covers two blocks):
+//   build table (i+1)&1 from LUT rows (i+1)&1          (staged at block i-1)
+//   pairs (i+1)&1   <- alpha/beta registers P^1         (loaded at block i-1)
+//   LUT rows i&1    <- LUT registers P (block i+2)      (loaded at block i-2)
+//   load alpha/beta of block i+3 into registers P^1, LUT of block i+4 into P
+// and the barrier at the end of block i publishes what block i+1 reads.
+template <int W, int C>
+struct ResCfg {
+    static constexpr int T = 64 * W;                  // threads
+    static constexpr int D = 2 * C;                   // ring: two blocks of tiles
+    static constexpr int RED = TAB_BYTES;
+    static constexpr int AB = RED + 2 * W * 64 * 16;
+    static constexpr int AB_BYTES = 16 * (RES_MAX_K / TILE_K) * 4;   // [G <= 32][16] dwords
+    static constexpr int LUT = AB + 2 * AB_BYTES;
+    static constexpr int XS = LUT + 2 * 512;
+    // rows of x that go through LDS on their way to the MFMA operands: a wave
+    // fetches each row of its C*128 k with one full-width load, instead of
+    // 4C loads in which only the M lanes of the operand layout are live
+    static constexpr int XRMAX = W <= 8 ? 8 : 4;
+    template <int MT>
+    static constexpr int x_rows() { return MT <= XRMAX ? MT : 0; }
+    template <int MT>
+    static constexpr int lds() { return XS + W * x_rows<MT>() * C * 256; }
+};
+
+template <int MT, int W, int C>
+__global__ __launch_bounds__(64 * W) void k_gemm_res(const GemmArgs args)
+{
+    using Cfg = ResCfg<W, C>;
+    constexpr int D = Cfg::D;
+    constexpr int VC = MT < 4 ? MT : 4;
+    constexpr int XR = Cfg::template x_rows<MT>();
+    static_assert(W * C * TILE_K == RES_MAX_K, "one part covers K <= 4096");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::template lds<MT>()];
 
     const int M = args.M, N = args.N, K = args.K, g = args.g;
     const int tid = threadIdx.x;
@@ -245,77 +384,123 @@ __global__ __launch_bounds__(GT) void k_gemm(const GemmArgs args)
     const int Kc = K / TILE_K;
     const int NB = (N + TILE_ROWS - 1) / TILE_ROWS;
     const int G = K / g;
-    const int s = blockIdx.x / args.Gp;
-    const int r = blockIdx.x % args.Gp;
-    const int nblk = r < NB ? (NB - 1 - r) / args.Gp + 1 : 0;
-    const int T = nblk * C;                 // tiles in this wave's sequence
-    const int cbase = s * (GW * C) + wave * C;
+    const int Gs = gridDim.x;
+    const int r = blockIdx.x;
+    const int nblk = r < NB ? (NB - 1 - r) / Gs + 1 : 0;
+    const int T = nblk * C;               // tiles in this wave's sequence
+    const int cbase = wave * C;
 
     const __amdgpu_buffer_rsrc_t rp =
         make_rsrc(args.packed, static_cast<uint32_t>(NB) * Kc * TILE_BYTES);
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(args.lut, static_cast<uint32_t>(N) * 32);
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(args.alpha, static_cast<uint32_t>(N) * G * 2);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(args.beta, static_cast<uint32_t>(N) * G * 2);
+    // alpha/beta are staged with 16-byte loads: the range is rounded up to 16 B
+    // (the 16-byte granule holding a valid byte never leaves that byte's page
+    // when the base is 16-byte aligned); the extra values only reach rows >= N.
+    const uint32_t ab_range = (static_cast<uint32_t>(N) * G * 2 + 15u) & ~15u;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(args.alpha, ab_range);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(args.beta, ab_range);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(args.x, static_cast<uint32_t>(M) * K * 2);
 
-    // ---- table rows: thread tid builds slot st (row st % 16), entries lo + 16*hi
-    const int st = tid & 31;
-    const int lo = tid >> 5;   // 0..15
-    u32x4_t lq0[LR], lq1[LR];
-    uint32_t llo[LR];
-    auto lut_load = [&](int i, u32x4_t& q0, u32x4_t& q1, uint32_t& ll) {
-        const uint32_t row = static_cast<uint32_t>(r + i * args.Gp) * TILE_ROWS + (st & 15);
-        const uint32_t off = i < nblk ? row * 32u : OOR;
-        q0 = load16(rl, off);
-        q1 = load16(rl, off + 16);
-        ll = load2(rl, off + 2 * lo);
+    // staging loads of block i: thread t < 32 fetches 16 B of the LUT rows,
+    // thread t < 2G fetches 16 B of alpha and of beta.  Offsets = a per-lane
+    // part (OOR for lanes with nothing to fetch) plus a uniform block part;
+    // blocks past the last one lie past the buffers, so no per-lane select
+    // (which the compiler may turn into branches) is needed.
+    const uint32_t ab_bytes = static_cast<uint32_t>(G) * 32;   // 16 rows x G x 2 B
+    const uint32_t lut_lane = tid < 32 ? static_cast<uint32_t>(tid) * 16 : OOR;
+    const uint32_t ab_lane = static_cast<uint32_t>(tid) * 16 < ab_bytes ? tid * 16 : OOR;
+    auto lut_load = [&](int i) {
+        return load16(rl, lut_lane + static_cast<uint32_t>(r + i * Gs) * 512);
     };
-    auto tab_build = [&](int buf, const u32x4_t& q0, const u32x4_t& q1, uint32_t ll) {
-        const uint32_t Lw[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
-        uint32_t* tw = reinterpret_cast<uint32_t*>(smem) + lo * 64 + buf * 32 + st;
-#pragma unroll
-        for (int hi = 0; hi < 16; ++hi)
-            tw[hi * 16 * 64] = __builtin_amdgcn_perm(Lw[hi >> 1], ll,
-                                                     (hi & 1) ? 0x07060100u : 0x05040100u);
+    auto ab_load = [&](int i, u32x4_t& qa, u32x4_t& qb) {
+        const uint32_t off = ab_lane + static_cast<uint32_t>(r + i * Gs) * ab_bytes;
+        qa = load16(ra, off);
+        qb = load16(rb, off);
+    };
+    auto lut_stage = [&](int buf, const u32x4_t& q) {
+        if (tid < 32)
+            lds_at<u32x4_t>(smem, Cfg::LUT + buf * 512 + tid * 16) = q;
+    };
+    auto ab_stage = [&](int buf, const u32x4_t& qa, const u32x4_t& qb) {
+        if (static_cast<uint32_t>(tid) * 16 < ab_bytes)
+            store_pairs(smem, Cfg::AB + buf * Cfg::AB_BYTES, tid, G, qa, qb);
     };
 
-    // ---- tile ring
+    // ---- tile ring (streamed once: non-temporal loads)
     u32x4_t pb[D];
-    uint32_t ab[D], bbv[D];
     const uint32_t tile_lane = static_cast<uint32_t>(lane) * 16;
     auto issue = [&](int u, int t) {
         const int i = t / C;
         const int c = cbase + t % C;
         const bool live = t < T && c < Kc;
-        const int b = r + i * args.Gp;
-        const uint32_t toff = static_cast<uint32_t>(b * Kc + c) * TILE_BYTES + tile_lane;
-        const uint32_t goff =
-            (static_cast<uint32_t>(b * TILE_ROWS + j) * G + (c * TILE_K) / g) * 2;
-        pb[u] = load16(rp, live ? toff : OOR);
-        ab[u] = load2(ra, live ? goff : OOR);
-        bbv[u] = load2(rb, live ? goff : OOR);
+        const int b = r + i * Gs;
+        pb[u] = load16_nt(rp, live ? static_cast<uint32_t>(b * Kc + c) * TILE_BYTES + tile_lane
+                                   : OOR);
     };
 
-    // ---- prologue: table of block 0, x operands, the first D tiles, tables 1..LR
-    lut_load(0, lq0[0], lq1[0], llo[0]);
+    // ---- prologue.  The loads of the staging registers go out before the
+    // ring, as they do in the loop, so that the waits the compiler derives for
+    // the loop (from both of its entries) leave the ring in flight.
+    u32x4_t l0 = lut_load(0), l1 = lut_load(1), a0, b0;
+    ab_load(0, a0, b0);
+    u32x4_t lq[2], aq[2], bq[2];
+    lq[0] = lut_load(2);
+    lq[1] = lut_load(3);
+    ab_load(1, aq[1], bq[1]);
+    ab_load(2, aq[0], bq[0]);
     u32x4_t xr[C][4];
+    u32x4_t xw[XR > 0 ? XR : 1];
+    if constexpr (XR > 0) {
+        // row m of x over this wave's C*128 k: lane l < 16C holds k = 8l .. 8l+7
+        const int k0 = cbase * TILE_K + lane * 8;
+        const uint32_t xk = (lane < 16 * C && k0 < K) ? static_cast<uint32_t>(k0) * 2 : OOR;
 #pragma unroll
-    for (int ci = 0; ci < C; ++ci) {
-        const int c = cbase + ci;
-        const bool live = j < M && c < Kc;
+        for (int m = 0; m < XR; ++m)
+            xw[m] = load16(rx, m < M ? xk + static_cast<uint32_t>(m * K) * 2 : OOR);
+    } else {
+        const uint32_t x_lane = j < M ? static_cast<uint32_t>(j * K + kq * 32) * 2 : OOR;
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
-            xr[ci][s4] = load16(rx, live ? static_cast<uint32_t>(
-                                               (j * K + c * TILE_K + kq * 32 + s4 * 8) * 2)
-                                         : OOR);
+        for (int ci = 0; ci < C; ++ci) {
+            const int c = cbase + ci;
+            const uint32_t xc = c < Kc ? static_cast<uint32_t>(c) * TILE_K * 2 : OOR;
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+                xr[ci][s4] = load16(rx, (x_lane | (xc & OOR)) + (xc & ~OOR) + s4 * 16);
+        }
     }
 #pragma unroll
     for (int u = 0; u < D; ++u)
         issue(u, u);
-    tab_build(0, lq0[0], lq1[0], llo[0]);
+    if constexpr (XR > 0) {
+        // through this wave's own LDS rows into the operand layout: lane
+        // (j, kq) takes row j, k = 128 ci + 32 kq + 8 s4 .. +8 (zero for j >= M)
+        constexpr int ROW = C * 256;
+        const uint32_t xs_base = Cfg::XS + wave * XR * ROW;
+        if (lane < 16 * C) {
 #pragma unroll
-    for (int q = 1; q <= LR; ++q)
-        lut_load(q, lq0[q % LR], lq1[q % LR], llo[q % LR]);
+            for (int m = 0; m < XR; ++m)
+                lds_at<u32x4_t>(smem, xs_base + m * ROW + lane * 16) = xw[m];
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int ci = 0; ci < C; ++ci)
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+                xr[ci][s4] = u32x4_t{0u, 0u, 0u, 0u};
+        if (j < M) {
+            const uint32_t rb0 = xs_base + j * ROW + kq * 64;
+#pragma unroll
+            for (int ci = 0; ci < C; ++ci)
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+                    xr[ci][s4] = lds_at<u32x4_t>(smem, rb0 + ci * 256 + s4 * 16);
+        }
+    }
+    lut_stage(0, l0);
+    lut_stage(1, l1);
+    ab_stage(0, a0, b0);
+    __syncthreads();
+    build_table<W>(smem, Cfg::LUT, 0, tid);
 
     // chunk sums of x: lane l gets sum_k x[4*(l/16) + v][k] in xs[ci][v]
     f32x4_t xs[C];
@@ -334,124 +519,167 @@ __global__ __launch_bounds__(GT) void k_gemm(const GemmArgs args)
     __syncthreads();
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem + TAB_BYTES);
-    const bool split = args.S > 1;
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem + Cfg::RED);
+    const uint32_t slot_lane = static_cast<uint32_t>(lane & 31) * 4;
+    int gi_c[C];
+#pragma unroll
+    for (int ci = 0; ci < C; ++ci)
+        gi_c[ci] = ((cbase + ci) * TILE_K) / g;
 
-    // The body is straight-line apart from uniform branches that skip the
-    // decode of tiles past the sequence: every load is issued on every path, so
-    // the in-flight ring survives the loop (no register copies, no early waits).
     for (int t0 = 0; t0 < T; t0 += D) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
             const int t = t0 + u;
             const int ci = u % C;
-            const int i = t / C;   // block number in this workgroup's sequence
+            const int P = (u / C) & 1;  // parity of block i
+            const int i = t / C;
             if (ci == 0) {
-                // start of block i: build the table of block i+1, then fetch the
-                // table rows of block i+1+LR into the slot just used.
-                const int q = (u / C + 1) % LR;
-                tab_build((i + 1) & 1, lq0[q], lq1[q], llo[q]);
-                lut_load(i + 1 + LR, lq0[q], lq1[q], llo[q]);
+                build_table<W>(smem, Cfg::LUT + ((i + 1) & 1) * 512, (i + 1) & 1, tid);
+                ab_stage(P ^ 1, aq[P ^ 1], bq[P ^ 1]);
+                lut_stage(P, lq[P]);
+                ab_load(i + 3, aq[P ^ 1], bq[P ^ 1]);
+                lq[P] = lut_load(i + 4);
             }
-            if (t < T) {
-                // decode tile t
-                const u32x4_t p = pb[u];
-                const float a = bf16_to_f32(ab[u]);
-                const float bt = bf16_to_f32(bbv[u]);
-                const uint32_t slot4 = static_cast<uint32_t>((i & 1) * 128 + (lane & 31) * 4);
-                f32x4_t ag = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    u32x4_t bw;
-                    bw[0] = lds_word(smem, tab_addr(p[s4], slot4, 0));
-                    bw[1] = lds_word(smem, tab_addr(p[s4], slot4, 1));
-                    bw[2] = lds_word(smem, tab_addr(p[s4], slot4, 2));
-                    bw[3] = lds_word(smem, tab_addr(p[s4], slot4, 3));
-                    ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, xr[ci][s4]), __builtin_bit_cast(bf16x8_t, bw),
-                        ag, 0, 0, 0);
-                }
+            {
+                // no branch around the decode, so the scheduler can overlap
+                // tiles; a tile past the sequence gets alpha = beta = 0
+                const uint32_t pr = t < T ? lds_at<uint32_t>(smem, Cfg::AB + P * Cfg::AB_BYTES +
+                                                                       (gi_c[ci] * 16 + j) * 4)
+                                          : 0u;
+                const f32x4_t ag = tile_dot(smem, P * 128 + slot_lane, pb[u], xr[ci]);
+                const float a = bf16_to_f32(pr & 0xFFFFu);
+                const float bt = bf16_to_f32(pr >> 16);
 #pragma unroll
                 for (int v = 0; v < VC; ++v)
                     acc[v] = fmaf(a, ag[v], fmaf(bt, xs[ci][v], acc[v]));
             }
             issue(u, t + D);
             if (ci == C - 1) {
-                // end of block i: partial sums of the 8 waves meet in LDS
-                red[((i & 1) * GW + wave) * 64 + lane] = acc;
+                red[(P * W + wave) * 64 + lane] = acc;
                 acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 __syncthreads();
-                if (wave == i % GW && i < nblk) {
-                    f32x4_t tot = red[((i & 1) * GW) * 64 + lane];
-#pragma unroll
-                    for (int w = 1; w < GW; ++w) {
-                        const f32x4_t o = red[((i & 1) * GW + w) * 64 + lane];
-#pragma unroll
-                        for (int v = 0; v < VC; ++v)
-                            tot[v] += o[v];
-                    }
-                    const int b = r + i * args.Gp;
-                    if (!split) {
-                        const int n = b * TILE_ROWS + j;
-#pragma unroll
-                        for (int v = 0; v < VC; ++v) {
-                            const int m = kq * 4 + v;
-                            if (m < M && n < N)
-                                args.y[static_cast<size_t>(m) * N + n] =
-                                    static_cast<uint16_t>(f32_to_bf16(tot[v]));
-                        }
-                    } else {
-                        float* pp =
-                            args.part + ((static_cast<size_t>(s) * NB + b) * 64 + lane) * VC;
-#pragma unroll
-                        for (int v = 0; v < VC; ++v)
-                            pp[v] = tot[v];
-                    }
-                }
+                if (wave == i % W && i < nblk)
+                    store_block<MT, W>(red + P * W * 64, args.y, lane, M, N,
+                                       (r + i * Gs) * TILE_ROWS);
             }
         }
     }
+}
 
-    if (!split)
-        return;
-    // ---- split K: the last workgroup to finish a block sums its S parts in order.
-    for (int i = wave; i < nblk; i += GW) {
-        const int b = r + i * args.Gp;
-        __threadfence();
-        uint32_t old = 0;
-        if (lane == 0)
-            old = atomicAdd(args.count + b, 1u);
-        old = __builtin_amdgcn_readfirstlane(old);
-        if (old != static_cast<uint32_t>(args.S - 1))
-            continue;
-        __threadfence();
-        float tot[VC];
+// ---- k_gemm_str: one row block per workgroup, x loaded per tile ----------
+//
+// LDS: [0, 64K) table (buffer 0 used), red[8][64] f32x4 (8 KB), alpha/beta
+// pairs [16][K/g] dwords (<= 32 KB), LUT rows [16][16] bf16.
+constexpr int STR_D = 8;
+constexpr int STR_RED = TAB_BYTES;
+constexpr int STR_AB = STR_RED + GW * 64 * 16;
+constexpr int STR_LUT = STR_AB + 16 * STR_MAX_G * 4;
+constexpr int STR_LDS = STR_LUT + 512;
+
+template <int MT>
+__global__ __launch_bounds__(GT) void k_gemm_str(const GemmArgs args)
+{
+    constexpr int D = STR_D;
+    constexpr int VC = MT < 4 ? MT : 4;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[STR_LDS];
+
+    const int M = args.M, N = args.N, K = args.K, g = args.g;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15;
+    const int kq = lane >> 4;
+    const int Kc = K / TILE_K;
+    const int NB = (N + TILE_ROWS - 1) / TILE_ROWS;
+    const int G = K / g;
+    const int b = blockIdx.x;
+    const int CB = (Kc + GW - 1) / GW;   // tiles per wave
+    const int c0 = wave * CB;
+
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc(args.packed, static_cast<uint32_t>(NB) * Kc * TILE_BYTES);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(args.lut, static_cast<uint32_t>(N) * 32);
+    // alpha/beta are staged with 16-byte loads: the range is rounded up to 16 B
+    // (the 16-byte granule holding a valid byte never leaves that byte's page
+    // when the base is 16-byte aligned); the extra values only reach rows >= N.
+    const uint32_t ab_range = (static_cast<uint32_t>(N) * G * 2 + 15u) & ~15u;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(args.alpha, ab_range);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(args.beta, ab_range);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(args.x, static_cast<uint32_t>(M) * K * 2);
+
+    // staging loads first, so that waiting for them leaves the ring in flight
+    const uint32_t ab_bytes = static_cast<uint32_t>(G) * 32;
+    const u32x4_t lq =
+        load16(rl, (tid < 32 ? static_cast<uint32_t>(tid) * 16 : OOR) + static_cast<uint32_t>(b) * 512);
+    u32x4_t aq[2], bq[2];
 #pragma unroll
-        for (int v = 0; v < VC; ++v)
-            tot[v] = 0.f;
-        for (int sp = 0; sp < args.S; ++sp) {
-            const float* pp = args.part + ((static_cast<size_t>(sp) * NB + b) * 64 + lane) * VC;
-#pragma unroll
-            for (int v = 0; v < VC; ++v)
-                tot[v] += __builtin_nontemporal_load(pp + v);
-        }
-        const int n = b * TILE_ROWS + j;
-#pragma unroll
-        for (int v = 0; v < VC; ++v) {
-            const int m = kq * 4 + v;
-            if (m < M && n < N)
-                args.y[static_cast<size_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16(tot[v]));
-        }
-        // leave this block's part of the workspace zero again, counter included
-        for (int sp = 0; sp < args.S; ++sp) {
-            float* pp = args.part + ((static_cast<size_t>(sp) * NB + b) * 64 + lane) * VC;
-#pragma unroll
-            for (int v = 0; v < VC; ++v)
-                pp[v] = 0.f;
-        }
-        if (lane == 0)
-            args.count[b] = 0u;
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t o = static_cast<uint32_t>(tid + h * GT) * 16;
+        const uint32_t off = (o < ab_bytes ? o : OOR) + static_cast<uint32_t>(b) * ab_bytes;
+        aq[h] = load16(ra, off);
+        bq[h] = load16(rb, off);
     }
+
+    u32x4_t pb[D];
+    u32x4_t px[D][4];
+    const uint32_t tile_lane = static_cast<uint32_t>(lane) * 16;
+    // x rows m >= M: a per-lane out-of-range base; dead tiles: a uniform one
+    const uint32_t x_lane = j < M ? static_cast<uint32_t>(j * K + kq * 32) * 2 : OOR;
+    auto issue = [&](int u, int t) {
+        const int c = c0 + t;
+        const bool live = t < CB && c < Kc;
+        pb[u] = load16(rp, live ? static_cast<uint32_t>(b * Kc + c) * TILE_BYTES + tile_lane : OOR);
+        const uint32_t xc = live ? static_cast<uint32_t>(c) * TILE_K * 2 : OOR;
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+            px[u][s4] = load16(rx, (x_lane | (xc & OOR)) + (xc & ~OOR) + s4 * 16);
+    };
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+        issue(u, u);
+
+    if (tid < 32)
+        lds_at<u32x4_t>(smem, STR_LUT + tid * 16) = lq;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        if (static_cast<uint32_t>(tid + h * GT) * 16 < ab_bytes)
+            store_pairs(smem, STR_AB, tid + h * GT, G, aq[h], bq[h]);
+    __syncthreads();
+    build_table<GW>(smem, STR_LUT, 0, tid);
+    __syncthreads();
+
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t slot4 = static_cast<uint32_t>(lane & 31) * 4;
+    for (int t0 = 0; t0 < CB; t0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int t = t0 + u;
+            const int c = c0 + t;
+            if (t < CB && c < Kc) {
+                const uint32_t pr =
+                    lds_at<uint32_t>(smem, STR_AB + (((c * TILE_K) / g) * 16 + j) * 4);
+                const float a = bf16_to_f32(pr & 0xFFFFu);
+                const uint32_t b2 = (pr & 0xFFFF0000u) | (pr >> 16);
+                const u32x4_t bv = {b2, b2, b2, b2};
+                const f32x4_t ag = tile_dot(smem, slot4, pb[u], px[u]);
+#pragma unroll
+                for (int v = 0; v < VC; ++v)
+                    acc[v] = fmaf(a, ag[v], acc[v]);
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, px[u][s4]), __builtin_bit_cast(bf16x8_t, bv),
+                        acc, 0, 0, 0);
+            }
+            issue(u, t + D);
+        }
+    }
+
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem + STR_RED);
+    red[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (wave == 0)
+        store_block<MT, GW>(red, args.y, lane, M, N, b * TILE_ROWS);
 }
 
 // ---------------------------------------------------------------------------
@@ -477,58 +705,24 @@ any4_status launched()
     return hipGetLastError() == hipSuccess ? ANY4_OK : ANY4_E_HIP;
 }
 
-// How a GEMM is split: C chunks per wave, S parts of K, Gp workgroups per part.
-struct Plan {
-    int C, S, Gp;
-};
-
-constexpr int PLAN_CUS = 256;   // the split is planned for a full MI355X
-
-Plan plan_for(int64_t N, int64_t K)
-{
-    const int64_t Kc = K / TILE_K, NB = row_blocks(N);
-    Plan best{4, 1, 1};
-    double best_cost = 1e30;
-    for (int C : {4, 2, 1}) {
-        const int64_t S = (Kc + GW * C - 1) / (GW * C);
-        int64_t Gp = PLAN_CUS / S;
-        if (Gp < 1)
-            Gp = 1;
-        if (Gp > NB)
-            Gp = NB;
-        const int64_t rounds = (NB + Gp - 1) / Gp;
-        // time of one workgroup: rounds x (C tiles + table build and barrier);
-        // a split adds the partial-sum traffic and the final sum.
-        const double cost = rounds * (C + 0.5) + (S > 1 ? 1.0 : 0.0);
-        if (cost < best_cost - 1e-9) {
-            best_cost = cost;
-            best = Plan{C, static_cast<int>(S), static_cast<int>(Gp)};
-        }
-    }
-    return best;
-}
-
-size_t split_bytes(int64_t M, int64_t N, const Plan& p, size_t* count_off)
-{
-    if (p.S <= 1) {
-        *count_off = 0;
-        return 0;
-    }
-    const int64_t NB = row_blocks(N);
-    const int64_t VC = M < 4 ? M : 4;
-    const size_t part = static_cast<size_t>(p.S) * NB * 64 * VC * sizeof(float);
-    *count_off = (part + 255) & ~static_cast<size_t>(255);
-    return *count_off + static_cast<size_t>(NB) * sizeof(uint32_t);
-}
+constexpr int RES_GRID = 256;   // k_gemm_res: one workgroup per CU of an MI355X
+#ifndef ANY4_RES_WAVES
+#define ANY4_RES_WAVES 8
+#endif
+constexpr int RES_W = ANY4_RES_WAVES;
+constexpr int RES_CW = RES_MAX_K / TILE_K / RES_W;
 
 template <int MT>
-void launch_gemm(const Plan& p, const GemmArgs& a, hipStream_t stream)
+void launch_gemm(const GemmArgs& a, hipStream_t stream)
 {
-    const dim3 grid(static_cast<unsigned>(p.S * p.Gp)), block(GT);
-    switch (p.C) {
-    case 4: hipLaunchKernelGGL((k_gemm<MT, 4, 8, 2>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((k_gemm<MT, 2, 8, 2>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((k_gemm<MT, 1, 8, 2>), grid, block, 0, stream, a); break;
+    const int64_t NB = row_blocks(a.N);
+    if (a.K <= RES_MAX_K) {
+        const int grid = static_cast<int>(NB < RES_GRID ? NB : RES_GRID);
+        hipLaunchKernelGGL((k_gemm_res<MT, RES_W, RES_CW>), dim3(grid), dim3(64 * RES_W), 0,
+                           stream, a);
+    } else {
+        hipLaunchKernelGGL(k_gemm_str<MT>, dim3(static_cast<unsigned>(NB)), dim3(GT), 0, stream,
+                           a);
     }
 }
 
@@ -545,8 +739,8 @@ const char* any4_status_string(any4_status s)
     case ANY4_OK: return "ANY4_OK: success";
     case ANY4_E_NULL: return "ANY4_E_NULL: a required pointer is NULL";
     case ANY4_E_SHAPE: return "ANY4_E_SHAPE: unsupported sizes (negative size, K not a multiple "
-                              "of 128, g not a positive multiple of 128, K % g != 0, M > 16, "
-                              "or buffers of 2 GiB or more)";
+                              "of 128, g not a positive multiple of 128, K % g != 0, K/g > 512, "
+                              "M > 16, or buffers of 2 GiB or more)";
     case ANY4_E_ALIGN: return "ANY4_E_ALIGN: a base pointer is not aligned as required";
     case ANY4_E_WORKSPACE: return "ANY4_E_WORKSPACE: workspace too small";
     case ANY4_E_HIP: return "ANY4_E_HIP: the HIP runtime reported an error";
@@ -609,12 +803,11 @@ any4_status any4_dequant(const uint8_t* packed, const uint16_t* lut, const uint1
 
 size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g)
 {
-    if (M <= 0 || M > 16 || N <= 0 || K <= 0 || !group_ok(K, g))
-        return 0;
-    if (any4_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31))
-        return 0;
-    size_t off = 0;
-    return split_bytes(M, N, plan_for(N, K), &off);
+    (void)M;
+    (void)N;
+    (void)K;
+    (void)g;
+    return 0;   // neither kernel needs device scratch
 }
 
 any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
@@ -622,18 +815,21 @@ any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* 
                       int64_t N, int64_t K, int64_t g, void* workspace, size_t workspace_bytes,
                       hipStream_t stream)
 {
-    if (M < 0 || M > 16 || N < 0 || !group_ok(K, g))
+    (void)workspace;
+    (void)workspace_bytes;
+    if (M < 0 || M > 16 || N < 0 || !group_ok(K, g) || K / (g > 0 ? g : 1) > STR_MAX_G)
         return ANY4_E_SHAPE;
     if (any4_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31) ||
-        static_cast<size_t>(M) * K * 2 >= (static_cast<size_t>(1) << 31))
+        static_cast<size_t>(M) * K * 2 >= (static_cast<size_t>(1) << 31) ||
+        static_cast<size_t>(N) * 32 >= (static_cast<size_t>(1) << 31))
         return ANY4_E_SHAPE;
     if (M == 0 || N == 0)
         return ANY4_OK;
     if (!y || (K > 0 && (!x || !packed || !lut || !alpha || !beta)))
         return ANY4_E_NULL;
     if (!aligned(y, 2) || (K > 0 && (!aligned(x, 16) || !aligned(packed, 16) ||
-                                     !aligned(lut, 16) || !aligned(alpha, 2) ||
-                                     !aligned(beta, 2))))
+                                     !aligned(lut, 16) || !aligned(alpha, 16) ||
+                                     !aligned(beta, 16))))
         return ANY4_E_ALIGN;
     (void)hipGetLastError();
     if (K == 0) {
@@ -642,13 +838,6 @@ any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* 
                            stream, y, n);
         return launched();
     }
-    const Plan p = plan_for(N, K);
-    size_t count_off = 0;
-    const size_t need = split_bytes(M, N, p, &count_off);
-    if (workspace_bytes < need)
-        return ANY4_E_WORKSPACE;
-    if (need > 0 && (!workspace || !aligned(workspace, 256)))
-        return workspace ? ANY4_E_ALIGN : ANY4_E_NULL;
     GemmArgs a;
     a.x = x;
     a.packed = packed;
@@ -656,25 +845,20 @@ any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* 
     a.alpha = alpha;
     a.beta = beta;
     a.y = y;
-    a.part = need ? static_cast<float*>(workspace) : nullptr;
-    a.count = need ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + count_off)
-                   : nullptr;
     a.M = static_cast<int>(M);
     a.N = static_cast<int>(N);
     a.K = static_cast<int>(K);
     a.g = static_cast<int>(g);
-    a.S = p.S;
-    a.Gp = p.Gp;
     if (M == 1)
-        launch_gemm<1>(p, a, stream);
+        launch_gemm<1>(a, stream);
     else if (M == 2)
-        launch_gemm<2>(p, a, stream);
+        launch_gemm<2>(a, stream);
     else if (M <= 4)
-        launch_gemm<4>(p, a, stream);
+        launch_gemm<4>(a, stream);
     else if (M <= 8)
-        launch_gemm<8>(p, a, stream);
+        launch_gemm<8>(a, stream);
     else
-        launch_gemm<16>(p, a, stream);
+        launch_gemm<16>(a, stream);
     return launched();
 }
 

@@ -87,12 +87,12 @@ def test_packed_bytes():
     assert any4.packed_bytes(-1, 128) == 0
 
 
-def test_gemm_workspace_errors():
-    # a shape that splits K needs a workspace: none given -> ANY4_E_WORKSPACE
-    need = any4.workspace_size(1, 64, 16384, 128)
-    assert need > 0
-    assert any4.gemm_raw(A, A, A, A, A, A, 1, 64, 16384, 128, None, 0, stream=0) == 4
-    assert any4.gemm_raw(A, A, A, A, A, A, 1, 64, 16384, 128, A + 16, need, stream=0) == 3
+def test_gemm_limits():
+    # K/g at most 512 (the alpha/beta staging of one row block)
+    assert any4.gemm_raw(A, A, A, A, A, A, 1, 16, 128 * 513, 128, stream=0) == 2
+    # alpha and beta are read with 16-byte loads
+    assert any4.gemm_raw(A, A, A, A + 2, A, A, 1, 16, 128, 128, stream=0) == 3
+    assert any4.gemm_raw(A, A, A, A, A + 8, A, 1, 16, 128, 128, stream=0) == 3
 
 
 def test_workspace_size_is_defined_for_all_shapes():

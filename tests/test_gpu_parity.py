@@ -147,7 +147,8 @@ def test_gemm_config4_sampled_rows(name):
         print(f"config 4 {name} M={M}: max err/tol = {r:.3e}", flush=True)
 
 
-@pytest.mark.parametrize("M,N,K,g", [(1, 17, 128, 128), (3, 50, 384, 128), (5, 1, 256, 256),
+@pytest.mark.parametrize("M,N,K,g", [(7, 16 * 700 + 5, 256, 128), (1, 16 * 1300, 512, 256),
+                                     (1, 17, 128, 128), (3, 50, 384, 128), (5, 1, 256, 256),
                                      (7, 33, 1024, 512), (16, 15, 128, 128), (9, 100, 2048, 1024),
                                      (12, 272, 640, 128), (2, 4097, 256, 128)])
 def test_gemm_ragged(M, N, K, g):
@@ -159,41 +160,17 @@ def test_gemm_ragged(M, N, K, g):
     gu.assert_within_bound(y, y_ref, ad, f"ragged {M}x{N}x{K} g{g}")
 
 
-# K split over workgroups: each 16-row block is summed from several parts by
-# whichever workgroup finishes it last, through the zeroed workspace.
+# Large K: one workgroup per 16-row block, x loaded with each tile.
 @pytest.mark.parametrize("M,N,K,g", [(1, 64, 16384, 128), (16, 100, 8192, 1024),
                                      (4, 300, 14336, 1024), (2, 17, 28672, 128),
-                                     (16, 4096, 14336, 1024)])
-def test_gemm_split_k(M, N, K, g):
-    assert any4.workspace_size(M, N, K, g) > 0, "shape expected to split K"
+                                     (16, 33, 65536, 128), (3, 16, 4224, 384)])
+def test_gemm_large_k(M, N, K, g):
     inp = workloads.generic(M * 3 + N + K, M, N, K, g)
     L = gu.Layer(inp)
     y_ref, ad = oracle.gemm(inp.x, L.w_ref(), nthreads=oracle.default_threads())
-    ws = torch.zeros(any4.workspace_size(M, N, K, g), dtype=torch.uint8, device=gu.DEV)
-    ys = []
-    for _ in range(3):   # the counters must come back to zero after every call
-        ys.append(any4.gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g, workspace=ws))
+    y = any4.gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g)
     torch.cuda.synchronize()
-    for y in ys:
-        gu.assert_within_bound(y, y_ref, ad, f"split {M}x{N}x{K} g{g}")
-        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
-    assert torch.count_nonzero(ws) == 0   # partial sums and counters cleared again
-
-
-def test_workspace_shared_across_shapes():
-    """One workspace serves calls of different split shapes in any order."""
-    shapes = [(16, 4096, 14336, 1024), (1, 300, 8192, 128), (8, 64, 16384, 128),
-              (16, 4096, 14336, 1024)]
-    need = max(any4.workspace_size(*s) for s in shapes)
-    ws = torch.zeros(need, dtype=torch.uint8, device=gu.DEV)
-    for i, (M, N, K, g) in enumerate(shapes):
-        inp = workloads.generic(900 + i, M, N, K, g)
-        L = gu.Layer(inp)
-        y = any4.gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g, workspace=ws)
-        torch.cuda.synchronize()
-        y_ref, ad = oracle.gemm(inp.x, L.w_ref(), nthreads=oracle.default_threads())
-        gu.assert_within_bound(y, y_ref, ad, f"shared workspace {M}x{N}x{K} g{g}")
-        assert torch.count_nonzero(ws) == 0
+    gu.assert_within_bound(y, y_ref, ad, f"large K {M}x{N}x{K} g{g}")
 
 
 # --------------------------------------------------------------------------
