@@ -7,15 +7,18 @@ seeded; idx uniform 0..15, per-row sorted N(0,1) bf16 table, alpha ~ U[0.005,
 A step is one any4_gemm at M=1 followed by one at M=16.  Every launch reads a
 different copy of the weights (rotating sets whose total exceeds twice the
 256 MB last-level cache), so the weights come from HBM.  Inputs are resident
-in HBM before the timed region starts.
+in HBM before the timed region starts.  The launches of the timed steps are
+recorded once in a HIP graph and replayed, so that the host's launch cost
+does not set the pace; HIP events on the replay stream bracket the timed
+region.
 
 value = algorithmic bytes of all timed launches / timed wall time (TB/s),
 where the algorithmic bytes of one launch are
     N*K/2 (indices) + 4*N*K/g (alpha, beta) + 32*N (tables) + 2*M*K (x) + 2*M*N (y).
-Per-launch durations come from HIP events recorded between the launches on
-the stream the kernels run on.
+Per-M launch durations come from graphs of that M alone (same events).
 
-Prints one JSON line.
+Prints one JSON line.  --traffic-probe instead runs a few launches of each M
+plus a device copy of known size, for hardware-counter collection.
 """
 from __future__ import annotations
 
@@ -38,7 +41,8 @@ CACHE_BYTES = 256 * 1024 ** 2   # MI355X last-level cache (MALL)
 N_, K_, G_ = 14336, 4096, 128
 MS = (1, 16)
 KERNEL_SRC = os.path.join(ROOT, "gemm_any4_amd", "csrc", "any4.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_config2.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_any4_gemm_14336x4096.json")
+COPY_BYTES = 256 * 1024 ** 2    # the calibration copy of --traffic-probe
 
 
 def algorithmic_bytes(M: int, N: int, K: int, g: int) -> int:
@@ -56,8 +60,8 @@ def kernel_source_hash() -> str:
 
 
 def _traffic(M: int):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, or None
-    if none exist for the current kernel source."""
+    """HBM bytes per launch from the committed counter summary, or None if it
+    was taken on another version of the kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -72,8 +76,6 @@ def _traffic(M: int):
 def cpu_baseline(seconds: float) -> dict:
     """The CPU oracle (dequant + fp64 GEMM) on the same workload, repeated for
     about `seconds` of wall time on this host's cores."""
-    import numpy as np  # noqa: F401
-
     import oracle
     import workloads
 
@@ -103,6 +105,75 @@ def cpu_baseline(seconds: float) -> dict:
     }
 
 
+def _setup(torch, any4, workloads, sets_arg: int):
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = workloads.generate(2)
+    wb = weight_bytes(N_, K_, G_)
+    R = sets_arg or max(2, math.ceil(2 * CACHE_BYTES / wb) + 1)
+
+    def b16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
+            torch.bfloat16)
+
+    idx_d = torch.from_numpy(inp.idx).to(dev)
+    packed0 = any4.pack(idx_d)
+    del idx_d
+    sets = [(packed0.clone(), b16(inp.lut), b16(inp.alpha), b16(inp.beta)) for _ in range(R)]
+    x = b16(inp.x)
+    ys = {M: torch.empty((M, N_), dtype=torch.bfloat16, device=dev) for M in MS}
+    return dev, R, sets, x, ys
+
+
+def _graph(torch, launch, steps: int, Ms):
+    """Record `steps` steps of launches (one per M in Ms) in a HIP graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                for M in Ms:
+                    launch(i, M)
+    torch.cuda.synchronize()
+    return g
+
+
+def _time_graph(torch, g, reps: int = 1) -> float:
+    """ms for `reps` replays of g; the HIP events go on the stream the replay
+    runs on (the current stream)."""
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(reps):
+        g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def traffic_probe(torch, any4, workloads, sets_arg: int) -> int:
+    """A few launches of each M and one COPY_BYTES device copy (the scale for
+    the FETCH_SIZE / WRITE_SIZE counters)."""
+    dev, R, sets, x, ys = _setup(torch, any4, workloads, sets_arg)
+    for i in range(6):
+        for M in MS:
+            p, l, a, b = sets[i % R]
+            any4.gemm(x[:M], p, l, a, b, G_, out=ys[M])
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_probe": True, "copy_bytes": COPY_BYTES,
+                      "launches_per_m": 6}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +182,7 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=0, help="rotating weight sets (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -128,79 +200,55 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     any4.lib()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+    if args.traffic_probe:
+        return traffic_probe(torch, any4, workloads, args.sets)
 
-    inp = workloads.generate(2)
+    dev, R, sets, x, ys = _setup(torch, any4, workloads, args.sets)
     wb = weight_bytes(N_, K_, G_)
-    R = args.sets or max(2, math.ceil(2 * CACHE_BYTES / wb) + 1)
 
-    def b16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
-            torch.bfloat16)
-
-    idx_d = torch.from_numpy(inp.idx).to(dev)
-    packed0 = any4.pack(idx_d)
-    del idx_d
-    sets = []
-    for r in range(R):
-        sets.append((packed0.clone(), b16(inp.lut), b16(inp.alpha), b16(inp.beta)))
-    x = b16(inp.x)
-    ys = {M: torch.empty((M, N_), dtype=torch.bfloat16, device=dev) for M in MS}
-    stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
-
-    def launch(step: int, M: int):
-        p, l, a, b = sets[step % R]
+    def launch(i: int, M: int):
+        p, l, a, b = sets[i % R]
         any4.gemm(x[:M], p, l, a, b, G_, out=ys[M])
 
+    # warmup (eager), then the graphs: the timed K steps, and K launches of each M
     for s in range(args.warmup):
         for M in MS:
             launch(s, M)
     torch.cuda.synchronize()
-
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(MS) * K + 1)]
-    torch.cuda.synchronize()
+    g_all = _graph(torch, launch, K, MS)
+    g_m = {M: _graph(torch, launch, K, (M,)) for M in MS}
+    for gg in [g_all] + list(g_m.values()):
+        _time_graph(torch, gg)              # one untimed replay of each graph
+
     t0 = time.perf_counter()
-    ev[0].record(stream)
-    i = 1
-    for s in range(K):
-        for M in MS:
-            launch(args.warmup + s, M)
-            ev[i].record(stream)
-            i += 1
-    torch.cuda.synchronize()
+    total_ms = _time_graph(torch, g_all)
     wall = time.perf_counter() - t0
-    total_ms = ev[0].elapsed_time(ev[-1])
-    per = {M: [] for M in MS}
-    i = 1
-    for s in range(K):
-        for M in MS:
-            per[M].append(ev[i - 1].elapsed_time(ev[i]))
-            i += 1
+
+    per_m = {}
+    reps = 3
+    for M in MS:
+        runs = [_time_graph(torch, g_m[M]) * 1e3 / K for _ in range(reps)]   # us per launch
+        us = float(np.median(runs))
+        bts = algorithmic_bytes(M, N_, K_, G_)
+        per_m[str(M)] = {
+            "us_per_launch": us,
+            "us_per_launch_runs": runs,
+            "bytes": bts,
+            "tbps": bts / (us * 1e-6) / 1e12,
+            "weight_gbps": wb / (us * 1e-6) / 1e9,
+            "pct_hbm_peak": 100.0 * bts / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+        }
 
     step_bytes = sum(algorithmic_bytes(M, N_, K_, G_) for M in MS)
     value = step_bytes * K / (total_ms * 1e-3) / 1e12
-    per_m = {}
-    for M in MS:
-        d = np.array(per[M]) * 1e3            # us
-        bts = algorithmic_bytes(M, N_, K_, G_)
-        per_m[str(M)] = {
-            "us_mean": float(d.mean()), "us_median": float(np.median(d)),
-            "us_p10": float(np.percentile(d, 10)), "us_p90": float(np.percentile(d, 90)),
-            "bytes": bts,
-            "tbps": bts / (d.mean() * 1e-6) / 1e12,
-            "weight_gbps": wb / (d.mean() * 1e-6) / 1e9,
-            "pct_hbm_peak": 100.0 * bts / (d.mean() * 1e-6) / (HBM_PEAK_GBS * 1e9),
-        }
-    dom = max(MS, key=lambda M: per_m[str(M)]["us_mean"])
+    dom = max(MS, key=lambda M: per_m[str(M)]["us_per_launch"])
     dm = per_m[str(dom)]
-    achieved = dm["bytes"] / (dm["us_mean"] * 1e-6) / 1e9
+    achieved = dm["bytes"] / (dm["us_per_launch"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": _traffic(dom),
-                "kernel": f"k_gemm<{dom}> (any4_gemm, M={dom})",
-                "bytes_per_launch": dm["bytes"], "launch_us_mean": dm["us_mean"]}
+                "kernel": f"k_gemm_res (any4_gemm, M={dom})",
+                "bytes_per_launch": dm["bytes"], "launch_us": dm["us_per_launch"]}
 
     out = {
         "metric": METRIC, "value": value, "unit": "TB/s", "n_gpus": 1, "steps": K,
@@ -209,7 +257,7 @@ def main() -> int:
         "config": {"workload": f"any4 MLP up/gate layer N={N_} K={K_} g={G_}, "
                                f"one any4_gemm at M=1 and one at M=16 per step",
                    "N": N_, "K": K_, "g": G_, "M": list(MS), "rotating_weight_sets": R,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "timing": "HIP graph replay, HIP events"},
         "roofline": roofline,
         "per_m": per_m,
         "host_wall_s": wall,

@@ -46,7 +46,8 @@
  *     buffer must be smaller than 2 GiB.
  *   - Alignment: x, idx, packed and w need 16-byte aligned base pointers;
  *     lut needs 16 bytes for any4_gemm and 2 for any4_dequant; alpha, beta and
- *     y need 2 bytes; the any4_gemm workspace needs 256 bytes.
+ *     y need 2 bytes, except that any4_gemm reads alpha and beta with 16-byte
+ *     loads and needs them 16-byte aligned.
  */
 #ifndef ANY4_H
 #define ANY4_H
@@ -107,9 +108,9 @@ any4_status any4_dequant(const uint8_t* packed, const uint16_t* lut, const uint1
 
 /*
  * any4_gemm_workspace_size -- bytes of device workspace any4_gemm needs for
- * this shape (0 when it needs none).  Returns 0 for shapes any4_gemm rejects.
- * The workspace holds per-part partial sums and one arrival counter per
- * 16-row block for the shapes where K is split across workgroups.
+ * this shape.  The current kernels need none: it returns 0 for every shape.
+ * (The workspace arguments stay in the ABI so that a kernel that needs
+ * scratch can be added without changing it.)
  */
 size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
 
@@ -117,8 +118,9 @@ size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
  * any4_gemm -- y = x * W^T with W the any4 weights above, for M = 1..16
  * (the explainer's section 三: decode batches of 1..16):
  *     y[m][n] = bf16_rne( sum_k x[m][k] * (alpha[n][k/g] * lut[n][idx[n][k]] + beta[n][k/g]) )
- * The weights are never written out: each 128-k chunk of a group contributes
- * alpha * sum_k x*lut[idx] + beta * sum_k x, accumulated in fp32.  The result
+ * The weights are never written out: each 128-k chunk contributes
+ * alpha * sum_k x*lut[idx] + beta * sum_k x (alpha, beta of the chunk's
+ * group), accumulated in fp32.  The result
  * is within
  *     |y - y_ref| <= 2e-3 * sum_k |x[m][k] * w[n][k]| + 1e-3
  * of the fp64 product with the bf16 dequantised weights for the workloads this
@@ -130,11 +132,8 @@ size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
  *   M in 0..16, N >= 0, K >= 0 with K % g == 0.  M*N == 0 is a no-op;
  *   K == 0 writes y = 0 (x, packed, lut, alpha and beta may then be NULL).
  *   workspace, workspace_bytes  device scratch of at least
- *       any4_gemm_workspace_size(M, N, K, g) bytes (NULL/0 when that is 0).
- *       It must be all zero bytes before its first use; every call that
- *       completes leaves it all zero again, so one zeroed workspace serves any
- *       number of calls.  Calls that may run at the same time need separate
- *       workspaces.
+ *       any4_gemm_workspace_size(M, N, K, g) bytes; NULL and 0 when that is 0,
+ *       which it is for every shape today.
  * Errors: ANY4_E_SHAPE, ANY4_E_NULL, ANY4_E_ALIGN, ANY4_E_WORKSPACE, ANY4_E_HIP.
  */
 any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
