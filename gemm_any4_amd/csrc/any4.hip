@@ -174,26 +174,23 @@ __global__ __launch_bounds__(256) void k_zero(uint16_t* __restrict__ y, size_t n
 }
 
 // Two kernels compute y = x * W^T; both work on 16-row blocks of W, with the
-// 8 waves of a workgroup splitting the block's K and meeting in LDS.
+// 8 waves of a workgroup splitting K and meeting in LDS at the end.
 //
-//   k_gemm_res  (K <= 4096) persistent: about one workgroup per CU walks row
-//               blocks r, r+G, r+2G, ...; wave w always decodes the same 4
-//               chunks of 128 k, so their x operands are loaded once, into
-//               VGPRs, and reused for every block.
+//   k_gemm_km   (K <= 4096) persistent, k-major: about one workgroup per CU
+//               owns row blocks r, r+G, r+2G, ... and decodes up to four of
+//               them together, chunk by chunk, against the same x operands.
 //   k_gemm_str  (any K) one workgroup per row block; a wave decodes K/8 of
 //               the block and loads the x operand of each chunk with the
 //               chunk's tile.
 //
 // Decode.  A packed byte (two indices) selects one dword of a pair table in
-// LDS: entry (hi << 4 | lo) holds (LUT[lo], LUT[hi]) as two bf16, which is
-// exactly one dword of an MFMA B operand.  The table of a row block has 32
-// slots per entry (slot = lane % 32, row = slot % 16); a wave64 LDS read is
-// served as two halves of 32 lanes, so every lane reads its own bank: no
-// conflicts.  Entry e of table buffer q sits at byte e*256 + q*128, so the
-// read address is one v_perm of the packed dword.
-//
-// Scale and offset.  Per 128-k chunk a lane accumulates sum_k x*LUT[idx] with
-// four MFMAs, then adds alpha times that sum, plus beta times sum_k x.
+// LDS: entry (hi << 4 | lo) holds the table values (L[lo], L[hi]) as two
+// 16-bit halves, in the order of an MFMA B operand dword.  The table of a row
+// block has 32 slots per entry (slot = lane % 32, row = slot % 16); a wave64
+// LDS read is served as two halves of 32 lanes, so every lane reads its own
+// bank: no conflicts.  Entry e of a table sits at byte e*256 (+128 for the
+// second table of a 64 KB region), so the read address is one v_perm of the
+// packed dword.
 //
 // Staging.  The table rows (16 x 32 B) and the block's alpha and beta
 // (16 x K/g bf16 each, contiguous in [N][K/g]) are fetched with coalesced
@@ -204,12 +201,11 @@ __global__ __launch_bounds__(256) void k_zero(uint16_t* __restrict__ y, size_t n
 // register ring.  Every load is a bounds-checked buffer load whose offset is
 // pushed out of range where there is nothing to read (past the wave's work,
 // x rows m >= M), so no branch guards a load and no traffic is made.  The
-// loop bodies are straight-line apart from uniform branches that skip the
-// decode of tiles past the sequence, so the ring survives the loop.
+// loop bodies are straight-line apart from uniform branches, so the ring
+// survives the loop.
 constexpr int GW = 8;                   // waves per workgroup
 constexpr int GT = 64 * GW;
-constexpr int TAB_BYTES = 256 * 256;    // 256 entries x 2 buffers x 32 slots x 4 B
-constexpr int RES_MAX_K = 4096;         // k_gemm_res: K covered by one workgroup
+constexpr int TAB_BYTES = 256 * 256;    // 256 entries x 2 tables x 32 slots x 4 B
 constexpr int STR_MAX_G = 512;          // k_gemm_str: K/g up to 512 (two staging rounds)
 
 struct GemmArgs {
@@ -234,12 +230,14 @@ __device__ __forceinline__ T& lds_at(uint8_t* smem, uint32_t byte_addr)
     return *reinterpret_cast<T*>(smem + byte_addr);
 }
 
-// Build table buffer `buf` of one row block from its 16 LUT rows, staged in
-// LDS at `lut_off` as [16 rows][16] bf16.  Thread t of the W*64 writes slot
-// t % 32 (row (t % 32) % 16) of the entries lo + 16*hi, lo = (t / 32) % 16,
-// for its share of the 16 hi.
+// Build the pair table of one row block, whose entry 0 starts at dword
+// `tab_dw` of LDS (entries 64 dwords apart), from its 16 table rows, staged
+// in LDS at `lut_off` as [16 rows][16] 16-bit values.  Thread t of the W*64
+// writes slot t % 32 (row (t % 32) % 16) of the entries lo + 16*hi,
+// lo = (t / 32) % 16, for its share of the 16 hi.
 template <int W>
-__device__ __forceinline__ void build_table(uint8_t* smem, uint32_t lut_off, int buf, int tid)
+__device__ __forceinline__ void build_table(uint8_t* smem, uint32_t lut_off, uint32_t tab_dw,
+                                            int tid)
 {
     constexpr int HPT = 128 / W;   // hi values per thread
     const int st = tid & 31;
@@ -250,7 +248,7 @@ __device__ __forceinline__ void build_table(uint8_t* smem, uint32_t lut_off, int
     const u32x4_t q1 = lds_at<u32x4_t>(smem, row + 16);
     const uint32_t ll = lds_at<uint16_t>(smem, row + 2 * lo);
     const uint32_t Lw[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
-    uint32_t* tw = reinterpret_cast<uint32_t*>(smem) + lo * 64 + buf * 32 + st;
+    uint32_t* tw = reinterpret_cast<uint32_t*>(smem) + tab_dw + lo * 64 + st;
     if constexpr (HPT == 16) {
 #pragma unroll
         for (int hi = 0; hi < 16; ++hi)
@@ -334,66 +332,157 @@ __device__ __forceinline__ void store_block(const f32x4_t* red, uint16_t* y, int
     }
 }
 
-// ---- k_gemm_res: persistent, x resident in VGPRs (K <= 4096) -------------
+// ---- k_gemm_km: k-major, every row block of a workgroup decoded together --
 //
-// W waves of C chunks each cover K <= W*C*128 = 4096.  LDS: [0, 64K) tables
-// (2 buffers), red[2][W][64] f32x4, alpha/beta pairs [2][G <= 32][16] dwords,
-// LUT rows [2][16][16] bf16, then (M <= XRMAX) x staging [W][M][C*256 B].
-// Pipeline at the start of block i (all waves), parity P = i & 1 known at
-// compile time (the loop body covers two blocks):
-//   build table (i+1)&1 from LUT rows (i+1)&1          (staged at block i-1)
-//   pairs (i+1)&1   <- alpha/beta registers P^1         (loaded at block i-1)
-//   LUT rows i&1    <- LUT registers P (block i+2)      (loaded at block i-2)
-//   load alpha/beta of block i+3 into registers P^1, LUT of block i+4 into P
-// and the barrier at the end of block i publishes what block i+1 reads.
-template <int W, int C>
-struct ResCfg {
-    static constexpr int T = 64 * W;                  // threads
-    static constexpr int D = 2 * C;                   // ring: two blocks of tiles
-    static constexpr int RED = TAB_BYTES;
-    static constexpr int AB = RED + 2 * W * 64 * 16;
-    static constexpr int AB_BYTES = 16 * (RES_MAX_K / TILE_K) * 4;   // [G <= 32][16] dwords
-    static constexpr int LUT = AB + 2 * AB_BYTES;
-    static constexpr int XS = LUT + 2 * 512;
-    // rows of x that go through LDS on their way to the MFMA operands: a wave
-    // fetches each row of its C*128 k with one full-width load, instead of
-    // 4C loads in which only the M lanes of the operand layout are live
-    static constexpr int XRMAX = W <= 8 ? 8 : 4;
-    template <int MT>
-    static constexpr int x_rows() { return MT <= XRMAX ? MT : 0; }
-    template <int MT>
-    static constexpr int lds() { return XS + W * x_rows<MT>() * C * 256; }
+// A workgroup owns the row blocks r, r+Gs, r+2Gs, ... (at most KM_MAX_BLK)
+// and takes them NBG at a time (a group): the pair tables of all NBG blocks
+// of a group are built once, then each wave walks its KM_C chunks of 128 k
+// and, for each chunk, decodes that chunk's tile of every block of the group
+// with the same x operands.  The loop has no barrier: the tables stay put
+// for the whole group, and the waves meet only at the group's end, where
+// their partial sums are added in LDS.
+//
+// Dequantisation.  Every weight is formed as w = bf16(fp32(alpha*L + beta))
+// before it enters the MFMA, the same value any4_dequant writes, so y is the
+// product over the dequantised matrix up to fp32 summation order.  The
+// tables hold L as f16, scaled per row by 2^-s so that the row's largest
+// finite magnitude lies in [2^14, 2^15): every value within 2^31 of it is
+// exact in f16, and alpha*2^s * (L*2^-s) = alpha*L exactly.  v_fma_mix_f32
+// takes an f16 half of the looked-up dword directly, so a dword of two
+// weights costs two fma_mix and one v_cvt_pk_bf16_f32.
+//
+// x: for M <= 2 the operands of the wave's 512 k are loaded once, in the
+// prologue, into VGPRs.  For larger M they travel in the ring with the
+// tiles: a chunk's 4 operand loads are issued right after the chunk's last
+// tile (its slot is free by then: the chunk DS chunks earlier, which used it,
+// has just been decoded), so waiting for them never waits for a later chunk.
+//
+// Decode: two tiles at a time (two blocks of one chunk, or two chunks): the
+// 32 table lookups, the dequantisation, then the two MFMA chains
+// interleaved, so the chains' latencies overlap.
+//
+// Prologue: the first ring loads go out with the staging loads; the rest are
+// spread over the table builds, so the builds overlap the first tiles'
+// latency instead of waiting behind a full ring.
+//
+// LDS:
+//   [0, TABS)  pair tables: table b sits in 64 KB region b/2, half b%2, entry
+//              e at byte e*256 + (b%2)*128 + slot*4 (the x staging of the
+//              prologue and the partial sums of a group's end reuse it)
+//   AB         [NBG][G <= 32][16 rows] (alpha | beta << 16) dwords
+//   LUTS       [NBG][16 rows][16] f16, each row scaled by 2^-s
+//   SCL        [NBG][16 rows] int: the row scale exponents s
+constexpr int KM_C = 4;                              // chunks per wave
+constexpr int KM_MAX_K = GW * KM_C * TILE_K;         // 4096
+constexpr int KM_MAX_G = KM_MAX_K / TILE_K;          // g >= 128
+constexpr int KM_MAX_BLK = 8;                        // row blocks per workgroup
+
+template <int NBG>
+struct KmCfg {
+    static constexpr int TABS = ((NBG + 1) / 2) * 65536;
+    static constexpr int AB_BLK = KM_MAX_G * 16 * 4;
+    static constexpr int AB = TABS;
+    static constexpr int LUTS = AB + NBG * AB_BLK;
+    static constexpr int SCL = LUTS + NBG * 512;     // [NBG][16 rows] int: row scale exponents
+    static constexpr int LDS = SCL + NBG * 64;
+    static constexpr int GS = KM_C * NBG;                                  // tiles per wave per group
+    static constexpr int D = GS > 8 ? (GS % 8 == 0 ? 8 : GS / 2) : GS;   // ring depth in tiles
+    static constexpr int DS = D / NBG;                                     // ... in chunks
+    static_assert(GS % D == 0 && D % NBG == 0, "the ring holds whole chunks of a group");
 };
 
-template <int MT, int W, int C>
-__global__ __launch_bounds__(64 * W) void k_gemm_res(const GemmArgs args)
+// (lane part | uniform part): either part may be OOR; valid parts are < 2^31.
+__device__ __forceinline__ uint32_t off2(uint32_t lane_part, uint32_t uni)
 {
-    using Cfg = ResCfg<W, C>;
+    return (lane_part | (uni & OOR)) + (uni & ~OOR);
+}
+
+// Largest biased exponent over the finite bf16 values of a row, whose 16
+// values are split over lanes l and l^1 (8 each in the 4 dwords of q).
+__device__ __forceinline__ int row_emax(const u32x4_t& q)
+{
+    int e = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e0 = (q[i] >> 7) & 0xFF;
+        const int e1 = (q[i] >> 23) & 0xFF;
+        e = max(e, e0 == 0xFF ? 0 : e0);
+        e = max(e, e1 == 0xFF ? 0 : e1);
+    }
+    return max(e, __shfl_xor(e, 1));
+}
+
+// Row scale exponent s: the largest finite magnitude times 2^-s lies in
+// [2^14, 2^15); at least -60 (rows of values below 2^-74).
+__device__ __forceinline__ int lut_scale(const u32x4_t& q)
+{
+    return max(row_emax(q) - 141, -60);
+}
+
+// 8 bf16 table values -> 8 f16 values times 2^-s
+__device__ __forceinline__ u32x4_t lut_to_f16(const u32x4_t& q, int s)
+{
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    u32x4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = __builtin_ldexpf(bf16_to_f32(q[i] & 0xFFFFu), -s);
+        const float hi = __builtin_ldexpf(bf16_to_f32(q[i] >> 16), -s);
+        const h2_t h = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+        r[i] = __builtin_bit_cast(uint32_t, h);
+    }
+    return r;
+}
+
+// bf16(a*L + b) for the two f16 table values of a pair dword, packed
+__device__ __forceinline__ uint32_t deq_pair(uint32_t d, float a, float b)
+{
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+    const h2_t l = __builtin_bit_cast(h2_t, d);
+    const f2_t w = {fmaf(a, static_cast<float>(l.x), b), fmaf(a, static_cast<float>(l.y), b)};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(w, bf2_t));
+}
+
+__device__ __forceinline__ u32x4_t deq_quad(const u32x4_t& q, float a, float b)
+{
+    return u32x4_t{deq_pair(q[0], a, b), deq_pair(q[1], a, b), deq_pair(q[2], a, b),
+                   deq_pair(q[3], a, b)};
+}
+
+template <int MT, int NBG>
+__global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
+{
+    using Cfg = KmCfg<NBG>;
+    constexpr int C = KM_C;
+    constexpr int GS = Cfg::GS;
     constexpr int D = Cfg::D;
+    constexpr int DS = Cfg::DS;
     constexpr int VC = MT < 4 ? MT : 4;
-    constexpr int XR = Cfg::template x_rows<MT>();
-    static_assert(W * C * TILE_K == RES_MAX_K, "one part covers K <= 4096");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::template lds<MT>()];
+    constexpr bool XSTREAM = MT > 2;
+    constexpr int XR = XSTREAM ? 1 : MT;   // resident x: rows fetched full width, via LDS
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS];
 
     const int M = args.M, N = args.N, K = args.K, g = args.g;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int j = lane & 15;      // tile row of this lane (B operand), x row m (A operand)
-    const int kq = lane >> 4;     // 32-k quarter of a chunk
+    const int j = lane & 15;
+    const int kq = lane >> 4;
     const int Kc = K / TILE_K;
     const int NB = (N + TILE_ROWS - 1) / TILE_ROWS;
     const int G = K / g;
     const int Gs = gridDim.x;
     const int r = blockIdx.x;
     const int nblk = r < NB ? (NB - 1 - r) / Gs + 1 : 0;
-    const int T = nblk * C;               // tiles in this wave's sequence
+    const int ngroups = (nblk + NBG - 1) / NBG;
     const int cbase = wave * C;
 
     const __amdgpu_buffer_rsrc_t rp =
         make_rsrc(args.packed, static_cast<uint32_t>(NB) * Kc * TILE_BYTES);
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(args.lut, static_cast<uint32_t>(N) * 32);
-    // alpha/beta are staged with 16-byte loads: the range is rounded up to 16 B
+    // alpha/beta are read with 16-byte loads: the range is rounded up to 16 B
     // (the 16-byte granule holding a valid byte never leaves that byte's page
     // when the base is 16-byte aligned); the extra values only reach rows >= N.
     const uint32_t ab_range = (static_cast<uint32_t>(N) * G * 2 + 15u) & ~15u;
@@ -401,81 +490,93 @@ __global__ __launch_bounds__(64 * W) void k_gemm_res(const GemmArgs args)
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(args.beta, ab_range);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(args.x, static_cast<uint32_t>(M) * K * 2);
 
-    // staging loads of block i: thread t < 32 fetches 16 B of the LUT rows,
-    // thread t < 2G fetches 16 B of alpha and of beta.  Offsets = a per-lane
-    // part (OOR for lanes with nothing to fetch) plus a uniform block part;
-    // blocks past the last one lie past the buffers, so no per-lane select
-    // (which the compiler may turn into branches) is needed.
-    const uint32_t ab_bytes = static_cast<uint32_t>(G) * 32;   // 16 rows x G x 2 B
-    const uint32_t lut_lane = tid < 32 ? static_cast<uint32_t>(tid) * 16 : OOR;
-    const uint32_t ab_lane = static_cast<uint32_t>(tid) * 16 < ab_bytes ? tid * 16 : OOR;
-    auto lut_load = [&](int i) {
-        return load16(rl, lut_lane + static_cast<uint32_t>(r + i * Gs) * 512);
+    // ---- staging of a group: wave b < NBG fetches block b's 16 table rows
+    // (lanes < 32) and its alpha and beta (lanes < 2G, 16 B each)
+    const uint32_t lut_lane = lane < 32 ? static_cast<uint32_t>(lane) * 16 : OOR;
+    const uint32_t ab_lane = lane < 2 * G ? static_cast<uint32_t>(lane) * 16 : OOR;
+    auto stage_load = [&](int gi, u32x4_t& lq, u32x4_t& aq, u32x4_t& bq) {
+        const int blk = gi * NBG + wave;
+        const bool live = wave < NBG && blk < nblk;
+        const uint32_t b = static_cast<uint32_t>(r + blk * Gs);
+        lq = load16(rl, off2(lut_lane, live ? b * 512 : OOR));
+        const uint32_t ao = off2(ab_lane, live ? b * (G * 32) : OOR);
+        aq = load16(ra, ao);
+        bq = load16(rb, ao);
     };
-    auto ab_load = [&](int i, u32x4_t& qa, u32x4_t& qb) {
-        const uint32_t off = ab_lane + static_cast<uint32_t>(r + i * Gs) * ab_bytes;
-        qa = load16(ra, off);
-        qb = load16(rb, off);
+    auto stage_store = [&](const u32x4_t& lq, const u32x4_t& aq, const u32x4_t& bq) {
+        // table rows as f16, scaled by 2^-s (s per row: the largest finite
+        // magnitude lands in [2^14, 2^15)), so every value within 2^31 of the
+        // row's largest is exact; the decode multiplies alpha by 2^s
+        const int sc = lut_scale(lq);   // all lanes: pairs of lanes share a row
+        const u32x4_t lh = lut_to_f16(lq, sc);
+        if (wave < NBG) {
+            if (lane < 32) {
+                lds_at<u32x4_t>(smem, Cfg::LUTS + wave * 512 + lane * 16) = lh;
+                if ((lane & 1) == 0)
+                    lds_at<int>(smem, Cfg::SCL + (wave * 16 + (lane >> 1)) * 4) = sc;
+            }
+            if (lane < 2 * G)
+                store_pairs(smem, Cfg::AB + wave * Cfg::AB_BLK, lane, G, aq, bq);
+        }
     };
-    auto lut_stage = [&](int buf, const u32x4_t& q) {
-        if (tid < 32)
-            lds_at<u32x4_t>(smem, Cfg::LUT + buf * 512 + tid * 16) = q;
-    };
-    auto ab_stage = [&](int buf, const u32x4_t& qa, const u32x4_t& qb) {
-        if (static_cast<uint32_t>(tid) * 16 < ab_bytes)
-            store_pairs(smem, Cfg::AB + buf * Cfg::AB_BYTES, tid, G, qa, qb);
+    auto build = [&](int bb) {
+        build_table<GW>(smem, Cfg::LUTS + bb * 512, (bb >> 1) * 16384 + (bb & 1) * 32, tid);
     };
 
-    // ---- tile ring (streamed once: non-temporal loads)
+    // ---- ring: tile v of group gi is chunk cbase + v / NBG of block
+    // gi*NBG + v % NBG (weights are streamed once: non-temporal loads); with
+    // XSTREAM, the x operands of chunk s of a group follow its first tile
     u32x4_t pb[D];
+    u32x4_t xq[XSTREAM ? DS : 1][4];
     const uint32_t tile_lane = static_cast<uint32_t>(lane) * 16;
-    auto issue = [&](int u, int t) {
-        const int i = t / C;
-        const int c = cbase + t % C;
-        const bool live = t < T && c < Kc;
-        const int b = r + i * Gs;
-        pb[u] = load16_nt(rp, live ? static_cast<uint32_t>(b * Kc + c) * TILE_BYTES + tile_lane
-                                   : OOR);
+    const uint32_t x_lane = j < M ? static_cast<uint32_t>(j * K + kq * 32) * 2 : OOR;
+    auto issue = [&](int gi, int uu) {
+        const int gg = gi + uu / GS;
+        const int v = uu % GS;
+        const int blk = gg * NBG + v % NBG;
+        const int c = cbase + v / NBG;
+        const bool live = blk < nblk && c < Kc;
+        // computed unconditionally and pushed out of range with one OR: a
+        // select here would become a branch around the load
+        const uint32_t uo = static_cast<uint32_t>((r + blk * Gs) * Kc + c) * TILE_BYTES |
+                            (static_cast<uint32_t>(!live) << 31);
+        pb[uu % D] = load16_nt(rp, off2(tile_lane, uo));
+        if constexpr (XSTREAM) {
+            if (v % NBG == NBG - 1) {
+                const bool xl = gg < ngroups && c < Kc;
+                const uint32_t xc =
+                    static_cast<uint32_t>(c) * TILE_K * 2 | (static_cast<uint32_t>(!xl) << 31);
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+                    xq[(uu / NBG) % DS][s4] = load16(rx, off2(x_lane, xc) + s4 * 16);
+            }
+        }
     };
 
-    // ---- prologue.  The loads of the staging registers go out before the
-    // ring, as they do in the loop, so that the waits the compiler derives for
-    // the loop (from both of its entries) leave the ring in flight.
-    u32x4_t l0 = lut_load(0), l1 = lut_load(1), a0, b0;
-    ab_load(0, a0, b0);
-    u32x4_t lq[2], aq[2], bq[2];
-    lq[0] = lut_load(2);
-    lq[1] = lut_load(3);
-    ab_load(1, aq[1], bq[1]);
-    ab_load(2, aq[0], bq[0]);
-    u32x4_t xr[C][4];
-    u32x4_t xw[XR > 0 ? XR : 1];
-    if constexpr (XR > 0) {
+    // ---- prologue
+    u32x4_t lq, aq, bq;
+    stage_load(0, lq, aq, bq);
+    u32x4_t xr[XSTREAM ? 1 : C][4];
+    u32x4_t xw[XR];
+    if constexpr (!XSTREAM) {
         // row m of x over this wave's C*128 k: lane l < 16C holds k = 8l .. 8l+7
         const int k0 = cbase * TILE_K + lane * 8;
         const uint32_t xk = (lane < 16 * C && k0 < K) ? static_cast<uint32_t>(k0) * 2 : OOR;
 #pragma unroll
         for (int m = 0; m < XR; ++m)
             xw[m] = load16(rx, m < M ? xk + static_cast<uint32_t>(m * K) * 2 : OOR);
-    } else {
-        const uint32_t x_lane = j < M ? static_cast<uint32_t>(j * K + kq * 32) * 2 : OOR;
-#pragma unroll
-        for (int ci = 0; ci < C; ++ci) {
-            const int c = cbase + ci;
-            const uint32_t xc = c < Kc ? static_cast<uint32_t>(c) * TILE_K * 2 : OOR;
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4)
-                xr[ci][s4] = load16(rx, (x_lane | (xc & OOR)) + (xc & ~OOR) + s4 * 16);
-        }
     }
+    constexpr int R0 = D < 2 ? D : 2;   // ring loads issued with the staging loads
 #pragma unroll
-    for (int u = 0; u < D; ++u)
-        issue(u, u);
-    if constexpr (XR > 0) {
-        // through this wave's own LDS rows into the operand layout: lane
-        // (j, kq) takes row j, k = 128 ci + 32 kq + 8 s4 .. +8 (zero for j >= M)
+    for (int u = 0; u < R0; ++u)
+        issue(0, u);
+    stage_store(lq, aq, bq);
+    if constexpr (!XSTREAM) {
+        // through this wave's own LDS rows (in the table region, free until
+        // the tables are built) into the operand layout: lane (j, kq) takes
+        // row j, k = 128 ci + 32 kq + 8 s4 .. +8 (zero for j >= M)
         constexpr int ROW = C * 256;
-        const uint32_t xs_base = Cfg::XS + wave * XR * ROW;
+        const uint32_t xs_base = wave * XR * ROW;
         if (lane < 16 * C) {
 #pragma unroll
             for (int m = 0; m < XR; ++m)
@@ -495,74 +596,125 @@ __global__ __launch_bounds__(64 * W) void k_gemm_res(const GemmArgs args)
                 for (int s4 = 0; s4 < 4; ++s4)
                     xr[ci][s4] = lds_at<u32x4_t>(smem, rb0 + ci * 256 + s4 * 16);
         }
-    }
-    lut_stage(0, l0);
-    lut_stage(1, l1);
-    ab_stage(0, a0, b0);
-    __syncthreads();
-    build_table<W>(smem, Cfg::LUT, 0, tid);
 
-    // chunk sums of x: lane l gets sum_k x[4*(l/16) + v][k] in xs[ci][v]
-    f32x4_t xs[C];
+    }
+    __syncthreads();
     {
-        const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+        constexpr int PER = (D - R0 + NBG - 1) / NBG;   // ring loads per table build
 #pragma unroll
-        for (int ci = 0; ci < C; ++ci) {
-            xs[ci] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int bb = 0; bb < NBG; ++bb) {
+            build(bb);
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4)
-                xs[ci] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, xr[ci][s4]), __builtin_bit_cast(bf16x8_t, ones),
-                    xs[ci], 0, 0, 0);
+            for (int u = R0 + bb * PER; u < R0 + (bb + 1) * PER && u < D; ++u)
+                issue(0, u);
         }
     }
     __syncthreads();
 
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem + Cfg::RED);
-    const uint32_t slot_lane = static_cast<uint32_t>(lane & 31) * 4;
-    int gi_c[C];
+    const uint32_t slot4 = static_cast<uint32_t>(lane & 31) * 4;
+    const uint32_t s1[2] = {slot4, slot4 | 0x10000u};   // region 0 / region 1
+    uint32_t ab_c[C];   // LDS offset of this lane's (alpha, beta) pair, block 0
 #pragma unroll
     for (int ci = 0; ci < C; ++ci)
-        gi_c[ci] = ((cbase + ci) * TILE_K) / g;
+        ab_c[ci] = Cfg::AB + ((((cbase + ci) * TILE_K) / g) * 16 + j) * 4;
 
-    for (int t0 = 0; t0 < T; t0 += D) {
+    constexpr int NA = NBG == 1 ? 2 : 1;   // one block: two chains, added at the end
+    f32x4_t acc[NBG][NA];
 #pragma unroll
-        for (int u = 0; u < D; ++u) {
-            const int t = t0 + u;
-            const int ci = u % C;
-            const int P = (u / C) & 1;  // parity of block i
-            const int i = t / C;
-            if (ci == 0) {
-                build_table<W>(smem, Cfg::LUT + ((i + 1) & 1) * 512, (i + 1) & 1, tid);
-                ab_stage(P ^ 1, aq[P ^ 1], bq[P ^ 1]);
-                lut_stage(P, lq[P]);
-                ab_load(i + 3, aq[P ^ 1], bq[P ^ 1]);
-                lq[P] = lut_load(i + 4);
-            }
-            {
-                // no branch around the decode, so the scheduler can overlap
-                // tiles; a tile past the sequence gets alpha = beta = 0
-                const uint32_t pr = t < T ? lds_at<uint32_t>(smem, Cfg::AB + P * Cfg::AB_BYTES +
-                                                                       (gi_c[ci] * 16 + j) * 4)
-                                          : 0u;
-                const f32x4_t ag = tile_dot(smem, P * 128 + slot_lane, pb[u], xr[ci]);
-                const float a = bf16_to_f32(pr & 0xFFFFu);
+    for (int bb = 0; bb < NBG; ++bb)
+#pragma unroll
+        for (int h = 0; h < NA; ++h)
+            acc[bb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    int rsc[NBG];   // scale exponent of this lane's row in each block's table
+    auto load_scales = [&]() {
+#pragma unroll
+        for (int bb = 0; bb < NBG; ++bb)
+            rsc[bb] = lds_at<int>(smem, Cfg::SCL + (bb * 16 + j) * 4);
+    };
+    load_scales();
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem);
+    auto reduce_store = [&](int gi) {   // after a barrier: tables are free
+#pragma unroll
+        for (int bb = 0; bb < NBG; ++bb) {
+            f32x4_t t = acc[bb][0];
+            if constexpr (NA > 1)
+                t += acc[bb][NA - 1];
+            red[(bb * GW + wave) * 64 + lane] = t;
+        }
+        __syncthreads();
+        const int blk = gi * NBG + wave;
+        if (wave < NBG && blk < nblk)
+            store_block<MT, GW>(red + wave * GW * 64, args.y, lane, M, N,
+                                (r + blk * Gs) * TILE_ROWS);
+    };
+
+    u32x4_t lqn, aqn, bqn;
+    for (int gi = 0; gi < ngroups; ++gi) {
+        if (gi > 0) {
+            __syncthreads();
+            reduce_store(gi - 1);
+            stage_store(lqn, aqn, bqn);
+            __syncthreads();
+#pragma unroll
+            for (int bb = 0; bb < NBG; ++bb)
+                build(bb);
+            __syncthreads();
+            load_scales();
+#pragma unroll
+            for (int bb = 0; bb < NBG; ++bb)
+#pragma unroll
+                for (int h = 0; h < NA; ++h)
+                    acc[bb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        stage_load(gi + 1, lqn, aqn, bqn);
+#pragma unroll
+        for (int u0 = 0; u0 < GS; u0 += 2) {
+            // two tiles at a time: lookups, w = bf16(alpha*L + beta) for every
+            // looked-up pair, then the two MFMA chains
+            u32x4_t bw[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int u = u0 + h;
+                const int s = u / NBG;
+                const int bb = u % NBG;
+                const u32x4_t p = pb[u % D];
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                    for (int jb = 0; jb < 4; ++jb)
+                        bw[h][s4][jb] = lds_at<uint32_t>(
+                            smem, __builtin_amdgcn_perm(p[s4], s1[bb >> 1],
+                                                        0x0C020000u | ((4u + jb) << 8)) +
+                                      (bb & 1) * 128);
+                const bool live = gi * NBG + bb < nblk && cbase + s < Kc;
+                const uint32_t pr = lds_at<uint32_t>(smem, ab_c[s] + bb * Cfg::AB_BLK) &
+                                    (live ? 0xFFFFFFFFu : 0u);
+                const float a = __builtin_ldexpf(bf16_to_f32(pr & 0xFFFFu), rsc[bb]);
                 const float bt = bf16_to_f32(pr >> 16);
 #pragma unroll
-                for (int v = 0; v < VC; ++v)
-                    acc[v] = fmaf(a, ag[v], fmaf(bt, xs[ci][v], acc[v]));
+                for (int s4 = 0; s4 < 4; ++s4)
+                    bw[h][s4] = deq_quad(bw[h][s4], a, bt);
             }
-            issue(u, t + D);
-            if (ci == C - 1) {
-                red[(P * W + wave) * 64 + lane] = acc;
-                acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                __syncthreads();
-                if (wave == i % W && i < nblk)
-                    store_block<MT, W>(red + P * W * 64, args.y, lane, M, N,
-                                       (r + i * Gs) * TILE_ROWS);
-            }
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int s = (u0 + h) / NBG;
+                    const int bb = (u0 + h) % NBG;
+                    const u32x4_t& xa = XSTREAM ? xq[s % DS][s4] : xr[XSTREAM ? 0 : s][s4];
+                    f32x4_t& ac = acc[bb][NBG == 1 ? h : 0];
+                    ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, xa), __builtin_bit_cast(bf16x8_t, bw[h][s4]),
+                        ac, 0, 0, 0);
+                }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                issue(gi, u0 + h + D);
         }
+    }
+    if (ngroups > 0) {
+        __syncthreads();
+        reduce_store(ngroups - 1);
     }
 }
 
@@ -705,21 +857,28 @@ any4_status launched()
     return hipGetLastError() == hipSuccess ? ANY4_OK : ANY4_E_HIP;
 }
 
-constexpr int RES_GRID = 256;   // k_gemm_res: one workgroup per CU of an MI355X
-#ifndef ANY4_RES_WAVES
-#define ANY4_RES_WAVES 8
-#endif
-constexpr int RES_W = ANY4_RES_WAVES;
-constexpr int RES_CW = RES_MAX_K / TILE_K / RES_W;
+constexpr int KM_GRID = 256;   // one workgroup per CU of an MI355X
 
 template <int MT>
 void launch_gemm(const GemmArgs& a, hipStream_t stream)
 {
     const int64_t NB = row_blocks(a.N);
-    if (a.K <= RES_MAX_K) {
-        const int grid = static_cast<int>(NB < RES_GRID ? NB : RES_GRID);
-        hipLaunchKernelGGL((k_gemm_res<MT, RES_W, RES_CW>), dim3(grid), dim3(64 * RES_W), 0,
-                           stream, a);
+    if (a.K <= KM_MAX_K) {
+        int64_t grid = NB < KM_GRID ? NB : KM_GRID;
+        if (grid * KM_MAX_BLK < NB)
+            grid = (NB + KM_MAX_BLK - 1) / KM_MAX_BLK;
+        const int64_t nb = (NB + grid - 1) / grid;               // blocks per workgroup
+        const int64_t groups = (nb + 3) / 4;
+        const int64_t nbg = (nb + groups - 1) / groups;           // blocks per group
+        const dim3 gd(static_cast<unsigned>(grid));
+        if (nbg == 1)
+            hipLaunchKernelGGL((k_gemm_km<MT, 1>), gd, dim3(GT), 0, stream, a);
+        else if (nbg == 2)
+            hipLaunchKernelGGL((k_gemm_km<MT, 2>), gd, dim3(GT), 0, stream, a);
+        else if (nbg == 3)
+            hipLaunchKernelGGL((k_gemm_km<MT, 3>), gd, dim3(GT), 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_gemm_km<MT, 4>), gd, dim3(GT), 0, stream, a);
     } else {
         hipLaunchKernelGGL(k_gemm_str<MT>, dim3(static_cast<unsigned>(NB)), dim3(GT), 0, stream,
                            a);

@@ -150,7 +150,11 @@ def test_gemm_config4_sampled_rows(name):
 @pytest.mark.parametrize("M,N,K,g", [(7, 16 * 700 + 5, 256, 128), (1, 16 * 1300, 512, 256),
                                      (1, 17, 128, 128), (3, 50, 384, 128), (5, 1, 256, 256),
                                      (7, 33, 1024, 512), (16, 15, 128, 128), (9, 100, 2048, 1024),
-                                     (12, 272, 640, 128), (2, 4097, 256, 128)])
+                                     (12, 272, 640, 128), (2, 4097, 256, 128),
+                                     # row blocks per workgroup 5..8: two groups of decoded
+                                     # blocks (3+2, 4+3, 4+4), and more than 256 workgroups
+                                     (4, 16 * 1100, 256, 128), (16, 16 * 1700 + 9, 128, 128),
+                                     (1, 16 * 2000 + 3, 128, 128), (3, 16 * 2100, 128, 128)])
 def test_gemm_ragged(M, N, K, g):
     inp = workloads.generic(M * 7 + N + K, M, N, K, g)
     L = gu.Layer(inp)
