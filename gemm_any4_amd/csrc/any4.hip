@@ -173,15 +173,13 @@ __global__ __launch_bounds__(256) void k_zero(uint16_t* __restrict__ y, size_t n
         y[i] = 0;
 }
 
-// Two kernels compute y = x * W^T; both work on 16-row blocks of W, with the
-// 8 waves of a workgroup splitting K and meeting in LDS at the end.
+// Two kernels compute y = x * W^T, both persistent and k-major: about one
+// workgroup per CU owns 16-row blocks r, r+G, r+2G, ... of W and decodes up
+// to four of them together, chunk (128 k) by chunk, against the same x
+// operands; the 8 waves split K and meet in LDS at the end.
 //
-//   k_gemm_km   (K <= 4096) persistent, k-major: about one workgroup per CU
-//               owns row blocks r, r+G, r+2G, ... and decodes up to four of
-//               them together, chunk by chunk, against the same x operands.
-//   k_gemm_str  (any K) one workgroup per row block; a wave decodes K/8 of
-//               the block and loads the x operand of each chunk with the
-//               chunk's tile.
+//   k_gemm_km   K <= 4096: a wave's 4 chunks, fully unrolled.
+//   k_gemm_kb   any K: a wave's K/1024 chunks in steps of the ring depth.
 //
 // Decode.  A packed byte (two indices) selects one dword of a pair table in
 // LDS: entry (hi << 4 | lo) holds the table values (L[lo], L[hi]) as two
@@ -206,7 +204,7 @@ __global__ __launch_bounds__(256) void k_zero(uint16_t* __restrict__ y, size_t n
 constexpr int GW = 8;                   // waves per workgroup
 constexpr int GT = 64 * GW;
 constexpr int TAB_BYTES = 256 * 256;    // 256 entries x 2 tables x 32 slots x 4 B
-constexpr int STR_MAX_G = 512;          // k_gemm_str: K/g up to 512 (two staging rounds)
+constexpr int MAX_G = 512;              // K/g: the alpha/beta staging of k_gemm_kb
 
 struct GemmArgs {
     const uint16_t* x;
@@ -287,25 +285,6 @@ __device__ __forceinline__ void store_pairs(uint8_t* smem, uint32_t base, int q,
             ++row;
         }
     }
-}
-
-// sum_k x*LUT[idx] over one tile: four MFMAs, B operands looked up in the
-// table through `slot4` (buffer and slot of this lane).
-__device__ __forceinline__ f32x4_t tile_dot(const uint8_t* smem, uint32_t slot4, const u32x4_t& p,
-                                            const u32x4_t (&xa)[4])
-{
-    f32x4_t ag = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-        u32x4_t bw;
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-            bw[jb] = *reinterpret_cast<const uint32_t*>(smem + tab_addr(p[s4], slot4, jb));
-        ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[s4]),
-                                                     __builtin_bit_cast(bf16x8_t, bw), ag, 0, 0,
-                                                     0);
-    }
-    return ag;
 }
 
 // The 8 waves' partial sums of one block, left by each wave in red[wave][lane],
@@ -538,8 +517,9 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
         const bool live = blk < nblk && c < Kc;
         // computed unconditionally and pushed out of range with one OR: a
         // select here would become a branch around the load
-        const uint32_t uo = static_cast<uint32_t>((r + blk * Gs) * Kc + c) * TILE_BYTES |
-                            (static_cast<uint32_t>(!live) << 31);
+        const uint32_t uo =
+            (static_cast<uint32_t>(r + blk * Gs) * static_cast<uint32_t>(Kc) + c) * TILE_BYTES |
+            (static_cast<uint32_t>(!live) << 31);
         pb[uu % D] = load16_nt(rp, off2(tile_lane, uo));
         if constexpr (XSTREAM) {
             if (v % NBG == NBG - 1) {
@@ -718,22 +698,56 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
     }
 }
 
-// ---- k_gemm_str: one row block per workgroup, x loaded per tile ----------
+// ---- k_gemm_kb: k-major for any K ------------------------------------------
 //
-// LDS: [0, 64K) table (buffer 0 used), red[8][64] f32x4 (8 KB), alpha/beta
-// pairs [16][K/g] dwords (<= 32 KB), LUT rows [16][16] bf16.
-constexpr int STR_D = 8;
-constexpr int STR_RED = TAB_BYTES;
-constexpr int STR_AB = STR_RED + GW * 64 * 16;
-constexpr int STR_LUT = STR_AB + 16 * STR_MAX_G * 4;
-constexpr int STR_LDS = STR_LUT + 512;
+// The k_gemm_km scheme for K > 4096: a workgroup owns row blocks r, r+Gs, ...
+// and decodes NBG of them together; wave w owns chunks [w*C, (w+1)*C) with
+// C = ceil(K/128 / 8), and walks them in steps of one chunk (the chunk's
+// tile of every block of the group).  The loop body is unrolled over DS
+// steps (the ring depth); a group's steps are padded to a multiple of DS
+// with dead steps (out-of-range loads, and a uniform branch skips their
+// decode).  x: with XL (M <= 2 and x small enough) the whole of x is copied
+// to LDS in the prologue and each chunk's operands are read from there by
+// the lanes of rows m < M; otherwise x travels in the ring, its operand
+// loads for a chunk following the chunk's last tile.  alpha and beta of a
+// whole group are staged in LDS by all threads, two 16-byte pieces per
+// thread and tensor at most.
+//
+// LDS:
+//   [0, TABS)  pair tables as in k_gemm_km (the partial sums reuse them)
+//   AB         [NBG][GMAX][16 rows] (alpha | beta << 16) dwords
+//   LUTS       [NBG][16 rows][16] f16, each row scaled by 2^-s
+//   SCL        [NBG][16 rows] int: the row scale exponents s
+//   XS         (XL) x as [M][K] bf16
+constexpr int KB_XL_PIECES = 7;   // 16-byte pieces of x per thread (XL): 56 KB
 
-template <int MT>
-__global__ __launch_bounds__(GT) void k_gemm_str(const GemmArgs args)
+template <int NBG, bool XL>
+struct KbCfg {
+    static constexpr int GMAX = NBG == 1 ? 512 : NBG == 2 ? 256 : NBG == 3 ? 144 : 112;
+    static constexpr int TABS = ((NBG + 1) / 2) * 65536;
+    static constexpr int AB_BLK = GMAX * 16 * 4;
+    static constexpr int AB = TABS;
+    static constexpr int LUTS = AB + NBG * AB_BLK;
+    static constexpr int SCL = LUTS + NBG * 512;
+    static constexpr int XS = SCL + NBG * 64;
+    static constexpr int XMAX = XL ? KB_XL_PIECES * GT * 16 : 0;   // bytes of x in LDS
+    static constexpr int LDS = XS + XMAX;
+    // ring depth in chunks: x in the ring costs 16 VGPRs per chunk
+    static constexpr int DS = XL ? (NBG == 1 ? 10 : NBG == 2 ? 6 : NBG == 3 ? 4 : 3)
+                                 : (NBG == 1 ? 6 : NBG == 2 ? 4 : 2);
+    static constexpr int D = DS * NBG;                             // ... in tiles
+    static_assert(D % 2 == 0, "tiles are decoded in pairs");
+    static_assert(LDS <= 160 * 1024, "LDS of one CU");
+};
+
+template <int MT, int NBG, bool XL>
+__global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
 {
-    constexpr int D = STR_D;
-    constexpr int VC = MT < 4 ? MT : 4;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[STR_LDS];
+    using Cfg = KbCfg<NBG, XL>;
+    constexpr int DS = Cfg::DS;
+    constexpr int D = Cfg::D;
+    constexpr int NA = NBG == 1 ? 2 : 1;   // one block: two chains, added at the end
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS];
 
     const int M = args.M, N = args.N, K = args.K, g = args.g;
     const int tid = threadIdx.x;
@@ -744,14 +758,19 @@ __global__ __launch_bounds__(GT) void k_gemm_str(const GemmArgs args)
     const int Kc = K / TILE_K;
     const int NB = (N + TILE_ROWS - 1) / TILE_ROWS;
     const int G = K / g;
-    const int b = blockIdx.x;
-    const int CB = (Kc + GW - 1) / GW;   // tiles per wave
-    const int c0 = wave * CB;
+    const int Gs = gridDim.x;
+    const int r = blockIdx.x;
+    const int nblk = r < NB ? (NB - 1 - r) / Gs + 1 : 0;
+    const int ngroups = (nblk + NBG - 1) / NBG;
+    const int C = (Kc + GW - 1) / GW;        // chunks per wave
+    const int CP = (C + DS - 1) / DS * DS;   // ... padded to whole bodies
+    const int cbase = wave * C;
+    const float inv_gc = 1.0f / static_cast<float>(g / TILE_K);   // chunk -> group
 
     const __amdgpu_buffer_rsrc_t rp =
         make_rsrc(args.packed, static_cast<uint32_t>(NB) * Kc * TILE_BYTES);
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(args.lut, static_cast<uint32_t>(N) * 32);
-    // alpha/beta are staged with 16-byte loads: the range is rounded up to 16 B
+    // alpha/beta are read with 16-byte loads: the range is rounded up to 16 B
     // (the 16-byte granule holding a valid byte never leaves that byte's page
     // when the base is 16-byte aligned); the extra values only reach rows >= N.
     const uint32_t ab_range = (static_cast<uint32_t>(N) * G * 2 + 15u) & ~15u;
@@ -759,79 +778,251 @@ __global__ __launch_bounds__(GT) void k_gemm_str(const GemmArgs args)
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(args.beta, ab_range);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(args.x, static_cast<uint32_t>(M) * K * 2);
 
-    // staging loads first, so that waiting for them leaves the ring in flight
-    const uint32_t ab_bytes = static_cast<uint32_t>(G) * 32;
-    const u32x4_t lq =
-        load16(rl, (tid < 32 ? static_cast<uint32_t>(tid) * 16 : OOR) + static_cast<uint32_t>(b) * 512);
-    u32x4_t aq[2], bq[2];
+    // ---- staging of a group.  Table rows: thread t < 32*NBG fetches piece
+    // t % 32 of block t / 32.  alpha and beta: piece q = t + 512h (h < 2) is
+    // piece q % 2G of block q / 2G.  Offsets carry the out-of-range bit
+    // instead of a select.
+    const int ab_per = 2 * G;
+    int ab_blk[2], ab_pc[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const uint32_t o = static_cast<uint32_t>(tid + h * GT) * 16;
-        const uint32_t off = (o < ab_bytes ? o : OOR) + static_cast<uint32_t>(b) * ab_bytes;
-        aq[h] = load16(ra, off);
-        bq[h] = load16(rb, off);
+        const int q = tid + h * GT;
+        ab_blk[h] = q / ab_per;
+        ab_pc[h] = q - ab_blk[h] * ab_per;
     }
-
-    u32x4_t pb[D];
-    u32x4_t px[D][4];
-    const uint32_t tile_lane = static_cast<uint32_t>(lane) * 16;
-    // x rows m >= M: a per-lane out-of-range base; dead tiles: a uniform one
-    const uint32_t x_lane = j < M ? static_cast<uint32_t>(j * K + kq * 32) * 2 : OOR;
-    auto issue = [&](int u, int t) {
-        const int c = c0 + t;
-        const bool live = t < CB && c < Kc;
-        pb[u] = load16(rp, live ? static_cast<uint32_t>(b * Kc + c) * TILE_BYTES + tile_lane : OOR);
-        const uint32_t xc = live ? static_cast<uint32_t>(c) * TILE_K * 2 : OOR;
+    auto stage_load = [&](int gi, u32x4_t& lq, u32x4_t (&aq)[2], u32x4_t (&bq)[2]) {
+        {
+            const int ib = tid >> 5;
+            const int blk = gi * NBG + ib;
+            const bool live = tid < 32 * NBG && blk < nblk;
+            const uint32_t o = (static_cast<uint32_t>(r + blk * Gs) * 512 + (tid & 31) * 16) |
+                               (static_cast<uint32_t>(!live) << 31);
+            lq = load16(rl, o);
+        }
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
-            px[u][s4] = load16(rx, (x_lane | (xc & OOR)) + (xc & ~OOR) + s4 * 16);
+        for (int h = 0; h < 2; ++h) {
+            const int blk = gi * NBG + ab_blk[h];
+            const bool live = ab_blk[h] < NBG && blk < nblk;
+            const uint32_t o =
+                (static_cast<uint32_t>(r + blk * Gs) * (G * 32) + ab_pc[h] * 16) |
+                (static_cast<uint32_t>(!live) << 31);
+            aq[h] = load16(ra, o);
+            bq[h] = load16(rb, o);
+        }
     };
+    auto stage_store = [&](const u32x4_t& lq, const u32x4_t (&aq)[2], const u32x4_t (&bq)[2]) {
+        const int sc = lut_scale(lq);   // all lanes: pairs of lanes share a row
+        const u32x4_t lh = lut_to_f16(lq, sc);
+        if (tid < 32 * NBG) {
+            lds_at<u32x4_t>(smem, Cfg::LUTS + tid * 16) = lh;
+            if ((tid & 1) == 0)
+                lds_at<int>(smem, Cfg::SCL + (tid >> 1) * 4) = sc;
+        }
 #pragma unroll
-    for (int u = 0; u < D; ++u)
-        issue(u, u);
+        for (int h = 0; h < 2; ++h)
+            if (ab_blk[h] < NBG)
+                store_pairs(smem, Cfg::AB + ab_blk[h] * Cfg::AB_BLK, ab_pc[h], G, aq[h], bq[h]);
+    };
+    auto build = [&](int bb) {
+        build_table<GW>(smem, Cfg::LUTS + bb * 512, (bb >> 1) * 16384 + (bb & 1) * 32, tid);
+    };
 
-    if (tid < 32)
-        lds_at<u32x4_t>(smem, STR_LUT + tid * 16) = lq;
+    // ---- ring.  Tile u of a body whose first step is (group gc, padded step
+    // sc) is chunk cbase + sc + u / NBG of block gc*NBG + u % NBG; past the
+    // group's CP steps the sequence continues with the next group.
+    u32x4_t pb[D];
+    u32x4_t xq[XL ? 1 : DS][4];
+    const uint32_t tile_lane = static_cast<uint32_t>(lane) * 16;
+    const uint32_t x_lane = j < M ? static_cast<uint32_t>(j * K + kq * 32) * 2 : OOR;
+    auto issue = [&](int gc, int sc, int uu) {
+        int st = sc + uu / NBG;
+        int gg = gc;
+        if (st >= CP) {
+            st -= CP;
+            ++gg;
+        }
+        const int bb = uu % NBG;
+        const int blk = gg * NBG + bb;
+        const int c = cbase + st;
+        const bool live = blk < nblk && st < C && c < Kc;
+        const uint32_t uo =
+            (static_cast<uint32_t>(r + blk * Gs) * static_cast<uint32_t>(Kc) + c) * TILE_BYTES |
+            (static_cast<uint32_t>(!live) << 31);
+        pb[uu % D] = load16_nt(rp, off2(tile_lane, uo));
+        if (!XL && bb == NBG - 1) {
+            const bool xl = gg < ngroups && st < C && c < Kc;
+            const uint32_t xc =
+                static_cast<uint32_t>(c) * TILE_K * 2 | (static_cast<uint32_t>(!xl) << 31);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-        if (static_cast<uint32_t>(tid + h * GT) * 16 < ab_bytes)
-            store_pairs(smem, STR_AB, tid + h * GT, G, aq[h], bq[h]);
-    __syncthreads();
-    build_table<GW>(smem, STR_LUT, 0, tid);
-    __syncthreads();
+            for (int s4 = 0; s4 < 4; ++s4)
+                xq[XL ? 0 : (uu / NBG) % DS][s4] = load16(rx, off2(x_lane, xc) + s4 * 16);
+        }
+    };
 
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    const uint32_t slot4 = static_cast<uint32_t>(lane & 31) * 4;
-    for (int t0 = 0; t0 < CB; t0 += D) {
+    // ---- prologue (as in k_gemm_km); with XL, x goes to LDS first
+    u32x4_t xc16[XL ? KB_XL_PIECES : 1];
+    const uint32_t xbytes = static_cast<uint32_t>(M) * K * 2;
+    if constexpr (XL) {
 #pragma unroll
-        for (int u = 0; u < D; ++u) {
-            const int t = t0 + u;
-            const int c = c0 + t;
-            if (t < CB && c < Kc) {
-                const uint32_t pr =
-                    lds_at<uint32_t>(smem, STR_AB + (((c * TILE_K) / g) * 16 + j) * 4);
-                const float a = bf16_to_f32(pr & 0xFFFFu);
-                const uint32_t b2 = (pr & 0xFFFF0000u) | (pr >> 16);
-                const u32x4_t bv = {b2, b2, b2, b2};
-                const f32x4_t ag = tile_dot(smem, slot4, pb[u], px[u]);
-#pragma unroll
-                for (int v = 0; v < VC; ++v)
-                    acc[v] = fmaf(a, ag[v], acc[v]);
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, px[u][s4]), __builtin_bit_cast(bf16x8_t, bv),
-                        acc, 0, 0, 0);
-            }
-            issue(u, t + D);
+        for (int i = 0; i < KB_XL_PIECES; ++i) {
+            const uint32_t o = static_cast<uint32_t>(tid + i * GT) * 16;
+            xc16[i] = load16(rx, o < xbytes ? o : OOR);
         }
     }
-
-    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem + STR_RED);
-    red[wave * 64 + lane] = acc;
+    u32x4_t lq, aq[2], bq[2];
+    stage_load(0, lq, aq, bq);
+    constexpr int R0 = 2;
+#pragma unroll
+    for (int u = 0; u < R0; ++u)
+        issue(0, 0, u);
+    stage_store(lq, aq, bq);
+    if constexpr (XL) {
+#pragma unroll
+        for (int i = 0; i < KB_XL_PIECES; ++i) {
+            const uint32_t o = static_cast<uint32_t>(tid + i * GT) * 16;
+            if (o < xbytes)
+                lds_at<u32x4_t>(smem, Cfg::XS + o) = xc16[i];
+        }
+    }
     __syncthreads();
-    if (wave == 0)
-        store_block<MT, GW>(red, args.y, lane, M, N, b * TILE_ROWS);
+    {
+        constexpr int PER = (D - R0 + NBG - 1) / NBG;
+#pragma unroll
+        for (int bb = 0; bb < NBG; ++bb) {
+            build(bb);
+#pragma unroll
+            for (int u = R0 + bb * PER; u < R0 + (bb + 1) * PER && u < D; ++u)
+                issue(0, 0, u);
+        }
+    }
+    __syncthreads();
+
+    const uint32_t slot4 = static_cast<uint32_t>(lane & 31) * 4;
+    const uint32_t s1[2] = {slot4, slot4 | 0x10000u};   // region 0 / region 1
+    f32x4_t acc[NBG][NA];
+#pragma unroll
+    for (int bb = 0; bb < NBG; ++bb)
+#pragma unroll
+        for (int h = 0; h < NA; ++h)
+            acc[bb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    int rsc[NBG];
+    auto load_scales = [&]() {
+#pragma unroll
+        for (int bb = 0; bb < NBG; ++bb)
+            rsc[bb] = lds_at<int>(smem, Cfg::SCL + (bb * 16 + j) * 4);
+    };
+    load_scales();
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(smem);
+    auto reduce_store = [&](int gi) {   // after a barrier: tables are free
+#pragma unroll
+        for (int bb = 0; bb < NBG; ++bb) {
+            f32x4_t t = acc[bb][0];
+            if constexpr (NA > 1)
+                t += acc[bb][NA - 1];
+            red[(bb * GW + wave) * 64 + lane] = t;
+        }
+        __syncthreads();
+        const int blk = gi * NBG + wave;
+        if (wave < NBG && blk < nblk)
+            store_block<MT, GW>(red + wave * GW * 64, args.y, lane, M, N,
+                                (r + blk * Gs) * TILE_ROWS);
+    };
+
+    u32x4_t lqn, aqn[2], bqn[2];
+    const int total = ngroups * (CP / DS);
+    int gc = 0, sc = 0;   // group and padded step of the body's first chunk
+    for (int it = 0; it < total; ++it) {
+        if (sc == 0) {
+            if (gc > 0) {
+                __syncthreads();
+                reduce_store(gc - 1);
+                stage_store(lqn, aqn, bqn);
+                __syncthreads();
+#pragma unroll
+                for (int bb = 0; bb < NBG; ++bb)
+                    build(bb);
+                __syncthreads();
+                load_scales();
+#pragma unroll
+                for (int bb = 0; bb < NBG; ++bb)
+#pragma unroll
+                    for (int h = 0; h < NA; ++h)
+                        acc[bb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+            stage_load(gc + 1, lqn, aqn, bqn);
+        }
+#pragma unroll
+        for (int u0 = 0; u0 < D; u0 += 2) {
+          const int st0 = sc + u0 / NBG, st1 = sc + (u0 + 1) / NBG;
+          const bool live0 = gc * NBG + u0 % NBG < nblk && st0 < C && cbase + st0 < Kc;
+          const bool live1 = gc * NBG + (u0 + 1) % NBG < nblk && st1 < C && cbase + st1 < Kc;
+          if (live0 || live1) {   // uniform: dead pairs (padding, absent blocks) are skipped
+            u32x4_t bw[2][4];
+            u32x4_t xv[XL ? 2 : 1][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int u = u0 + h;
+                const int st = sc + u / NBG;
+                const int bb = u % NBG;
+                const u32x4_t p = pb[u];
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                    for (int jb = 0; jb < 4; ++jb)
+                        bw[h][s4][jb] = lds_at<uint32_t>(
+                            smem, __builtin_amdgcn_perm(p[s4], s1[bb >> 1],
+                                                        0x0C020000u | ((4u + jb) << 8)) +
+                                      (bb & 1) * 128);
+                const int c = cbase + st;
+                const bool live = gc * NBG + bb < nblk && st < C && c < Kc;
+                const int grp =
+                    min(static_cast<int>((static_cast<float>(c) + 0.5f) * inv_gc), G - 1);
+                const uint32_t pr =
+                    lds_at<uint32_t>(smem, Cfg::AB + bb * Cfg::AB_BLK + (grp * 16 + j) * 4) &
+                    (live ? 0xFFFFFFFFu : 0u);
+                const float a = __builtin_ldexpf(bf16_to_f32(pr & 0xFFFFu), rsc[bb]);
+                const float bt = bf16_to_f32(pr >> 16);
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+                    bw[h][s4] = deq_quad(bw[h][s4], a, bt);
+                if constexpr (XL) {
+                    // the chunk's x in the operand layout; lanes of rows m >= M
+                    // read row M-1 (those MFMA rows are never stored), so no
+                    // branch splits the body
+                    const uint32_t xo =
+                        Cfg::XS + (static_cast<uint32_t>(j < M ? j : M - 1) * K + c * TILE_K +
+                                   kq * 32) * 2;
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4)
+                        xv[h][s4] = lds_at<u32x4_t>(smem, xo + s4 * 16);
+                }
+            }
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int u = u0 + h;
+                    f32x4_t& ac = acc[u % NBG][NBG == 1 ? h : 0];
+                    const u32x4_t& xa = XL ? xv[XL ? h : 0][s4] : xq[XL ? 0 : u / NBG][s4];
+                    ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, xa), __builtin_bit_cast(bf16x8_t, bw[h][s4]),
+                        ac, 0, 0, 0);
+                }
+          }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                issue(gc, sc, u0 + h + D);
+        }
+        sc += DS;
+        if (sc == CP) {
+            sc = 0;
+            ++gc;
+        }
+    }
+    if (ngroups > 0) {
+        __syncthreads();
+        reduce_store(ngroups - 1);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -863,14 +1054,14 @@ template <int MT>
 void launch_gemm(const GemmArgs& a, hipStream_t stream)
 {
     const int64_t NB = row_blocks(a.N);
+    int64_t grid = NB < KM_GRID ? NB : KM_GRID;
+    if (grid * KM_MAX_BLK < NB)
+        grid = (NB + KM_MAX_BLK - 1) / KM_MAX_BLK;
+    const int64_t nb = (NB + grid - 1) / grid;                // row blocks per workgroup
+    int64_t groups = (nb + 3) / 4;
+    int64_t nbg = (nb + groups - 1) / groups;                 // ... decoded together
+    const dim3 gd(static_cast<unsigned>(grid));
     if (a.K <= KM_MAX_K) {
-        int64_t grid = NB < KM_GRID ? NB : KM_GRID;
-        if (grid * KM_MAX_BLK < NB)
-            grid = (NB + KM_MAX_BLK - 1) / KM_MAX_BLK;
-        const int64_t nb = (NB + grid - 1) / grid;               // blocks per workgroup
-        const int64_t groups = (nb + 3) / 4;
-        const int64_t nbg = (nb + groups - 1) / groups;           // blocks per group
-        const dim3 gd(static_cast<unsigned>(grid));
         if (nbg == 1)
             hipLaunchKernelGGL((k_gemm_km<MT, 1>), gd, dim3(GT), 0, stream, a);
         else if (nbg == 2)
@@ -879,10 +1070,33 @@ void launch_gemm(const GemmArgs& a, hipStream_t stream)
             hipLaunchKernelGGL((k_gemm_km<MT, 3>), gd, dim3(GT), 0, stream, a);
         else
             hipLaunchKernelGGL((k_gemm_km<MT, 4>), gd, dim3(GT), 0, stream, a);
-    } else {
-        hipLaunchKernelGGL(k_gemm_str<MT>, dim3(static_cast<unsigned>(NB)), dim3(GT), 0, stream,
-                           a);
+        return;
     }
+    // alpha/beta of a group must fit the LDS staging of k_gemm_kb
+    const int64_t G = a.K / a.g;
+    while (nbg > 1 && G > (nbg == 4 ? KbCfg<4, false>::GMAX
+                                    : nbg == 3 ? KbCfg<3, false>::GMAX : KbCfg<2, false>::GMAX))
+        --nbg;
+    // x in LDS: M <= 2, at most two blocks per group, and x small enough
+    const bool xl = MT <= 2 && nbg <= 2 &&
+                    static_cast<int64_t>(a.M) * a.K * 2 <= KbCfg<1, true>::XMAX;
+    if (xl) {
+        if constexpr (MT <= 2) {
+            if (nbg == 1)
+                hipLaunchKernelGGL((k_gemm_kb<MT, 1, true>), gd, dim3(GT), 0, stream, a);
+            else
+                hipLaunchKernelGGL((k_gemm_kb<MT, 2, true>), gd, dim3(GT), 0, stream, a);
+        }
+        return;
+    }
+    if (nbg == 1)
+        hipLaunchKernelGGL((k_gemm_kb<MT, 1, false>), gd, dim3(GT), 0, stream, a);
+    else if (nbg == 2)
+        hipLaunchKernelGGL((k_gemm_kb<MT, 2, false>), gd, dim3(GT), 0, stream, a);
+    else if (nbg == 3)
+        hipLaunchKernelGGL((k_gemm_kb<MT, 3, false>), gd, dim3(GT), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_gemm_kb<MT, 4, false>), gd, dim3(GT), 0, stream, a);
 }
 
 }  // namespace
@@ -976,7 +1190,7 @@ any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* 
 {
     (void)workspace;
     (void)workspace_bytes;
-    if (M < 0 || M > 16 || N < 0 || !group_ok(K, g) || K / (g > 0 ? g : 1) > STR_MAX_G)
+    if (M < 0 || M > 16 || N < 0 || !group_ok(K, g) || K / (g > 0 ? g : 1) > MAX_G)
         return ANY4_E_SHAPE;
     if (any4_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31) ||
         static_cast<size_t>(M) * K * 2 >= (static_cast<size_t>(1) << 31) ||

@@ -164,10 +164,13 @@ def test_gemm_ragged(M, N, K, g):
     gu.assert_within_bound(y, y_ref, ad, f"ragged {M}x{N}x{K} g{g}")
 
 
-# Large K: one workgroup per 16-row block, x loaded with each tile.
+# Large K (> 4096): x staged in LDS (M <= 2, x <= 56 KB) or carried with the
+# tiles; one or two row blocks decoded together, one or two groups of them.
 @pytest.mark.parametrize("M,N,K,g", [(1, 64, 16384, 128), (16, 100, 8192, 1024),
                                      (4, 300, 14336, 1024), (2, 17, 28672, 128),
-                                     (16, 33, 65536, 128), (3, 16, 4224, 384)])
+                                     (16, 33, 65536, 128), (3, 16, 4224, 384),
+                                     (2, 16 * 300 + 7, 8192, 128), (1, 16 * 1000, 20480, 128),
+                                     (5, 16 * 900, 6144, 256)])
 def test_gemm_large_k(M, N, K, g):
     inp = workloads.generic(M * 3 + N + K, M, N, K, g)
     L = gu.Layer(inp)
