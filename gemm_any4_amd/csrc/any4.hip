@@ -649,6 +649,13 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
         stage_load(gi + 1, lqn, aqn, bqn);
 #pragma unroll
         for (int u0 = 0; u0 < GS; u0 += 2) {
+            // Issue priority alternates every two pairs.  Two waves share a
+            // SIMD; at equal priority the older one is always preferred, runs
+            // ahead, and the younger one then finishes alone.
+            if ((u0 >> 2) & 1)
+                __builtin_amdgcn_s_setprio(1);
+            else
+                __builtin_amdgcn_s_setprio(0);
             // two tiles at a time: lookups, w = bf16(alpha*L + beta) for every
             // looked-up pair, then the two MFMA chains
             u32x4_t bw[2][4];
@@ -692,6 +699,7 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
                 issue(gi, u0 + h + D);
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (ngroups > 0) {
         __syncthreads();
         reduce_store(ngroups - 1);
@@ -953,6 +961,11 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
         }
 #pragma unroll
         for (int u0 = 0; u0 < D; u0 += 2) {
+          // issue priority alternates every two pairs (see k_gemm_km)
+          if ((u0 >> 2) & 1)
+              __builtin_amdgcn_s_setprio(1);
+          else
+              __builtin_amdgcn_s_setprio(0);
           const int st0 = sc + u0 / NBG, st1 = sc + (u0 + 1) / NBG;
           const bool live0 = gc * NBG + u0 % NBG < nblk && st0 < C && cbase + st0 < Kc;
           const bool live1 = gc * NBG + (u0 + 1) % NBG < nblk && st1 < C && cbase + st1 < Kc;
@@ -1019,6 +1032,7 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
             ++gc;
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (ngroups > 0) {
         __syncthreads();
         reduce_store(ngroups - 1);
