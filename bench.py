@@ -17,6 +17,10 @@ where the algorithmic bytes of one launch are
     N*K/2 (indices) + 4*N*K/g (alpha, beta) + 32*N (tables) + 2*M*K (x) + 2*M*N (y).
 Per-M launch durations come from graphs of that M alone (same events).
 
+The same graph timing is also reported, outside `value`, for the other
+headline layer (N=4096, K=14336, g=1024, config 3 of the survey) at M=1 and
+M=16, under "other_layers".
+
 Prints one JSON line.  --traffic-probe instead runs a few launches of each M
 plus a device copy of known size, for hardware-counter collection.
 """
@@ -105,12 +109,13 @@ def cpu_baseline(seconds: float) -> dict:
     }
 
 
-def _setup(torch, any4, workloads, sets_arg: int):
+def _setup(torch, any4, workloads, sets_arg: int, cfg: int = 2):
     import numpy as np
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    inp = workloads.generate(2)
+    inp = workloads.generate(cfg)
+    N_, K_, G_ = inp.N, inp.K, inp.g
     wb = weight_bytes(N_, K_, G_)
     R = sets_arg or max(2, math.ceil(2 * CACHE_BYTES / wb) + 1)
 
@@ -125,6 +130,35 @@ def _setup(torch, any4, workloads, sets_arg: int):
     x = b16(inp.x)
     ys = {M: torch.empty((M, N_), dtype=torch.bfloat16, device=dev) for M in MS}
     return dev, R, sets, x, ys
+
+
+def other_layer(torch, any4, workloads, cfg: int, steps: int) -> dict:
+    """Per-launch µs of any4_gemm on config `cfg`'s layer at each M in MS
+    (graph replays over rotating weight sets, as for the main workload)."""
+    import numpy as np
+
+    c = workloads.CONFIGS[cfg]
+    dev, R, sets, x, ys = _setup(torch, any4, workloads, 0, cfg)
+
+    def launch(i: int, M: int):
+        p, l, a, b = sets[i % R]
+        any4.gemm(x[:M], p, l, a, b, c.g, out=ys[M])
+
+    out = {"N": c.N, "K": c.K, "g": c.g, "rotating_weight_sets": R}
+    for M in MS:
+        for i in range(5):
+            launch(i, M)
+        g = _graph(torch, launch, steps, (M,))
+        _time_graph(torch, g)
+        us = float(np.median([_time_graph(torch, g) * 1e3 / steps for _ in range(3)]))
+        bts = algorithmic_bytes(M, c.N, c.K, c.g)
+        out[str(M)] = {"us_per_launch": us, "bytes": bts,
+                       "tbps": bts / (us * 1e-6) / 1e12,
+                       "pct_hbm_peak": 100.0 * bts / (us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+        del g
+    del sets
+    torch.cuda.empty_cache()
+    return out
 
 
 def _graph(torch, launch, steps: int, Ms):
@@ -182,6 +216,7 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=0, help="rotating weight sets (0 = auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-layers", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true")
     args = ap.parse_args()
 
@@ -247,7 +282,7 @@ def main() -> int:
     achieved = dm["bytes"] / (dm["us_per_launch"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": _traffic(dom),
-                "kernel": f"k_gemm_res (any4_gemm, M={dom})",
+                "kernel": f"k_gemm_km (any4_gemm, M={dom})",
                 "bytes_per_launch": dm["bytes"], "launch_us": dm["us_per_launch"]}
 
     out = {
@@ -262,6 +297,10 @@ def main() -> int:
         "per_m": per_m,
         "host_wall_s": wall,
     }
+    if not args.no_other_layers:
+        del g_all, g_m, sets
+        torch.cuda.empty_cache()
+        out["other_layers"] = {"config3": other_layer(torch, any4, workloads, 3, min(K, 100))}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
