@@ -330,15 +330,17 @@ __device__ __forceinline__ void store_block(const f32x4_t* red, uint16_t* y, int
 // takes an f16 half of the looked-up dword directly, so a dword of two
 // weights costs two fma_mix and one v_cvt_pk_bf16_f32.
 //
-// x: for M <= 2 the operands of the wave's 512 k are loaded once, in the
-// prologue, into VGPRs.  For larger M they travel in the ring with the
-// tiles: a chunk's 4 operand loads are issued right after the chunk's last
+// x: for M <= 2 the whole of x (<= 16 KB) is copied to LDS in the prologue
+// and each pair's operands are read from there (lanes of rows m >= M read
+// row M-1: those MFMA rows are never stored).  For larger M they travel in
+// the ring with the tiles: a chunk's 4 operand loads are issued right after the chunk's last
 // tile (its slot is free by then: the chunk DS chunks earlier, which used it,
 // has just been decoded), so waiting for them never waits for a later chunk.
 //
 // Decode: two tiles at a time (two blocks of one chunk, or two chunks): the
 // 32 table lookups, the dequantisation, then the two MFMA chains
-// interleaved, so the chains' latencies overlap.
+// interleaved, so the chains' latencies overlap; the next pair's lookups are
+// issued before the current pair is dequantised.
 //
 // Prologue: the first ring loads go out with the staging loads; the rest are
 // spread over the table builds, so the builds overlap the first tiles'
@@ -351,6 +353,7 @@ __device__ __forceinline__ void store_block(const f32x4_t* red, uint16_t* y, int
 //   AB         [NBG][G <= 32][16 rows] (alpha | beta << 16) dwords
 //   LUTS       [NBG][16 rows][16] f16, each row scaled by 2^-s
 //   SCL        [NBG][16 rows] int: the row scale exponents s
+//   XS         (M <= 2) x as [M][K] bf16
 constexpr int KM_C = 4;                              // chunks per wave
 constexpr int KM_MAX_K = GW * KM_C * TILE_K;         // 4096
 constexpr int KM_MAX_G = KM_MAX_K / TILE_K;          // g >= 128
@@ -363,7 +366,8 @@ struct KmCfg {
     static constexpr int AB = TABS;
     static constexpr int LUTS = AB + NBG * AB_BLK;
     static constexpr int SCL = LUTS + NBG * 512;     // [NBG][16 rows] int: row scale exponents
-    static constexpr int LDS = SCL + NBG * 64;
+    static constexpr int XS = SCL + NBG * 64;        // x as [M <= 2][K <= 4096] bf16
+    static constexpr int LDS = XS + 2 * KM_MAX_K * 2;
     static constexpr int GS = KM_C * NBG;                                  // tiles per wave per group
     static constexpr int D = GS > 8 ? (GS % 8 == 0 ? 8 : GS / 2) : GS;   // ring depth in tiles
     static constexpr int DS = D / NBG;                                     // ... in chunks
@@ -440,7 +444,6 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
     constexpr int DS = Cfg::DS;
     constexpr int VC = MT < 4 ? MT : 4;
     constexpr bool XSTREAM = MT > 2;
-    constexpr int XR = XSTREAM ? 1 : MT;   // resident x: rows fetched full width, via LDS
     __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS];
 
     const int M = args.M, N = args.N, K = args.K, g = args.g;
@@ -536,15 +539,15 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
     // ---- prologue
     u32x4_t lq, aq, bq;
     stage_load(0, lq, aq, bq);
-    u32x4_t xr[XSTREAM ? 1 : C][4];
-    u32x4_t xw[XR];
+    // x (M <= 2): the whole of x to LDS, two 16-byte pieces per thread
+    u32x4_t xc16[2];
+    const uint32_t xbytes = static_cast<uint32_t>(M) * K * 2;
     if constexpr (!XSTREAM) {
-        // row m of x over this wave's C*128 k: lane l < 16C holds k = 8l .. 8l+7
-        const int k0 = cbase * TILE_K + lane * 8;
-        const uint32_t xk = (lane < 16 * C && k0 < K) ? static_cast<uint32_t>(k0) * 2 : OOR;
 #pragma unroll
-        for (int m = 0; m < XR; ++m)
-            xw[m] = load16(rx, m < M ? xk + static_cast<uint32_t>(m * K) * 2 : OOR);
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t o = static_cast<uint32_t>(tid + i * GT) * 16;
+            xc16[i] = load16(rx, o < xbytes ? o : OOR);
+        }
     }
     constexpr int R0 = D < 2 ? D : 2;   // ring loads issued with the staging loads
 #pragma unroll
@@ -552,31 +555,13 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
         issue(0, u);
     stage_store(lq, aq, bq);
     if constexpr (!XSTREAM) {
-        // through this wave's own LDS rows (in the table region, free until
-        // the tables are built) into the operand layout: lane (j, kq) takes
-        // row j, k = 128 ci + 32 kq + 8 s4 .. +8 (zero for j >= M)
-        constexpr int ROW = C * 256;
-        const uint32_t xs_base = wave * XR * ROW;
-        if (lane < 16 * C) {
+        // past x the region is zeroed: chunks past K read it (their weights
+        // are zero, and 0 * NaN left over in LDS would not be)
 #pragma unroll
-            for (int m = 0; m < XR; ++m)
-                lds_at<u32x4_t>(smem, xs_base + m * ROW + lane * 16) = xw[m];
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t o = static_cast<uint32_t>(tid + i * GT) * 16;
+            lds_at<u32x4_t>(smem, Cfg::XS + o) = o < xbytes ? xc16[i] : u32x4_t{0u, 0u, 0u, 0u};
         }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int ci = 0; ci < C; ++ci)
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4)
-                xr[ci][s4] = u32x4_t{0u, 0u, 0u, 0u};
-        if (j < M) {
-            const uint32_t rb0 = xs_base + j * ROW + kq * 64;
-#pragma unroll
-            for (int ci = 0; ci < C; ++ci)
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4)
-                    xr[ci][s4] = lds_at<u32x4_t>(smem, rb0 + ci * 256 + s4 * 16);
-        }
-
     }
     __syncthreads();
     {
@@ -647,18 +632,13 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
                     acc[bb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
         stage_load(gi + 1, lqn, aqn, bqn);
-#pragma unroll
-        for (int u0 = 0; u0 < GS; u0 += 2) {
-            // Issue priority alternates every two pairs.  Two waves share a
-            // SIMD; at equal priority the older one is always preferred, runs
-            // ahead, and the younger one then finishes alone.
-            if ((u0 >> 2) & 1)
-                __builtin_amdgcn_s_setprio(1);
-            else
-                __builtin_amdgcn_s_setprio(0);
-            // two tiles at a time: lookups, w = bf16(alpha*L + beta) for every
-            // looked-up pair, then the two MFMA chains
-            u32x4_t bw[2][4];
+        // Decode, software-pipelined over pairs of tiles: the 32 table lookups
+        // (and two alpha/beta reads) of the next pair are issued before the
+        // current pair is dequantised, so their LDS latency is covered by the
+        // current pair's VALU work.
+        u32x4_t bwp[2][2][4];
+        uint32_t prp[2][2];
+        auto fetch = [&](int u0, u32x4_t (&bw)[2][4], uint32_t (&pr)[2]) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int u = u0 + h;
@@ -673,9 +653,47 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
                             smem, __builtin_amdgcn_perm(p[s4], s1[bb >> 1],
                                                         0x0C020000u | ((4u + jb) << 8)) +
                                       (bb & 1) * 128);
+                pr[h] = lds_at<uint32_t>(smem, ab_c[s] + bb * Cfg::AB_BLK);
+            }
+        };
+        fetch(0, bwp[0], prp[0]);
+#pragma unroll
+        for (int u0 = 0; u0 < GS; u0 += 2) {
+            // Issue priority alternates every two pairs.  Two waves share a
+            // SIMD; at equal priority the older one is always preferred, runs
+            // ahead, and the younger one then finishes alone.
+            if ((u0 >> 2) & 1)
+                __builtin_amdgcn_s_setprio(1);
+            else
+                __builtin_amdgcn_s_setprio(0);
+            const int cur = (u0 >> 1) & 1;
+            if (u0 + 2 < GS)
+                fetch(u0 + 2, bwp[cur ^ 1], prp[cur ^ 1]);
+            u32x4_t (&bw)[2][4] = bwp[cur];
+            // x of the pair's chunk(s) from LDS (M <= 2); lanes of rows m >= M
+            // read row M-1: those MFMA rows are never stored
+            // (a pair spans two chunks when NBG is odd)
+            constexpr int NX = NBG % 2 == 1 ? 2 : 1;
+            u32x4_t xv[XSTREAM ? 1 : NX][4];
+            if constexpr (!XSTREAM) {
+#pragma unroll
+                for (int h = 0; h < NX; ++h) {
+                    const int c = cbase + (u0 + h) / NBG;
+                    const uint32_t xo =
+                        Cfg::XS +
+                        (static_cast<uint32_t>(j < M ? j : M - 1) * K + c * TILE_K + kq * 32) * 2;
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4)
+                        xv[h][s4] = lds_at<u32x4_t>(smem, xo + s4 * 16);
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int u = u0 + h;
+                const int s = u / NBG;
+                const int bb = u % NBG;
                 const bool live = gi * NBG + bb < nblk && cbase + s < Kc;
-                const uint32_t pr = lds_at<uint32_t>(smem, ab_c[s] + bb * Cfg::AB_BLK) &
-                                    (live ? 0xFFFFFFFFu : 0u);
+                const uint32_t pr = prp[cur][h] & (live ? 0xFFFFFFFFu : 0u);
                 const float a = __builtin_ldexpf(bf16_to_f32(pr & 0xFFFFu), rsc[bb]);
                 const float bt = bf16_to_f32(pr >> 16);
 #pragma unroll
@@ -688,7 +706,8 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
                 for (int h = 0; h < 2; ++h) {
                     const int s = (u0 + h) / NBG;
                     const int bb = (u0 + h) % NBG;
-                    const u32x4_t& xa = XSTREAM ? xq[s % DS][s4] : xr[XSTREAM ? 0 : s][s4];
+                    const u32x4_t& xa =
+                        XSTREAM ? xq[s % DS][s4] : xv[XSTREAM || NX == 1 ? 0 : h][s4];
                     f32x4_t& ac = acc[bb][NBG == 1 ? h : 0];
                     ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8_t, xa), __builtin_bit_cast(bf16x8_t, bw[h][s4]),
@@ -885,11 +904,11 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
         issue(0, 0, u);
     stage_store(lq, aq, bq);
     if constexpr (XL) {
+        // past x the region is zeroed (see k_gemm_km)
 #pragma unroll
         for (int i = 0; i < KB_XL_PIECES; ++i) {
             const uint32_t o = static_cast<uint32_t>(tid + i * GT) * 16;
-            if (o < xbytes)
-                lds_at<u32x4_t>(smem, Cfg::XS + o) = xc16[i];
+            lds_at<u32x4_t>(smem, Cfg::XS + o) = o < xbytes ? xc16[i] : u32x4_t{0u, 0u, 0u, 0u};
         }
     }
     __syncthreads();
@@ -1002,8 +1021,10 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
                     // the chunk's x in the operand layout; lanes of rows m >= M
                     // read row M-1 (those MFMA rows are never stored), so no
                     // branch splits the body
+                    // a dead tile (w = 0) past K reads the last chunk: any finite x
+                    const int cx = c < Kc ? c : Kc - 1;
                     const uint32_t xo =
-                        Cfg::XS + (static_cast<uint32_t>(j < M ? j : M - 1) * K + c * TILE_K +
+                        Cfg::XS + (static_cast<uint32_t>(j < M ? j : M - 1) * K + cx * TILE_K +
                                    kq * 32) * 2;
 #pragma unroll
                     for (int s4 = 0; s4 < 4; ++s4)
