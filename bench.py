@@ -18,8 +18,10 @@ where the algorithmic bytes of one launch are
 Per-M launch durations come from graphs of that M alone (same events).
 
 The same graph timing is also reported, outside `value`, for the other
-headline layer (N=4096, K=14336, g=1024, config 3 of the survey) at M=1 and
-M=16, under "other_layers".
+layer shape, the MLP down projection N=4096, K=14336, g=1024, at M=1 and
+M=16, under "other_layers"; and for both layers with plain int4 weights
+(any4_gemm_int4 on the same codes, scales and offsets, no table), under
+"int4_no_table", which puts a number on what the table lookup costs.
 
 Prints one JSON line.  --traffic-probe instead runs a few launches of each M
 plus a device copy of known size, for hardware-counter collection.
@@ -132,9 +134,10 @@ def _setup(torch, any4, workloads, sets_arg: int, cfg: int = 2):
     return dev, R, sets, x, ys
 
 
-def other_layer(torch, any4, workloads, cfg: int, steps: int) -> dict:
-    """Per-launch µs of any4_gemm on config `cfg`'s layer at each M in MS
-    (graph replays over rotating weight sets, as for the main workload)."""
+def other_layer(torch, any4, workloads, cfg: int, steps: int, int4: bool = False) -> dict:
+    """Per-launch µs of any4_gemm (or, with int4, of any4_gemm_int4 on the same
+    codes, scales and offsets) on config `cfg`'s layer at each M in MS (graph
+    replays over rotating weight sets, as for the main workload)."""
     import numpy as np
 
     c = workloads.CONFIGS[cfg]
@@ -142,7 +145,10 @@ def other_layer(torch, any4, workloads, cfg: int, steps: int) -> dict:
 
     def launch(i: int, M: int):
         p, l, a, b = sets[i % R]
-        any4.gemm(x[:M], p, l, a, b, c.g, out=ys[M])
+        if int4:
+            any4.gemm_int4(x[:M], p, a, b, c.g, out=ys[M])
+        else:
+            any4.gemm(x[:M], p, l, a, b, c.g, out=ys[M])
 
     out = {"N": c.N, "K": c.K, "g": c.g, "rotating_weight_sets": R}
     for M in MS:
@@ -301,6 +307,10 @@ def main() -> int:
         del g_all, g_m, sets
         torch.cuda.empty_cache()
         out["other_layers"] = {"config3": other_layer(torch, any4, workloads, 3, min(K, 100))}
+        # the same layers as plain int4 (no table lookup): the cost of the table
+        out["int4_no_table"] = {f"config{c}": other_layer(torch, any4, workloads, c,
+                                                          min(K, 100), int4=True)
+                                for c in (2, 3)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -33,7 +33,7 @@ _STATUS_NAMES = {0: "ANY4_OK", 1: "ANY4_E_NULL", 2: "ANY4_E_SHAPE", 3: "ANY4_E_A
 
 # every symbol include/any4.h declares
 EXPORTS = ("any4_packed_bytes", "any4_pack", "any4_dequant", "any4_gemm_workspace_size",
-           "any4_gemm", "any4_status_string")
+           "any4_gemm", "any4_gemm_int4", "any4_status_string")
 
 _lib = None
 
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.any4_gemm_workspace_size.argtypes = [I64, I64, I64, I64]
         L.any4_gemm.restype = ctypes.c_int
         L.any4_gemm.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P, SZ, P]
+        L.any4_gemm_int4.restype = ctypes.c_int
+        L.any4_gemm_int4.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
         L.any4_status_string.restype = ctypes.c_char_p
         L.any4_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -136,6 +138,12 @@ def gemm_raw(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
              ws_ptr=None, ws_bytes=0, stream=None) -> int:
     return lib().any4_gemm(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
                            ws_ptr, ws_bytes, _stream(stream))
+
+
+def gemm_int4_raw(x_ptr, packed_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
+                  stream=None) -> int:
+    return lib().any4_gemm_int4(x_ptr, packed_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
+                                _stream(stream))
 
 
 # --------------------------------------------------------------------------
@@ -228,4 +236,24 @@ def gemm(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: torch.
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     check(gemm_raw(_ptr(x), _ptr(packed), _ptr(lut), _ptr(alpha), _ptr(beta), _ptr(out), M, N, K,
                    g, ws_ptr, ws_bytes, sh))
+    return out
+
+
+def gemm_int4(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+              g: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y [M, N] = x [M, K] * W^T with plain int4 weights w = alpha * q + beta
+    (q the 4-bit code, 0..15; N from alpha)."""
+    _b16(x, "x"), _b16(alpha, "alpha"), _b16(beta, "beta")
+    M, K = x.shape
+    if g <= 0 or K % g or alpha.dim() != 2 or alpha.shape[1] != K // g or beta.shape != alpha.shape:
+        raise ValueError("alpha/beta must be [N, K/g]")
+    N = alpha.shape[0]
+    _check_packed(packed, N, K)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _b16(out, "y")
+    if out.shape != (M, N):
+        raise ValueError("y must be [M, N]")
+    check(gemm_int4_raw(_ptr(x), _ptr(packed), _ptr(alpha), _ptr(beta), _ptr(out), M, N, K, g,
+                        stream))
     return out

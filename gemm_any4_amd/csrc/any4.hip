@@ -428,13 +428,35 @@ __device__ __forceinline__ uint32_t deq_pair(uint32_t d, float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(w, bf2_t));
 }
 
+// int4 (no table): the four bytes of a packed dword give the B-operand
+// dwords bf16(a*lo + b) | bf16(a*hi + b) << 16, lo/hi the byte's nibbles
+__device__ __forceinline__ u32x4_t deq_int4(uint32_t d, float a, float b)
+{
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+    // The masks go through asm so that the byte conversions below stay single
+    // v_cvt_f32_ubyte<jb> instructions: with the mask visible, the compiler
+    // folds each into a bit-field extract plus a conversion.
+    uint32_t lo, hi;
+    asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(d));
+    asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(d >> 4));
+    u32x4_t r;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+        const f2_t w = {fmaf(a, static_cast<float>((lo >> (8 * jb)) & 0xFFu), b),
+                        fmaf(a, static_cast<float>((hi >> (8 * jb)) & 0xFFu), b)};
+        r[jb] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, bf2_t));
+    }
+    return r;
+}
+
 __device__ __forceinline__ u32x4_t deq_quad(const u32x4_t& q, float a, float b)
 {
     return u32x4_t{deq_pair(q[0], a, b), deq_pair(q[1], a, b), deq_pair(q[2], a, b),
                    deq_pair(q[3], a, b)};
 }
 
-template <int MT, int NBG>
+template <int MT, int NBG, bool I4>
 __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
 {
     using Cfg = KmCfg<NBG>;
@@ -480,7 +502,10 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
         const int blk = gi * NBG + wave;
         const bool live = wave < NBG && blk < nblk;
         const uint32_t b = static_cast<uint32_t>(r + blk * Gs);
-        lq = load16(rl, off2(lut_lane, live ? b * 512 : OOR));
+        if constexpr (!I4)
+            lq = load16(rl, off2(lut_lane, live ? b * 512 : OOR));
+        else
+            lq = u32x4_t{0u, 0u, 0u, 0u};
         const uint32_t ao = off2(ab_lane, live ? b * (G * 32) : OOR);
         aq = load16(ra, ao);
         bq = load16(rb, ao);
@@ -489,10 +514,14 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
         // table rows as f16, scaled by 2^-s (s per row: the largest finite
         // magnitude lands in [2^14, 2^15)), so every value within 2^31 of the
         // row's largest is exact; the decode multiplies alpha by 2^s
-        const int sc = lut_scale(lq);   // all lanes: pairs of lanes share a row
-        const u32x4_t lh = lut_to_f16(lq, sc);
+        int sc = 0;
+        u32x4_t lh = lq;
+        if constexpr (!I4) {
+            sc = lut_scale(lq);   // all lanes: pairs of lanes share a row
+            lh = lut_to_f16(lq, sc);
+        }
         if (wave < NBG) {
-            if (lane < 32) {
+            if (!I4 && lane < 32) {
                 lds_at<u32x4_t>(smem, Cfg::LUTS + wave * 512 + lane * 16) = lh;
                 if ((lane & 1) == 0)
                     lds_at<int>(smem, Cfg::SCL + (wave * 16 + (lane >> 1)) * 4) = sc;
@@ -502,7 +531,8 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
         }
     };
     auto build = [&](int bb) {
-        build_table<GW>(smem, Cfg::LUTS + bb * 512, (bb >> 1) * 16384 + (bb & 1) * 32, tid);
+        if constexpr (!I4)
+            build_table<GW>(smem, Cfg::LUTS + bb * 512, (bb >> 1) * 16384 + (bb & 1) * 32, tid);
     };
 
     // ---- ring: tile v of group gi is chunk cbase + v / NBG of block
@@ -594,7 +624,7 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
     auto load_scales = [&]() {
 #pragma unroll
         for (int bb = 0; bb < NBG; ++bb)
-            rsc[bb] = lds_at<int>(smem, Cfg::SCL + (bb * 16 + j) * 4);
+            rsc[bb] = I4 ? 0 : lds_at<int>(smem, Cfg::SCL + (bb * 16 + j) * 4);
     };
     load_scales();
     f32x4_t* red = reinterpret_cast<f32x4_t*>(smem);
@@ -646,13 +676,18 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
                 const int bb = u % NBG;
                 const u32x4_t p = pb[u % D];
 #pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4)
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    if constexpr (I4) {
+                        bw[h][s4] = u32x4_t{p[s4], 0u, 0u, 0u};   // decoded later
+                    } else {
 #pragma unroll
-                    for (int jb = 0; jb < 4; ++jb)
-                        bw[h][s4][jb] = lds_at<uint32_t>(
-                            smem, __builtin_amdgcn_perm(p[s4], s1[bb >> 1],
-                                                        0x0C020000u | ((4u + jb) << 8)) +
-                                      (bb & 1) * 128);
+                        for (int jb = 0; jb < 4; ++jb)
+                            bw[h][s4][jb] = lds_at<uint32_t>(
+                                smem, __builtin_amdgcn_perm(p[s4], s1[bb >> 1],
+                                                            0x0C020000u | ((4u + jb) << 8)) +
+                                          (bb & 1) * 128);
+                    }
+                }
                 pr[h] = lds_at<uint32_t>(smem, ab_c[s] + bb * Cfg::AB_BLK);
             }
         };
@@ -698,7 +733,7 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
                 const float bt = bf16_to_f32(pr >> 16);
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4)
-                    bw[h][s4] = deq_quad(bw[h][s4], a, bt);
+                    bw[h][s4] = I4 ? deq_int4(bw[h][s4][0], a, bt) : deq_quad(bw[h][s4], a, bt);
             }
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4)
@@ -767,7 +802,7 @@ struct KbCfg {
     static_assert(LDS <= 160 * 1024, "LDS of one CU");
 };
 
-template <int MT, int NBG, bool XL>
+template <int MT, int NBG, bool XL, bool I4>
 __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
 {
     using Cfg = KbCfg<NBG, XL>;
@@ -824,7 +859,10 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
             const bool live = tid < 32 * NBG && blk < nblk;
             const uint32_t o = (static_cast<uint32_t>(r + blk * Gs) * 512 + (tid & 31) * 16) |
                                (static_cast<uint32_t>(!live) << 31);
-            lq = load16(rl, o);
+            if constexpr (!I4)
+                lq = load16(rl, o);
+            else
+                lq = u32x4_t{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -838,9 +876,13 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
         }
     };
     auto stage_store = [&](const u32x4_t& lq, const u32x4_t (&aq)[2], const u32x4_t (&bq)[2]) {
-        const int sc = lut_scale(lq);   // all lanes: pairs of lanes share a row
-        const u32x4_t lh = lut_to_f16(lq, sc);
-        if (tid < 32 * NBG) {
+        int sc = 0;
+        u32x4_t lh = lq;
+        if constexpr (!I4) {
+            sc = lut_scale(lq);   // all lanes: pairs of lanes share a row
+            lh = lut_to_f16(lq, sc);
+        }
+        if (!I4 && tid < 32 * NBG) {
             lds_at<u32x4_t>(smem, Cfg::LUTS + tid * 16) = lh;
             if ((tid & 1) == 0)
                 lds_at<int>(smem, Cfg::SCL + (tid >> 1) * 4) = sc;
@@ -851,7 +893,8 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
                 store_pairs(smem, Cfg::AB + ab_blk[h] * Cfg::AB_BLK, ab_pc[h], G, aq[h], bq[h]);
     };
     auto build = [&](int bb) {
-        build_table<GW>(smem, Cfg::LUTS + bb * 512, (bb >> 1) * 16384 + (bb & 1) * 32, tid);
+        if constexpr (!I4)
+            build_table<GW>(smem, Cfg::LUTS + bb * 512, (bb >> 1) * 16384 + (bb & 1) * 32, tid);
     };
 
     // ---- ring.  Tile u of a body whose first step is (group gc, padded step
@@ -936,7 +979,7 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
     auto load_scales = [&]() {
 #pragma unroll
         for (int bb = 0; bb < NBG; ++bb)
-            rsc[bb] = lds_at<int>(smem, Cfg::SCL + (bb * 16 + j) * 4);
+            rsc[bb] = I4 ? 0 : lds_at<int>(smem, Cfg::SCL + (bb * 16 + j) * 4);
     };
     load_scales();
     f32x4_t* red = reinterpret_cast<f32x4_t*>(smem);
@@ -997,14 +1040,16 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
                 const int st = sc + u / NBG;
                 const int bb = u % NBG;
                 const u32x4_t p = pb[u];
+                if constexpr (!I4) {
 #pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4)
+                    for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-                    for (int jb = 0; jb < 4; ++jb)
-                        bw[h][s4][jb] = lds_at<uint32_t>(
-                            smem, __builtin_amdgcn_perm(p[s4], s1[bb >> 1],
-                                                        0x0C020000u | ((4u + jb) << 8)) +
-                                      (bb & 1) * 128);
+                        for (int jb = 0; jb < 4; ++jb)
+                            bw[h][s4][jb] = lds_at<uint32_t>(
+                                smem, __builtin_amdgcn_perm(p[s4], s1[bb >> 1],
+                                                            0x0C020000u | ((4u + jb) << 8)) +
+                                          (bb & 1) * 128);
+                }
                 const int c = cbase + st;
                 const bool live = gc * NBG + bb < nblk && st < C && c < Kc;
                 const int grp =
@@ -1016,7 +1061,7 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
                 const float bt = bf16_to_f32(pr >> 16);
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4)
-                    bw[h][s4] = deq_quad(bw[h][s4], a, bt);
+                    bw[h][s4] = I4 ? deq_int4(p[s4], a, bt) : deq_quad(bw[h][s4], a, bt);
                 if constexpr (XL) {
                     // the chunk's x in the operand layout; lanes of rows m >= M
                     // read row M-1 (those MFMA rows are never stored), so no
@@ -1085,7 +1130,7 @@ any4_status launched()
 
 constexpr int KM_GRID = 256;   // one workgroup per CU of an MI355X
 
-template <int MT>
+template <int MT, bool I4>
 void launch_gemm(const GemmArgs& a, hipStream_t stream)
 {
     const int64_t NB = row_blocks(a.N);
@@ -1098,13 +1143,13 @@ void launch_gemm(const GemmArgs& a, hipStream_t stream)
     const dim3 gd(static_cast<unsigned>(grid));
     if (a.K <= KM_MAX_K) {
         if (nbg == 1)
-            hipLaunchKernelGGL((k_gemm_km<MT, 1>), gd, dim3(GT), 0, stream, a);
+            hipLaunchKernelGGL((k_gemm_km<MT, 1, I4>), gd, dim3(GT), 0, stream, a);
         else if (nbg == 2)
-            hipLaunchKernelGGL((k_gemm_km<MT, 2>), gd, dim3(GT), 0, stream, a);
+            hipLaunchKernelGGL((k_gemm_km<MT, 2, I4>), gd, dim3(GT), 0, stream, a);
         else if (nbg == 3)
-            hipLaunchKernelGGL((k_gemm_km<MT, 3>), gd, dim3(GT), 0, stream, a);
+            hipLaunchKernelGGL((k_gemm_km<MT, 3, I4>), gd, dim3(GT), 0, stream, a);
         else
-            hipLaunchKernelGGL((k_gemm_km<MT, 4>), gd, dim3(GT), 0, stream, a);
+            hipLaunchKernelGGL((k_gemm_km<MT, 4, I4>), gd, dim3(GT), 0, stream, a);
         return;
     }
     // alpha/beta of a group must fit the LDS staging of k_gemm_kb
@@ -1118,23 +1163,87 @@ void launch_gemm(const GemmArgs& a, hipStream_t stream)
     if (xl) {
         if constexpr (MT <= 2) {
             if (nbg == 1)
-                hipLaunchKernelGGL((k_gemm_kb<MT, 1, true>), gd, dim3(GT), 0, stream, a);
+                hipLaunchKernelGGL((k_gemm_kb<MT, 1, true, I4>), gd, dim3(GT), 0, stream, a);
             else
-                hipLaunchKernelGGL((k_gemm_kb<MT, 2, true>), gd, dim3(GT), 0, stream, a);
+                hipLaunchKernelGGL((k_gemm_kb<MT, 2, true, I4>), gd, dim3(GT), 0, stream, a);
         }
         return;
     }
     if (nbg == 1)
-        hipLaunchKernelGGL((k_gemm_kb<MT, 1, false>), gd, dim3(GT), 0, stream, a);
+        hipLaunchKernelGGL((k_gemm_kb<MT, 1, false, I4>), gd, dim3(GT), 0, stream, a);
     else if (nbg == 2)
-        hipLaunchKernelGGL((k_gemm_kb<MT, 2, false>), gd, dim3(GT), 0, stream, a);
+        hipLaunchKernelGGL((k_gemm_kb<MT, 2, false, I4>), gd, dim3(GT), 0, stream, a);
     else if (nbg == 3)
-        hipLaunchKernelGGL((k_gemm_kb<MT, 3, false>), gd, dim3(GT), 0, stream, a);
+        hipLaunchKernelGGL((k_gemm_kb<MT, 3, false, I4>), gd, dim3(GT), 0, stream, a);
     else
-        hipLaunchKernelGGL((k_gemm_kb<MT, 4, false>), gd, dim3(GT), 0, stream, a);
+        hipLaunchKernelGGL((k_gemm_kb<MT, 4, false, I4>), gd, dim3(GT), 0, stream, a);
 }
 
 }  // namespace
+
+// Argument checks and dispatch shared by any4_gemm (table lookup) and
+// any4_gemm_int4 (the 4-bit code itself is the value; lut unused).
+static any4_status gemm_call(bool i4, const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
+                      const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
+                      int64_t N, int64_t K, int64_t g, hipStream_t stream)
+{
+    if (M < 0 || M > 16 || N < 0 || !group_ok(K, g) || K / (g > 0 ? g : 1) > MAX_G)
+        return ANY4_E_SHAPE;
+    if (any4_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31) ||
+        static_cast<size_t>(M) * K * 2 >= (static_cast<size_t>(1) << 31) ||
+        static_cast<size_t>(N) * 32 >= (static_cast<size_t>(1) << 31))
+        return ANY4_E_SHAPE;
+    if (M == 0 || N == 0)
+        return ANY4_OK;
+    if (!y || (K > 0 && (!x || !packed || (!i4 && !lut) || !alpha || !beta)))
+        return ANY4_E_NULL;
+    if (!aligned(y, 2) || (K > 0 && (!aligned(x, 16) || !aligned(packed, 16) ||
+                                     (!i4 && !aligned(lut, 16)) || !aligned(alpha, 16) ||
+                                     !aligned(beta, 16))))
+        return ANY4_E_ALIGN;
+    (void)hipGetLastError();
+    if (K == 0) {
+        const size_t n = static_cast<size_t>(M) * N;
+        hipLaunchKernelGGL(k_zero, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                           stream, y, n);
+        return launched();
+    }
+    GemmArgs a;
+    a.x = x;
+    a.packed = packed;
+    a.lut = lut;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.y = y;
+    a.M = static_cast<int>(M);
+    a.N = static_cast<int>(N);
+    a.K = static_cast<int>(K);
+    a.g = static_cast<int>(g);
+    if (i4) {
+        if (M == 1)
+            launch_gemm<1, true>(a, stream);
+        else if (M == 2)
+            launch_gemm<2, true>(a, stream);
+        else if (M <= 4)
+            launch_gemm<4, true>(a, stream);
+        else if (M <= 8)
+            launch_gemm<8, true>(a, stream);
+        else
+            launch_gemm<16, true>(a, stream);
+    } else {
+        if (M == 1)
+            launch_gemm<1, false>(a, stream);
+        else if (M == 2)
+            launch_gemm<2, false>(a, stream);
+        else if (M <= 4)
+            launch_gemm<4, false>(a, stream);
+        else if (M <= 8)
+            launch_gemm<8, false>(a, stream);
+        else
+            launch_gemm<16, false>(a, stream);
+    }
+    return launched();
+}
 
 // ---------------------------------------------------------------------------
 // C ABI
@@ -1225,49 +1334,14 @@ any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* 
 {
     (void)workspace;
     (void)workspace_bytes;
-    if (M < 0 || M > 16 || N < 0 || !group_ok(K, g) || K / (g > 0 ? g : 1) > MAX_G)
-        return ANY4_E_SHAPE;
-    if (any4_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31) ||
-        static_cast<size_t>(M) * K * 2 >= (static_cast<size_t>(1) << 31) ||
-        static_cast<size_t>(N) * 32 >= (static_cast<size_t>(1) << 31))
-        return ANY4_E_SHAPE;
-    if (M == 0 || N == 0)
-        return ANY4_OK;
-    if (!y || (K > 0 && (!x || !packed || !lut || !alpha || !beta)))
-        return ANY4_E_NULL;
-    if (!aligned(y, 2) || (K > 0 && (!aligned(x, 16) || !aligned(packed, 16) ||
-                                     !aligned(lut, 16) || !aligned(alpha, 16) ||
-                                     !aligned(beta, 16))))
-        return ANY4_E_ALIGN;
-    (void)hipGetLastError();
-    if (K == 0) {
-        const size_t n = static_cast<size_t>(M) * N;
-        hipLaunchKernelGGL(k_zero, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
-                           stream, y, n);
-        return launched();
-    }
-    GemmArgs a;
-    a.x = x;
-    a.packed = packed;
-    a.lut = lut;
-    a.alpha = alpha;
-    a.beta = beta;
-    a.y = y;
-    a.M = static_cast<int>(M);
-    a.N = static_cast<int>(N);
-    a.K = static_cast<int>(K);
-    a.g = static_cast<int>(g);
-    if (M == 1)
-        launch_gemm<1>(a, stream);
-    else if (M == 2)
-        launch_gemm<2>(a, stream);
-    else if (M <= 4)
-        launch_gemm<4>(a, stream);
-    else if (M <= 8)
-        launch_gemm<8>(a, stream);
-    else
-        launch_gemm<16>(a, stream);
-    return launched();
+    return gemm_call(false, x, packed, lut, alpha, beta, y, M, N, K, g, stream);
+}
+
+any4_status any4_gemm_int4(const uint16_t* x, const uint8_t* packed, const uint16_t* alpha,
+                           const uint16_t* beta, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                           int64_t g, hipStream_t stream)
+{
+    return gemm_call(true, x, packed, nullptr, alpha, beta, y, M, N, K, g, stream);
 }
 
 }  // extern "C"

@@ -64,7 +64,7 @@ typedef enum any4_status {
     ANY4_OK = 0,
     ANY4_E_NULL = 1,      /* a required pointer is NULL                               */
     ANY4_E_SHAPE = 2,     /* a size is negative, K is not a multiple of 128, g is not a
-                             positive multiple of 128, K % g != 0, M > 16 (any4_gemm),
+                             positive multiple of 128, K % g != 0, M > 16 or K/g > 512 (any4_gemm*),
                              or a buffer would be 2 GiB or larger                     */
     ANY4_E_ALIGN = 3,     /* a base pointer misses the alignment stated above          */
     ANY4_E_WORKSPACE = 4, /* workspace smaller than any4_gemm_workspace_size()         */
@@ -117,20 +117,19 @@ size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
 /*
  * any4_gemm -- y = x * W^T with W the any4 weights above, for M = 1..16
  * (the explainer's section 三: decode batches of 1..16):
- *     y[m][n] = bf16_rne( sum_k x[m][k] * (alpha[n][k/g] * lut[n][idx[n][k]] + beta[n][k/g]) )
- * The weights are never written out: each 128-k chunk contributes
- * alpha * sum_k x*lut[idx] + beta * sum_k x (alpha, beta of the chunk's
- * group), accumulated in fp32.  The result
- * is within
+ *     y[m][n] = bf16_rne( sum_k x[m][k] * w[n][k] )
+ * with w[n][k] exactly the any4_dequant value (every weight is dequantised to
+ * that bf16 inside the kernel; the weights are never written to memory).  The
+ * products and the sum are fp32 (matrix-core accumulation), so the result is
+ * within
  *     |y - y_ref| <= 2e-3 * sum_k |x[m][k] * w[n][k]| + 1e-3
- * of the fp64 product with the bf16 dequantised weights for the workloads this
- * library is tested on.  Runs are deterministic (same inputs, same bits): the
- * summation order depends only on the shape.
+ * of the fp64 product with those bf16 weights.  Runs are deterministic (same
+ * inputs, same bits): the summation order depends only on the shape.
  *   x                         device, [M][K] bf16, read-only.
  *   packed, lut, alpha, beta  device, read-only.
  *   y                         device, [M][N] bf16, written.
- *   M in 0..16, N >= 0, K >= 0 with K % g == 0.  M*N == 0 is a no-op;
- *   K == 0 writes y = 0 (x, packed, lut, alpha and beta may then be NULL).
+ *   M in 0..16, N >= 0, K >= 0 with K % g == 0 and K/g <= 512.  M*N == 0 is a
+ *   no-op; K == 0 writes y = 0 (x, packed, lut, alpha and beta may then be NULL).
  *   workspace, workspace_bytes  device scratch of at least
  *       any4_gemm_workspace_size(M, N, K, g) bytes; NULL and 0 when that is 0,
  *       which it is for every shape today.
@@ -140,6 +139,21 @@ any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* 
                       const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
                       int64_t N, int64_t K, int64_t g, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/*
+ * any4_gemm_int4 -- the same product for plain asymmetric int4 weights, the
+ * baseline the explainer compares any4 against (section 二: int4 is the fixed
+ * table 0..15, with the group scale and offset of step 1):
+ *     w[n][k] = bf16_rne( fp32( alpha[n][k/g] * q[n][k] + beta[n][k/g] ) )
+ *     y[m][n] = bf16_rne( sum_k x[m][k] * w[n][k] )
+ * q[n][k] is the 4-bit code in `packed` (same tile layout), read as 0..15.
+ * The result is bit-identical to any4_gemm with every table row 0, 1, .., 15,
+ * and carries the same error bound.  Arguments, sizes, alignment and errors as
+ * any4_gemm, without lut and without the (always empty) workspace.
+ */
+any4_status any4_gemm_int4(const uint16_t* x, const uint8_t* packed, const uint16_t* alpha,
+                           const uint16_t* beta, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                           int64_t g, hipStream_t stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char* any4_status_string(any4_status s);

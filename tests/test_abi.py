@@ -15,7 +15,7 @@ def _declared_functions():
     with open(os.path.join(ROOT, "include", "any4.h")) as f:
         src = f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(any4_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(any4_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_binding_exports():
@@ -99,3 +99,17 @@ def test_workspace_size_is_defined_for_all_shapes():
     for M in (1, 2, 4, 8, 16):
         assert any4.workspace_size(M, 14336, 4096, 128) >= 0
     assert any4.workspace_size(17, 16, 128, 128) == 0
+
+
+def test_gemm_int4_errors():
+    # same checks as any4_gemm, without the table
+    assert any4.gemm_int4_raw(A, A, A, A, A, 17, 16, 128, 128, stream=0) == 2
+    assert any4.gemm_int4_raw(A, A, A, A, A, 1, 16, 384, 256, stream=0) == 2
+    assert any4.gemm_int4_raw(A, A, A, A, A, 1, 16, 128 * 513, 128, stream=0) == 2
+    assert any4.gemm_int4_raw(None, A, A, A, A, 1, 16, 128, 128, stream=0) == 1
+    assert any4.gemm_int4_raw(A, None, A, A, A, 1, 16, 128, 128, stream=0) == 1
+    assert any4.gemm_int4_raw(A, A, None, A, A, 1, 16, 128, 128, stream=0) == 1
+    assert any4.gemm_int4_raw(A, A, A, A, None, 1, 16, 128, 128, stream=0) == 1
+    assert any4.gemm_int4_raw(A + 2, A, A, A, A, 1, 16, 128, 128, stream=0) == 3
+    assert any4.gemm_int4_raw(A, A, A + 2, A, A, 1, 16, 128, 128, stream=0) == 3
+    assert any4.gemm_int4_raw(None, None, None, None, None, 0, 16, 128, 128, stream=0) == 0

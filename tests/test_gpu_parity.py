@@ -6,6 +6,8 @@
     oracle's fp64 product, for configs 0-3 at every batch size (all outputs)
     and config 4 (70B decoder-layer shapes from the oracle's k-means) on
     sampled rows;
+  * plain int4 (no table): bitwise equal to the table path with every row
+    0..15 and within the bound of the oracle;
   * invariants on the device: identity table returns the indices, one-hot x
     returns a column of the dequantised W bit-exactly, permuting the table
     with its indices leaves y bit-identical, x = 0 gives 0, runs are
@@ -178,6 +180,57 @@ def test_gemm_large_k(M, N, K, g):
     y = any4.gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g)
     torch.cuda.synchronize()
     gu.assert_within_bound(y, y_ref, ad, f"large K {M}x{N}x{K} g{g}")
+
+
+# --------------------------------------------------------------------------
+# plain int4 (no table): w = alpha * q + beta
+# --------------------------------------------------------------------------
+def _identity_table(N):
+    return np.tile(workloads.to_bf16_bits(np.arange(16.0)), (N, 1))
+
+
+# Full-size layers (14336x4096 and 4096x14336, the k-major kernels for K <= 4096
+# and for larger K), ragged shapes and large K.
+@pytest.mark.parametrize("M,N,K,g,cfg", [(1, 0, 0, 0, 2), (16, 0, 0, 0, 2), (1, 0, 0, 0, 3),
+                                         (16, 0, 0, 0, 3), (3, 16 * 700 + 5, 256, 128, None),
+                                         (1, 17, 128, 128, None), (16, 15, 128, 128, None),
+                                         (1, 16 * 2000 + 3, 128, 128, None),
+                                         (2, 16 * 300 + 7, 8192, 128, None),
+                                         (5, 100, 14336, 1024, None), (16, 33, 65536, 128, None)])
+def test_gemm_int4(M, N, K, g, cfg):
+    """any4_gemm_int4 is bitwise any4_gemm with every table row 0..15, and both
+    are within the bound of the oracle's product with the int4 weights."""
+    if cfg is not None:
+        inp = gu.config_layer(cfg).inp
+        x = gu.config_layer(cfg).x[:M]
+        x_host = inp.x[:M]
+    else:
+        inp = workloads.generic(M * 11 + N + K, M, N, K, g)
+        x, x_host = gu.dev_b16(inp.x), inp.x
+    lut = _identity_table(inp.N)
+    L = gu.Layer(workloads.Any4Inputs(inp.N, inp.K, inp.g, inp.idx, lut, inp.alpha, inp.beta,
+                                      x_host))
+    y4 = any4.gemm_int4(x, L.packed, L.alpha, L.beta, inp.g)
+    y = any4.gemm(x, L.packed, L.lut, L.alpha, L.beta, inp.g)
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.host_b16(y4), gu.host_b16(y))
+    w_int4 = L.w_ref()     # the oracle's dequant with the identity table is int4
+    rows = np.arange(inp.N)
+    if inp.N * inp.K > 1 << 24:   # full-size layers: sampled rows
+        rng = np.random.default_rng(M)
+        rows = np.unique(np.concatenate([[0, inp.N - 1], rng.choice(inp.N, 300, replace=False)]))
+    y_ref, ad = oracle.gemm(x_host, w_int4[rows], nthreads=oracle.default_threads())
+    gu.assert_within_bound(y4[:, torch.from_numpy(rows).to(gu.DEV)], y_ref, ad,
+                           f"int4 {M}x{inp.N}x{inp.K} g{inp.g}")
+
+
+def test_gemm_int4_empty_and_k0():
+    x = torch.zeros((3, 0), dtype=torch.bfloat16, device=gu.DEV)
+    e = torch.zeros((40, 0), dtype=torch.bfloat16, device=gu.DEV)
+    y = torch.full((3, 40), 7.0, dtype=torch.bfloat16, device=gu.DEV)
+    any4.gemm_int4(x, torch.zeros((0,), dtype=torch.uint8, device=gu.DEV), e, e, 128, out=y)
+    torch.cuda.synchronize()
+    assert (y == 0).all()
 
 
 # --------------------------------------------------------------------------
