@@ -21,7 +21,9 @@ The same graph timing is also reported, outside `value`, for the other
 layer shape, the MLP down projection N=4096, K=14336, g=1024, at M=1 and
 M=16, under "other_layers"; and for both layers with plain int4 weights
 (any4_gemm_int4 on the same codes, scales and offsets, no table), under
-"int4_no_table", which puts a number on what the table lookup costs.
+"int4_no_table", which puts a number on what the table lookup costs; and
+at prefill batches M = 64, 256, 1024 on the up/gate layer (TFLOP/s against
+the bf16 matrix peak), under "prefill".
 
 Prints one JSON line.  --traffic-probe instead runs a few launches of each M
 plus a device copy of known size, for hardware-counter collection.
@@ -43,6 +45,7 @@ if ROOT not in sys.path:
 METRIC = ("any4_gemm µs + achieved HBM TB/s (% of peak), M=1 and M=16, "
           "N×K=14336×4096")
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 CACHE_BYTES = 256 * 1024 ** 2   # MI355X last-level cache (MALL)
 N_, K_, G_ = 14336, 4096, 128
 MS = (1, 16)
@@ -161,6 +164,38 @@ def other_layer(torch, any4, workloads, cfg: int, steps: int, int4: bool = False
         out[str(M)] = {"us_per_launch": us, "bytes": bts,
                        "tbps": bts / (us * 1e-6) / 1e12,
                        "pct_hbm_peak": 100.0 * bts / (us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+        del g
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
+def prefill(torch, any4, workloads, Ms) -> dict:
+    """µs and TFLOP/s of any4_gemm at prefill batches M > 16 on the up/gate
+    layer (the tiled MFMA kernel), graph-timed over rotating weight sets."""
+    import numpy as np
+
+    c = workloads.CONFIGS[2]
+    dev, R, sets, x, ys = _setup(torch, any4, workloads, 0, 2)
+    out = {"N": c.N, "K": c.K, "g": c.g, "peak_tflops_bf16": MFMA_BF16_PEAK_TFLOPS}
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    for M in Ms:
+        xb = torch.randn(M, c.K, generator=gen).to(torch.bfloat16).to(dev)
+        yb = torch.empty(M, c.N, device=dev, dtype=torch.bfloat16)
+
+        def launch(i: int, M: int):
+            p, l, a, b = sets[i % R]
+            any4.gemm(xb, p, l, a, b, c.g, out=yb)
+
+        for i in range(3):
+            launch(i, M)
+        steps = 20
+        g = _graph(torch, launch, steps, (M,))
+        _time_graph(torch, g)
+        us = float(np.median([_time_graph(torch, g) * 1e3 / steps for _ in range(3)]))
+        tf = 2.0 * M * c.N * c.K / (us * 1e-6) / 1e12
+        out[str(M)] = {"us_per_launch": us, "tflops": tf,
+                       "pct_mfma_peak": 100.0 * tf / MFMA_BF16_PEAK_TFLOPS}
         del g
     del sets
     torch.cuda.empty_cache()
@@ -311,6 +346,8 @@ def main() -> int:
         out["int4_no_table"] = {f"config{c}": other_layer(torch, any4, workloads, c,
                                                           min(K, 100), int4=True)
                                 for c in (2, 3)}
+    if not args.no_other_layers:
+        out["prefill"] = prefill(torch, any4, workloads, (64, 256, 1024))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)

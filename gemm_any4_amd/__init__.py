@@ -12,7 +12,7 @@ Tensors
   lut     bf16   [N, 16]    per-row table
   alpha   bf16   [N, K/g]   per-group scale
   beta    bf16   [N, K/g]   per-group offset
-  x       bf16   [M, K]     M = 1..16
+  x       bf16   [M, K]     M = 1..16 (decode); larger M also accepted
   y       bf16   [M, N]
   w       bf16   [N, K]
 (bf16 tensors may also be given as int16/uint16 bit patterns.)

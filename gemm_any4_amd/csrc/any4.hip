@@ -1105,6 +1105,158 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
     }
 }
 
+// ---- k_gemm_big: M > 16, a plain LDS-tiled MFMA GEMM over dequantised tiles --
+//
+// (Plain int4, any4_gemm_int4: no table pointer, the codes 0..15 are the values.)
+// For batches past the decode sizes the product is compute-bound and each
+// weight tile is used by many x rows, so the weights are dequantised once per
+// workgroup into LDS and consumed from there.  A workgroup of 4 waves computes
+// a BM x 64 block of y (BM rows of x, 64 rows of W = 4 row blocks): per chunk of
+// 128 k, thread t dequantises its 16-byte slot of row block t / 64 (the slot
+// of lane t % 64: row t % 16, k 32 * ((t % 64) / 16) .. + 31) exactly as
+// any4_dequant does, into W's LDS tile, the threads copy x's BM x 128 tile
+// (rows >= M read as zero), and after a barrier each wave multiplies its
+// (BM/2) x 32 part with 16x16x32 bf16 MFMAs.
+//
+// LDS: XS [BM][128 + 8] bf16, WS [64][128 + 8] bf16 (rows padded by 16 B so
+// that the 16 rows of an operand read fall in different banks), LT [64][16]
+// fp32 (the table rows of the workgroup's 64 weight rows).
+constexpr int BIG_BN = 64;
+constexpr int BIG_LD = TILE_K + 8;   // padded row length in bf16
+
+template <int BM>
+__global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
+{
+    constexpr int MTW = BM / 32;   // 16-row m tiles per wave (the wave's BM/2 rows)
+    __shared__ __attribute__((aligned(16))) uint16_t xs[BM * BIG_LD];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[BIG_BN * BIG_LD];
+    __shared__ float lt[BIG_BN * 16];
+
+    const int M = args.M, N = args.N, K = args.K, g = args.g;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int Kc = K / TILE_K;
+    const int G = K / g;
+    const int n0 = blockIdx.x * BIG_BN;
+    const int m0 = blockIdx.y * BM;
+
+    // table rows of the 64 weight rows (rows >= N: zeros); no table (plain
+    // int4): the codes themselves, 0..15
+    for (int e = tid; e < BIG_BN * 16; e += 256) {
+        const int n = n0 + e / 16;
+        lt[e] = n >= N      ? 0.f
+                : args.lut ? bf16_to_f32(args.lut[static_cast<size_t>(n) * 16 + (e & 15)])
+                           : static_cast<float>(e & 15);
+    }
+
+    // this thread's dequantisation slot
+    const int tb = tid >> 6;                 // row block within the workgroup
+    const int wrow = tb * 16 + (lane & 15);  // row within the 64
+    const int wn = n0 + wrow;
+    const int wk = (lane >> 4) * 32;         // k offset within the chunk
+    const int blk = (n0 >> 4) + tb;          // global row block
+    const bool wlive = wn < N;
+
+    f32x4_t acc[MTW][2];
+#pragma unroll
+    for (int a = 0; a < MTW; ++a)
+        acc[a][0] = acc[a][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int wm = (wave >> 1) * (BM / 2);   // the wave's rows within BM
+    const int wc = (wave & 1) * 32;          // ... and columns within the 64
+    const int j = lane & 15;
+    const int kq = lane >> 4;
+
+    // chunk c's global data, fetched one chunk ahead into registers: this
+    // thread's packed slot, its group's alpha and beta, and its x pieces
+    constexpr int XP = BM * 16 / 256;   // 16-byte x pieces per thread
+    u32x4_t pk = {0u, 0u, 0u, 0u};
+    uint32_t ab = 0;
+    u32x4_t xv[XP];
+    auto fetch = [&](int c) {
+        if (wlive) {
+            const int k0 = c * TILE_K + wk;
+            pk = *reinterpret_cast<const u32x4_t*>(
+                args.packed + (static_cast<size_t>(blk) * Kc + c) * TILE_BYTES + lane * 16);
+            ab = args.alpha[static_cast<size_t>(wn) * G + k0 / g] |
+                 (static_cast<uint32_t>(args.beta[static_cast<size_t>(wn) * G + k0 / g]) << 16);
+        }
+#pragma unroll
+        for (int i = 0; i < XP; ++i) {
+            const int piece = tid + i * 256;
+            const int m = m0 + (piece >> 4);
+            xv[i] = u32x4_t{0u, 0u, 0u, 0u};
+            if (m < M)
+                xv[i] = *reinterpret_cast<const u32x4_t*>(
+                    args.x + static_cast<size_t>(m) * K + c * TILE_K + (piece & 15) * 8);
+        }
+    };
+    fetch(0);
+    for (int c = 0; c < Kc; ++c) {
+        __syncthreads();   // the previous chunk's tiles are consumed (and lt is written)
+        // weights: 32 per thread, exactly the any4_dequant values
+        {
+            u32x4_t out[4] = {};
+            if (wlive) {
+                const float a = bf16_to_f32(ab & 0xFFFFu);
+                const float bt = bf16_to_f32(ab >> 16);
+                const float* L = lt + wrow * 16;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const uint32_t byte = (pk[q >> 2] >> (8 * (q & 3))) & 0xFFu;
+                    const float lo = fmaf(a, L[byte & 15u], bt);
+                    const float hi = fmaf(a, L[byte >> 4], bt);
+                    out[q >> 2][q & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+                }
+            }
+            u32x4_t* dst = reinterpret_cast<u32x4_t*>(ws + wrow * BIG_LD + wk);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                dst[q] = out[q];
+        }
+        // x: BM rows x 128 k
+#pragma unroll
+        for (int i = 0; i < XP; ++i) {
+            const int piece = tid + i * 256;
+            *reinterpret_cast<u32x4_t*>(xs + (piece >> 4) * BIG_LD + (piece & 15) * 8) = xv[i];
+        }
+        if (c + 1 < Kc)
+            fetch(c + 1);
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < TILE_K / 32; ++ks) {
+            const int k = ks * 32 + kq * 8;
+            u32x4_t bf[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+                bf[nt] = *reinterpret_cast<const u32x4_t*>(ws + (wc + nt * 16 + j) * BIG_LD + k);
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt) {
+                const u32x4_t af =
+                    *reinterpret_cast<const u32x4_t*>(xs + (wm + mt * 16 + j) * BIG_LD + k);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, af), __builtin_bit_cast(bf16x8_t, bf[nt]),
+                        acc[mt][nt], 0, 0, 0);
+            }
+        }
+    }
+    // lane l holds y[m = 4 * (l / 16) + v][n = l % 16] of each 16 x 16 tile
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = m0 + wm + mt * 16 + kq * 4 + v;
+                const int n = n0 + wc + nt * 16 + j;
+                if (m < M && n < N)
+                    args.y[static_cast<size_t>(m) * N + n] =
+                        static_cast<uint16_t>(f32_to_bf16(acc[mt][nt][v]));
+            }
+}
+
 // ---------------------------------------------------------------------------
 // host helpers
 // ---------------------------------------------------------------------------
@@ -1181,13 +1333,42 @@ void launch_gemm(const GemmArgs& a, hipStream_t stream)
 
 }  // namespace
 
+// M = 1..16: the streaming kernels, instantiated for 1, 2, 4, 8 and 16 rows
+static void launch_decode(const GemmArgs& a, bool i4, hipStream_t stream)
+{
+    if (i4) {
+        if (a.M == 1)
+            launch_gemm<1, true>(a, stream);
+        else if (a.M == 2)
+            launch_gemm<2, true>(a, stream);
+        else if (a.M <= 4)
+            launch_gemm<4, true>(a, stream);
+        else if (a.M <= 8)
+            launch_gemm<8, true>(a, stream);
+        else
+            launch_gemm<16, true>(a, stream);
+    } else {
+        if (a.M == 1)
+            launch_gemm<1, false>(a, stream);
+        else if (a.M == 2)
+            launch_gemm<2, false>(a, stream);
+        else if (a.M <= 4)
+            launch_gemm<4, false>(a, stream);
+        else if (a.M <= 8)
+            launch_gemm<8, false>(a, stream);
+        else
+            launch_gemm<16, false>(a, stream);
+    }
+}
+
 // Argument checks and dispatch shared by any4_gemm (table lookup) and
 // any4_gemm_int4 (the 4-bit code itself is the value; lut unused).
 static any4_status gemm_call(bool i4, const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
                       const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
                       int64_t N, int64_t K, int64_t g, hipStream_t stream)
 {
-    if (M < 0 || M > 16 || N < 0 || !group_ok(K, g) || K / (g > 0 ? g : 1) > MAX_G)
+    if (M < 0 || N < 0 || !group_ok(K, g) || K / (g > 0 ? g : 1) > MAX_G ||
+        (M > 16 && (M + 63) / 64 > 65535))
         return ANY4_E_SHAPE;
     if (any4_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31) ||
         static_cast<size_t>(M) * K * 2 >= (static_cast<size_t>(1) << 31) ||
@@ -1219,29 +1400,32 @@ static any4_status gemm_call(bool i4, const uint16_t* x, const uint8_t* packed, 
     a.N = static_cast<int>(N);
     a.K = static_cast<int>(K);
     a.g = static_cast<int>(g);
-    if (i4) {
-        if (M == 1)
-            launch_gemm<1, true>(a, stream);
-        else if (M == 2)
-            launch_gemm<2, true>(a, stream);
-        else if (M <= 4)
-            launch_gemm<4, true>(a, stream);
-        else if (M <= 8)
-            launch_gemm<8, true>(a, stream);
-        else
-            launch_gemm<16, true>(a, stream);
-    } else {
-        if (M == 1)
-            launch_gemm<1, false>(a, stream);
-        else if (M == 2)
-            launch_gemm<2, false>(a, stream);
-        else if (M <= 4)
-            launch_gemm<4, false>(a, stream);
-        else if (M <= 8)
-            launch_gemm<8, false>(a, stream);
-        else
-            launch_gemm<16, false>(a, stream);
+    if (M > 16 && M <= 48) {
+        // a few decode batches: the streaming kernels on 16-row slices of x and
+        // y (each slice re-reads the weights, still cheaper than the tiled
+        // kernel while it cannot fill the chip)
+        for (int64_t m0 = 0; m0 < M; m0 += 16) {
+            GemmArgs s16 = a;
+            s16.x = x + m0 * K;
+            s16.y = y + m0 * N;
+            s16.M = static_cast<int>(M - m0 < 16 ? M - m0 : 16);
+            launch_decode(s16, i4, stream);
+        }
+        return launched();
     }
+    if (M > 16) {
+        if (M <= 64) {
+            const dim3 gd(static_cast<unsigned>((N + BIG_BN - 1) / BIG_BN),
+                          static_cast<unsigned>((M + 63) / 64));
+            hipLaunchKernelGGL((k_gemm_big<64>), gd, dim3(256), 0, stream, a);
+        } else {
+            const dim3 gd(static_cast<unsigned>((N + BIG_BN - 1) / BIG_BN),
+                          static_cast<unsigned>((M + 127) / 128));
+            hipLaunchKernelGGL((k_gemm_big<128>), gd, dim3(256), 0, stream, a);
+        }
+        return launched();
+    }
+    launch_decode(a, i4, stream);
     return launched();
 }
 
@@ -1257,7 +1441,7 @@ const char* any4_status_string(any4_status s)
     case ANY4_E_NULL: return "ANY4_E_NULL: a required pointer is NULL";
     case ANY4_E_SHAPE: return "ANY4_E_SHAPE: unsupported sizes (negative size, K not a multiple "
                               "of 128, g not a positive multiple of 128, K % g != 0, K/g > 512, "
-                              "M > 16, or buffers of 2 GiB or more)";
+                              "M above 65535*64, or buffers of 2 GiB or more)";
     case ANY4_E_ALIGN: return "ANY4_E_ALIGN: a base pointer is not aligned as required";
     case ANY4_E_WORKSPACE: return "ANY4_E_WORKSPACE: workspace too small";
     case ANY4_E_HIP: return "ANY4_E_HIP: the HIP runtime reported an error";

@@ -64,7 +64,7 @@ typedef enum any4_status {
     ANY4_OK = 0,
     ANY4_E_NULL = 1,      /* a required pointer is NULL                               */
     ANY4_E_SHAPE = 2,     /* a size is negative, K is not a multiple of 128, g is not a
-                             positive multiple of 128, K % g != 0, M > 16 or K/g > 512 (any4_gemm*),
+                             positive multiple of 128, K % g != 0, K/g > 512 or M > 65535*64 (any4_gemm*),
                              or a buffer would be 2 GiB or larger                     */
     ANY4_E_ALIGN = 3,     /* a base pointer misses the alignment stated above          */
     ANY4_E_WORKSPACE = 4, /* workspace smaller than any4_gemm_workspace_size()         */
@@ -115,8 +115,11 @@ any4_status any4_dequant(const uint8_t* packed, const uint16_t* lut, const uint1
 size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
 
 /*
- * any4_gemm -- y = x * W^T with W the any4 weights above, for M = 1..16
- * (the explainer's section 三: decode batches of 1..16):
+ * any4_gemm -- y = x * W^T with W the any4 weights above.  Built for the
+ * decode batches M = 1..16 of the explainer's section 三 (weights streamed
+ * once, decoded in registers); larger M (prefill) also works: up to 48 rows
+ * as 16-row slices, beyond that a tiled matrix-core product over weight
+ * tiles dequantised in on-chip memory.
  *     y[m][n] = bf16_rne( sum_k x[m][k] * w[n][k] )
  * with w[n][k] exactly the any4_dequant value (every weight is dequantised to
  * that bf16 inside the kernel; the weights are never written to memory).  The
@@ -128,8 +131,9 @@ size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
  *   x                         device, [M][K] bf16, read-only.
  *   packed, lut, alpha, beta  device, read-only.
  *   y                         device, [M][N] bf16, written.
- *   M in 0..16, N >= 0, K >= 0 with K % g == 0 and K/g <= 512.  M*N == 0 is a
- *   no-op; K == 0 writes y = 0 (x, packed, lut, alpha and beta may then be NULL).
+ *   M >= 0 (at most 65535*64), N >= 0, K >= 0 with K % g == 0 and K/g <= 512.
+ *   M*N == 0 is a no-op; K == 0 writes y = 0 (x, packed, lut, alpha and beta
+ *   may then be NULL).
  *   workspace, workspace_bytes  device scratch of at least
  *       any4_gemm_workspace_size(M, N, K, g) bytes; NULL and 0 when that is 0,
  *       which it is for every shape today.

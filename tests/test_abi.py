@@ -38,7 +38,8 @@ def test_status_strings():
 A = 1 << 20          # a 16-byte aligned fake address (never dereferenced)
 
 
-@pytest.mark.parametrize("M,N,K,g", [(17, 16, 128, 128), (-1, 16, 128, 128), (1, -1, 128, 128),
+@pytest.mark.parametrize("M,N,K,g", [(65535 * 64 + 1, 16, 128, 128), (-1, 16, 128, 128),
+                                     (1, -1, 128, 128),
                                      (1, 16, 128, 64), (1, 16, 256, 96), (1, 16, 384, 256),
                                      (1, 16, -128, 128), (1, 16, 128, 0)])
 def test_gemm_shape_errors(M, N, K, g):
@@ -103,7 +104,7 @@ def test_workspace_size_is_defined_for_all_shapes():
 
 def test_gemm_int4_errors():
     # same checks as any4_gemm, without the table
-    assert any4.gemm_int4_raw(A, A, A, A, A, 17, 16, 128, 128, stream=0) == 2
+    assert any4.gemm_int4_raw(A, A, A, A, A, 65535 * 64 + 1, 16, 128, 128, stream=0) == 2
     assert any4.gemm_int4_raw(A, A, A, A, A, 1, 16, 384, 256, stream=0) == 2
     assert any4.gemm_int4_raw(A, A, A, A, A, 1, 16, 128 * 513, 128, stream=0) == 2
     assert any4.gemm_int4_raw(None, A, A, A, A, 1, 16, 128, 128, stream=0) == 1

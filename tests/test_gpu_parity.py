@@ -6,6 +6,8 @@
     oracle's fp64 product, for configs 0-3 at every batch size (all outputs)
     and config 4 (70B decoder-layer shapes from the oracle's k-means) on
     sampled rows;
+  * M > 16 (16-row slices, the tiled kernel): within the bound on ragged shapes, sampled rows
+    of the 14336x4096 layer, and one-hot rows giving dequantised columns;
   * plain int4 (no table): bitwise equal to the table path with every row
     0..15 and within the bound of the oracle;
   * invariants on the device: identity table returns the indices, one-hot x
@@ -183,6 +185,56 @@ def test_gemm_large_k(M, N, K, g):
 
 
 # --------------------------------------------------------------------------
+# M > 16: 16-row slices (M <= 48), then the LDS-tiled MFMA kernel (64 or 128
+# x rows per workgroup)
+# --------------------------------------------------------------------------
+# 17..48: 16-row slices through the streaming kernels; above: the tiled kernel
+@pytest.mark.parametrize("M,N,K,g", [(17, 40, 256, 128), (48, 70, 256, 128), (49, 33, 256, 128),
+                                     (64, 64, 128, 128), (65, 100, 512, 128),
+                                     (100, 300, 1024, 256), (128, 17, 384, 128),
+                                     (129, 65, 2048, 1024), (300, 130, 640, 128),
+                                     (33, 16 * 50 + 3, 14336, 1024)])
+def test_gemm_large_m(M, N, K, g):
+    inp = workloads.generic(M * 5 + N + K, M, N, K, g)
+    L = gu.Layer(inp)
+    y = any4.gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g)
+    torch.cuda.synchronize()
+    y_ref, ad = oracle.gemm(inp.x, L.w_ref(), nthreads=oracle.default_threads())
+    gu.assert_within_bound(y, y_ref, ad, f"large M {M}x{N}x{K} g{g}")
+
+
+@pytest.mark.parametrize("M", [32, 256])
+def test_gemm_large_m_config2_sampled_rows(M):
+    """The 14336x4096 layer at prefill batches: sampled rows against the oracle."""
+    L = gu.config_layer(2)
+    rng = np.random.default_rng(M)
+    x_host = workloads.to_bf16_bits(rng.standard_normal((M, L.K)))
+    y = any4.gemm(gu.dev_b16(x_host), L.packed, L.lut, L.alpha, L.beta, L.g)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, L.N - 1], rng.choice(L.N, 200, replace=False)]))
+    y_ref, ad = oracle.gemm(x_host, L.w_ref()[rows], nthreads=oracle.default_threads())
+    gu.assert_within_bound(y[:, torch.from_numpy(rows).to(gu.DEV)], y_ref, ad,
+                           f"config 2 M={M}")
+
+
+def test_gemm_large_m_one_hot_x_returns_dequantised_columns():
+    """One-hot x rows (M = 40) give the dequantised columns exactly: the tiled
+    kernel multiplies the any4_dequant values."""
+    inp = workloads.generic(91, 40, 48, 512, 128)
+    L = gu.Layer(inp)
+    w_ref = L.w_ref()
+    one = workloads.to_bf16_bits(np.array([1.0]))[0]
+    x = np.zeros((40, 512), np.uint16)
+    ks = np.arange(40) * 12 + 3
+    x[np.arange(40), ks] = one
+    y = any4.gemm(gu.dev_b16(x), L.packed, L.lut, L.alpha, L.beta, 128)
+    torch.cuda.synchronize()
+    yb = gu.host_b16(y)
+    for m, k in enumerate(ks):
+        assert np.array_equal(yb[m], w_ref[:, k]), k
+
+
+# --------------------------------------------------------------------------
 # plain int4 (no table): w = alpha * q + beta
 # --------------------------------------------------------------------------
 def _identity_table(N):
@@ -196,7 +248,8 @@ def _identity_table(N):
                                          (1, 17, 128, 128, None), (16, 15, 128, 128, None),
                                          (1, 16 * 2000 + 3, 128, 128, None),
                                          (2, 16 * 300 + 7, 8192, 128, None),
-                                         (5, 100, 14336, 1024, None), (16, 33, 65536, 128, None)])
+                                         (5, 100, 14336, 1024, None), (16, 33, 65536, 128, None),
+                                         (40, 70, 512, 128, None), (200, 33, 1024, 256, None)])
 def test_gemm_int4(M, N, K, g, cfg):
     """any4_gemm_int4 is bitwise any4_gemm with every table row 0..15, and both
     are within the bound of the oracle's product with the int4 weights."""
