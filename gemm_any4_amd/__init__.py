@@ -33,7 +33,7 @@ _STATUS_NAMES = {0: "ANY4_OK", 1: "ANY4_E_NULL", 2: "ANY4_E_SHAPE", 3: "ANY4_E_A
 
 # every symbol include/any4.h declares
 EXPORTS = ("any4_packed_bytes", "any4_pack", "any4_dequant", "any4_gemm_workspace_size",
-           "any4_gemm", "any4_gemm_int4", "any4_status_string")
+           "any4_gemm", "any4_gemm_int4", "any4_quantize", "any4_status_string")
 
 _lib = None
 
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.any4_gemm.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P, SZ, P]
         L.any4_gemm_int4.restype = ctypes.c_int
         L.any4_gemm_int4.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
+        L.any4_quantize.restype = ctypes.c_int
+        L.any4_quantize.argtypes = [P, P, P, P, P, P, I64, I64, I64, ctypes.c_int, P]
         L.any4_status_string.restype = ctypes.c_char_p
         L.any4_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -144,6 +146,12 @@ def gemm_int4_raw(x_ptr, packed_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
                   stream=None) -> int:
     return lib().any4_gemm_int4(x_ptr, packed_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
                                 _stream(stream))
+
+
+def quantize_raw(w_ptr, ex_ptr, idx_ptr, lut_ptr, alpha_ptr, beta_ptr, N, K, g, iters,
+                 stream=None) -> int:
+    return lib().any4_quantize(w_ptr, ex_ptr, idx_ptr, lut_ptr, alpha_ptr, beta_ptr, N, K, g,
+                               iters, _stream(stream))
 
 
 # --------------------------------------------------------------------------
@@ -257,3 +265,27 @@ def gemm_int4(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, beta: 
     check(gemm_int4_raw(_ptr(x), _ptr(packed), _ptr(alpha), _ptr(beta), _ptr(out), M, N, K, g,
                         stream))
     return out
+
+
+def quantize(W: torch.Tensor, ex: torch.Tensor, g: int, iters: int = 10, stream=None):
+    """any4-quantise W fp32 [N, K] with channel importance ex fp32 [K] (E|x|).
+
+    Returns (idx uint8 [N, K], lut bf16 [N, 16], alpha bf16 [N, K/g],
+    beta bf16 [N, K/g]); pack idx with pack() before gemm()."""
+    for t, name in ((W, "W"), (ex, "ex")):
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32, got {t.dtype}")
+        _dev(t, name)
+    N, K = W.shape
+    if ex.shape != (K,):
+        raise ValueError("ex must be [K]")
+    if g <= 0 or K % g:
+        raise ValueError("g must divide K")
+    dev = W.device
+    idx = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    lut = torch.empty((N, 16), dtype=torch.bfloat16, device=dev)
+    alpha = torch.empty((N, K // g), dtype=torch.bfloat16, device=dev)
+    beta = torch.empty((N, K // g), dtype=torch.bfloat16, device=dev)
+    check(quantize_raw(_ptr(W), _ptr(ex), _ptr(idx), _ptr(lut), _ptr(alpha), _ptr(beta), N, K, g,
+                       iters, stream))
+    return idx, lut, alpha, beta

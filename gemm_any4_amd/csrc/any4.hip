@@ -1258,6 +1258,130 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
 }
 
 // ---------------------------------------------------------------------------
+// quantiser
+// ---------------------------------------------------------------------------
+// binary64 -> bf16 bits with a single rounding to nearest even: the value is
+// first narrowed to binary32 with round-to-odd (truncate, then set the last
+// bit if anything was dropped), which keeps enough information for the
+// second rounding, binary32 -> bf16 to nearest even, to equal the direct one.
+__device__ __forceinline__ uint32_t f64_to_bf16(double d)
+{
+    if (d != d)
+        return 0x7FC0u;
+    float f = __double2float_rz(d);
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if (static_cast<double>(f) != d && (u & 0x7F800000u) != 0x7F800000u)
+        u |= 1u;
+    return f32_to_bf16(__builtin_bit_cast(float, u));
+}
+
+__device__ __forceinline__ double bf16_to_f64(uint32_t h)
+{
+    return static_cast<double>(bf16_to_f32(h));
+}
+
+// index of the nearest of the 16 table values (ties: the lower index)
+__device__ __forceinline__ int nearest16(double v, const double (&L)[16])
+{
+    int best = 0;
+    double bd = fabs(v - L[0]);
+#pragma unroll
+    for (int q = 1; q < 16; ++q) {
+        const double d = fabs(v - L[q]);
+        if (d < bd) {
+            bd = d;
+            best = q;
+        }
+    }
+    return best;
+}
+
+// One thread per weight row, everything in binary64 and in the order below,
+// so that the result is a deterministic function of the inputs:
+//   1. per group of g weights: beta = bf16(min), alpha = bf16((max - min) / 15)
+//   2. normalised weights ws = (w - beta) / alpha (0 where alpha = 0), their
+//      importance wt = alpha * ex[k]
+//   3. table L = 0, 1, .., 15; `iters` rounds of: every weight to its nearest
+//      table value, then L[q] = sum(wt * ws) / sum(wt) over the members of q
+//      in increasing k (products and sums rounded separately); empty
+//      clusters keep their value
+//   4. table stored in bf16; every weight assigned to the nearest stored value
+// The per-thread sums live in LDS: [2][16][QT] doubles.
+constexpr int QT = 64;   // threads (rows) per workgroup
+
+__global__ __launch_bounds__(QT) void k_quantize(const float* __restrict__ W,
+                                                 const float* __restrict__ ex,
+                                                 uint8_t* __restrict__ idx,
+                                                 uint16_t* __restrict__ lut,
+                                                 uint16_t* __restrict__ alpha,
+                                                 uint16_t* __restrict__ beta, int N, int K,
+                                                 int g, int iters)
+{
+    __shared__ double sums[2][16][QT];
+    const int t = threadIdx.x;
+    const int n = blockIdx.x * QT + t;
+    if (n >= N)
+        return;   // no barrier follows: the sums are per thread
+    const int G = K / g;
+    const float* row = W + static_cast<size_t>(n) * K;
+    uint16_t* an = alpha + static_cast<size_t>(n) * G;
+    uint16_t* bn = beta + static_cast<size_t>(n) * G;
+
+    for (int j = 0; j < G; ++j) {   // 1. group scale
+        double lo = row[j * g], hi = lo;
+        for (int k = j * g + 1; k < (j + 1) * g; ++k) {
+            const double v = row[k];
+            lo = v < lo ? v : lo;
+            hi = v > hi ? v : hi;
+        }
+        bn[j] = static_cast<uint16_t>(f64_to_bf16(lo));
+        an[j] = static_cast<uint16_t>(f64_to_bf16((hi - lo) / 15.0));
+    }
+
+    double L[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        L[q] = q;
+    for (int it = 0; it < iters; ++it) {   // 3. weighted k-means
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            sums[0][q][t] = sums[1][q][t] = 0.0;
+        for (int j = 0; j < G; ++j) {
+            const double al = bf16_to_f64(an[j]);
+            const double be = bf16_to_f64(bn[j]);
+            for (int k = j * g; k < (j + 1) * g; ++k) {
+                const double ws = al != 0.0 ? (static_cast<double>(row[k]) - be) / al : 0.0;
+                const double wt = __dmul_rn(al, static_cast<double>(ex[k]));
+                const int q = nearest16(ws, L);
+                sums[0][q][t] = __dadd_rn(sums[0][q][t], __dmul_rn(wt, ws));
+                sums[1][q][t] = __dadd_rn(sums[1][q][t], wt);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            if (sums[1][q][t] > 0.0)
+                L[q] = sums[0][q][t] / sums[1][q][t];
+    }
+
+    double Lq[16];   // 4. the stored table and the final assignment
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const uint32_t h = f64_to_bf16(L[q]);
+        lut[static_cast<size_t>(n) * 16 + q] = static_cast<uint16_t>(h);
+        Lq[q] = bf16_to_f64(h);
+    }
+    uint8_t* in = idx + static_cast<size_t>(n) * K;
+    for (int j = 0; j < G; ++j) {
+        const double al = bf16_to_f64(an[j]);
+        const double be = bf16_to_f64(bn[j]);
+        for (int k = j * g; k < (j + 1) * g; ++k) {
+            const double ws = al != 0.0 ? (static_cast<double>(row[k]) - be) / al : 0.0;
+            in[k] = static_cast<uint8_t>(nearest16(ws, Lq));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host helpers
 // ---------------------------------------------------------------------------
 bool aligned(const void* p, uintptr_t a)
@@ -1526,6 +1650,27 @@ any4_status any4_gemm_int4(const uint16_t* x, const uint8_t* packed, const uint1
                            int64_t g, hipStream_t stream)
 {
     return gemm_call(true, x, packed, nullptr, alpha, beta, y, M, N, K, g, stream);
+}
+
+any4_status any4_quantize(const float* W, const float* ex, uint8_t* idx, uint16_t* lut,
+                          uint16_t* alpha, uint16_t* beta, int64_t N, int64_t K, int64_t g,
+                          int iters, hipStream_t stream)
+{
+    if (N < 0 || K < 0 || g <= 0 || K % g != 0 || iters < 0 ||
+        static_cast<size_t>(N) * K >= (static_cast<size_t>(1) << 31))
+        return ANY4_E_SHAPE;
+    if (N == 0 || K == 0)
+        return ANY4_OK;
+    if (!W || !ex || !idx || !lut || !alpha || !beta)
+        return ANY4_E_NULL;
+    if (!aligned(W, 4) || !aligned(ex, 4) || !aligned(lut, 2) || !aligned(alpha, 2) ||
+        !aligned(beta, 2))
+        return ANY4_E_ALIGN;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_quantize, dim3(static_cast<unsigned>((N + QT - 1) / QT)), dim3(QT), 0,
+                       stream, W, ex, idx, lut, alpha, beta, static_cast<int>(N),
+                       static_cast<int>(K), static_cast<int>(g), iters);
+    return launched();
 }
 
 }  // extern "C"

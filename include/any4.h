@@ -159,6 +159,39 @@ any4_status any4_gemm_int4(const uint16_t* x, const uint8_t* packed, const uint1
                            const uint16_t* beta, uint16_t* y, int64_t M, int64_t N, int64_t K,
                            int64_t g, hipStream_t stream);
 
+/*
+ * any4_quantize -- the any4 quantiser: turns weights into the idx, lut, alpha
+ * and beta arrays above (the explainer, section 二: step 1, group scaling and
+ * the calibration statistic E|x|; step 2, the E-step / M-step iteration that
+ * learns each row's 16 table values, weighting each weight by alpha * E|x|).
+ * Per row, in binary64 and in this order:
+ *   1. per group of g weights: beta = bf16(min), alpha = bf16((max - min) / 15)
+ *      (the asymmetric range mapping that makes the start table 0..15 plain
+ *      int4);
+ *   2. ws = (w - beta) / alpha (0 where alpha == 0), wt = alpha * ex[k];
+ *   3. L = 0, 1, .., 15, then `iters` rounds of: assign every weight to its
+ *      nearest table value (ties: the lower index), then
+ *      L[q] = sum(wt * ws) / sum(wt) over the members of q, summed in
+ *      increasing k with products and sums rounded separately; a cluster
+ *      without members keeps its value;
+ *   4. lut = bf16(L), and idx = the nearest stored value for every weight.
+ * The result is a deterministic function of the inputs.  One GPU thread
+ * works through one row (the sums must run in k order), so this is an
+ * offline step: milliseconds per layer.
+ *   W      device, [N][K] fp32, read-only.
+ *   ex     device, [K] fp32, E|x| of each input channel, read-only.
+ *   idx    device, [N][K] uint8 (values 0..15), written; pack it with any4_pack.
+ *   lut    device, [N][16] bf16, written.
+ *   alpha, beta  device, [N][K/g] bf16, written.
+ *   N >= 0, K >= 0, g > 0 with K % g == 0, iters >= 0, N*K < 2^31.
+ *   N*K == 0 is a no-op.
+ * Errors: ANY4_E_SHAPE, ANY4_E_NULL, ANY4_E_ALIGN (W or ex not 4-byte aligned,
+ * lut, alpha or beta not 2-byte aligned), ANY4_E_HIP.
+ */
+any4_status any4_quantize(const float* W, const float* ex, uint8_t* idx, uint16_t* lut,
+                          uint16_t* alpha, uint16_t* beta, int64_t N, int64_t K, int64_t g,
+                          int iters, hipStream_t stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char* any4_status_string(any4_status s);
 

@@ -114,3 +114,12 @@ def test_gemm_int4_errors():
     assert any4.gemm_int4_raw(A + 2, A, A, A, A, 1, 16, 128, 128, stream=0) == 3
     assert any4.gemm_int4_raw(A, A, A + 2, A, A, 1, 16, 128, 128, stream=0) == 3
     assert any4.gemm_int4_raw(None, None, None, None, None, 0, 16, 128, 128, stream=0) == 0
+
+
+def test_quantize_errors():
+    assert any4.quantize_raw(A, A, A, A, A, A, 4, 256, 96, 10, stream=0) == 2     # K % g
+    assert any4.quantize_raw(A, A, A, A, A, A, 4, 256, 128, -1, stream=0) == 2    # iters
+    assert any4.quantize_raw(A, A, A, A, A, A, -1, 256, 128, 1, stream=0) == 2
+    assert any4.quantize_raw(A, None, A, A, A, A, 4, 256, 128, 1, stream=0) == 1
+    assert any4.quantize_raw(A + 2, A, A, A, A, A, 4, 256, 128, 1, stream=0) == 3
+    assert any4.quantize_raw(None, None, None, None, None, None, 0, 256, 128, 1, stream=0) == 0

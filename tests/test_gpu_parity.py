@@ -8,6 +8,8 @@
     sampled rows;
   * M > 16 (16-row slices, the tiled kernel): within the bound on ragged shapes, sampled rows
     of the 14336x4096 layer, and one-hot rows giving dequantised columns;
+  * fixed formats (int4, fp4 E2M1, nf4) as tables: dequant bit-exact, gemm
+    within the bound;
   * plain int4 (no table): bitwise equal to the table path with every row
     0..15 and within the bound of the oracle;
   * invariants on the device: identity table returns the indices, one-hot x
@@ -284,6 +286,25 @@ def test_gemm_int4_empty_and_k0():
     any4.gemm_int4(x, torch.zeros((0,), dtype=torch.uint8, device=gu.DEV), e, e, 128, out=y)
     torch.cuda.synchronize()
     assert (y == 0).all()
+
+
+# --------------------------------------------------------------------------
+# fixed 4-bit formats (int4, fp4, nf4) as tables through the same kernels
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt", ["int4", "fp4", "nf4"])
+@pytest.mark.parametrize("N,K,g", [(1000, 2048, 128), (300, 8192, 1024)])
+def test_fixed_formats(fmt, N, K, g):
+    inp = workloads.generic(17 + N + K, 16, N, K, g)
+    lut = np.tile(workloads.fixed_table(fmt), (N, 1))
+    L = gu.Layer(workloads.Any4Inputs(N, K, g, inp.idx, lut, inp.alpha, inp.beta, inp.x))
+    w = any4.dequant(L.packed, L.lut, L.alpha, L.beta, g)
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.host_b16(w), L.w_ref())
+    for M in (1, 16):
+        y = any4.gemm(L.x[:M], L.packed, L.lut, L.alpha, L.beta, g)
+        torch.cuda.synchronize()
+        y_ref, ad = oracle.gemm(inp.x[:M], L.w_ref(), nthreads=oracle.default_threads())
+        gu.assert_within_bound(y, y_ref, ad, f"{fmt} M={M} {N}x{K} g{g}")
 
 
 # --------------------------------------------------------------------------

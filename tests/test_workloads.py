@@ -49,3 +49,21 @@ def test_raw_layer_prefix_rows_identical():
     r = workloads.raw_layer("qkvo", rows=4)
     assert r.W.shape == (4, 8192) and r.Ex.shape == (8192,) and r.x.shape == (16, 8192)
     assert np.all(r.Ex > 0)
+
+
+def test_fixed_tables():
+    """The baseline 4-bit formats as tables: int4 is the integer grid, fp4 is
+    E2M1 (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, sign in bit 3), nf4 is a
+    sorted normal-quantile grid spanning [-1, 1] with an exact zero."""
+    f = workloads.bf16_bits_to_f64
+    assert np.array_equal(f(workloads.fixed_table("int4")), np.arange(16.0))
+    fp4 = f(workloads.fixed_table("fp4"))
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    assert np.array_equal(fp4[:8], mags) and np.array_equal(fp4[8:], -mags)
+    assert workloads.fixed_table("fp4")[8] == 0x8000          # -0
+    nf4 = f(workloads.fixed_table("nf4"))
+    assert nf4[0] == -1.0 and nf4[15] == 1.0 and nf4[7] == 0.0
+    assert np.all(np.diff(nf4) > 0)
+    # quantile spacing: the steps grow towards the tails on both sides
+    d = np.diff(nf4)
+    assert np.all(np.diff(d[8:]) > 0) and np.all(np.diff(d[:7]) < 0)

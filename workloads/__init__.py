@@ -172,3 +172,36 @@ def raw_layer(name: str, rows: int | None = None) -> RawLayer:
         W = np.ascontiguousarray(W[:rows])
         N = rows
     return RawLayer(name, N, K, CONFIG4_G, W, Ex, x)
+
+
+def fixed_table(name: str) -> np.ndarray:
+    """The 16 values of a fixed 4-bit format as bf16 bits, for running the
+    baseline formats the pages compare any4 with through the same table path:
+
+      "int4"  0, 1, ..., 15 (uniform integer grid; scale and offset do the rest)
+      "fp4"   E2M1 (sign, 2 exponent bits with bias 1, 1 mantissa bit): code
+              s<<3 | e<<1 | m is (-1)^s * (m/2) for e = 0, else
+              (-1)^s * 2^(e-1) * (1 + m/2); 0..7 positive, 8..15 negative
+      "nf4"   normal-float grid: quantiles of N(0, 1), eight on the positive
+              side and seven on the negative side, each side scaled to reach
+              1 in magnitude, plus an exact 0 (this module's reading of the
+              published construction: the outermost quantile is taken at
+              probability 1 - 1/32 on each side)
+    """
+    if name == "int4":
+        v = np.arange(16, dtype=np.float64)
+    elif name == "fp4":
+        v = np.empty(16)
+        for code in range(16):
+            s, e, m = code >> 3, (code >> 1) & 3, code & 1
+            mag = m / 2.0 if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 2.0)
+            v[code] = -mag if s else mag
+    elif name == "nf4":
+        from scipy.stats import norm
+        top = 1.0 - 1.0 / 32.0
+        pos = norm.ppf(0.5 + np.arange(1, 9) * (top - 0.5) / 8)
+        neg = -norm.ppf(0.5 + np.arange(1, 8) * (top - 0.5) / 7)
+        v = np.concatenate([np.sort(neg / neg.min() * -1.0), [0.0], pos / pos.max()])
+    else:
+        raise ValueError(name)
+    return to_bf16_bits(v)
