@@ -60,6 +60,13 @@ def _load():
         lib.orc_group_scale.argtypes = [P, I64, I64, I64, P, P]
         lib.orc_kmeans_row.restype = None
         lib.orc_kmeans_row.argtypes = [P, P, I64, ctypes.c_int, P, P, P]
+        lib.orc_kmeans_quantize_q.restype = ctypes.c_int
+        lib.orc_kmeans_quantize_q.argtypes = [P, P, I64, I64, I64, ctypes.c_int, ctypes.c_int,
+                                              P, P, P, P, ctypes.c_int]
+        lib.orc_kmeans_row_q.restype = None
+        lib.orc_kmeans_row_q.argtypes = [P, P, I64, ctypes.c_int, ctypes.c_int, P, P, P]
+        lib.orc_group_scale_q.restype = None
+        lib.orc_group_scale_q.argtypes = [P, I64, I64, I64, ctypes.c_int, P, P]
         lib.orc_kmeans_quantize.restype = ctypes.c_int
         lib.orc_kmeans_quantize.argtypes = [P, P, I64, I64, I64, ctypes.c_int, P, P, P, P,
                                             ctypes.c_int]
@@ -202,46 +209,53 @@ def tolerance(absdot: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # quantiser
 # --------------------------------------------------------------------------
-def group_scale(W, g: int):
+def group_scale(W, g: int, levels: int = 16):
+    """Min-max group scale onto [0, levels - 1] (bf16 alpha, beta)."""
     W = _c(W, np.float64)
     N, K = W.shape
     a = np.empty((N, K // g), np.uint16)
     b = np.empty((N, K // g), np.uint16)
-    _load().orc_group_scale(_ptr(W), N, K, g, _ptr(a), _ptr(b))
+    _load().orc_group_scale_q(_ptr(W), N, K, g, levels, _ptr(a), _ptr(b))
     return a, b
 
 
-def kmeans_row(ws, wt, iters: int, init=None, trace: bool = False):
-    """Weighted k-means of one row in the normalised domain (fp64).
+def kmeans_row(ws, wt, iters: int, init=None, trace: bool = False, levels: int = 16):
+    """Weighted k-means of one row in the normalised domain (fp64), with
+    `levels` table values (16; 8 or 4 for any3 / any2).
 
-    Returns (L[16] fp64, idx[K] u8) or (L, idx, trace[2*iters])."""
+    Returns (L[levels] fp64, idx[K] u8) or (L, idx, trace[2*iters])."""
     ws = _c(ws, np.float64)
     wt = _c(wt, np.float64)
     K = ws.size
-    L = _c(np.arange(16) if init is None else init, np.float64).copy()
+    L = _c(np.arange(levels) if init is None else init, np.float64).copy()
+    assert L.shape == (levels,)
     idx = np.empty(K, np.uint8)
     tr = np.empty(max(1, 2 * iters), np.float64)
-    _load().orc_kmeans_row(_ptr(ws), _ptr(wt), K, iters, _ptr(L), _ptr(idx),
-                           _ptr(tr) if trace else None)
+    _load().orc_kmeans_row_q(_ptr(ws), _ptr(wt), K, iters, levels, _ptr(L), _ptr(idx),
+                             _ptr(tr) if trace else None)
     if trace:
         return L, idx, tr[: 2 * iters]
     return L, idx
 
 
-def kmeans_quantize(W, Ex, g: int, iters: int = 10, nthreads: int | None = None):
-    """any4-quantise W[N, K] (fp64) with channel importance Ex[K] = E|x|.
+def kmeans_quantize(W, Ex, g: int, iters: int = 10, nthreads: int | None = None,
+                    bits: int = 4):
+    """any4-quantise W[N, K] (fp64) with channel importance Ex[K] = E|x|
+    (bits = 3 or 2: any3 / any2, 8 or 4 table values, the rest of the 16-entry
+    row zero).
 
     Returns (idx u8 [N, K], lut bf16 bits [N, 16], alpha, beta bf16 bits [N, K/g])."""
     W = _c(W, np.float64)
     Ex = _c(Ex, np.float64)
     N, K = W.shape
-    assert Ex.shape == (K,) and K % g == 0
+    assert Ex.shape == (K,) and K % g == 0 and bits in (2, 3, 4)
     idx = np.empty((N, K), np.uint8)
     lut = np.empty((N, 16), np.uint16)
     a = np.empty((N, K // g), np.uint16)
     b = np.empty((N, K // g), np.uint16)
-    rc = _load().orc_kmeans_quantize(_ptr(W), _ptr(Ex), N, K, g, iters, _ptr(idx), _ptr(lut),
-                                     _ptr(a), _ptr(b), nthreads or default_threads())
+    rc = _load().orc_kmeans_quantize_q(_ptr(W), _ptr(Ex), N, K, g, iters, 1 << bits, _ptr(idx),
+                                       _ptr(lut), _ptr(a), _ptr(b),
+                                       nthreads or default_threads())
     if rc != 0:
         raise MemoryError("oracle quantiser could not allocate its row buffers")
     return idx, lut, a, b

@@ -15,6 +15,9 @@
  *           beta), step 2 "E-Step" / "M-Step" (weighted k-means that learns the
  *           per-row table), section 3 (overhead: 16 table entries per row),
  *           section 三 (the matmul runs at batch 1..16).
+ *   [PAPER] "any4: Learned 4-bit Numeric Representation for LLMs" (the
+ *           shd-paper.top summary), abstract: the same method at 3 and 2 bits
+ *           (any3, any2).
  *   [ABS]   "any4: Learned 4-bit Numeric Representation for LLMs" (the
  *           shd-paper.top summary), abstract: a lookup-table GEMM for decode.
  *   [INT]   "量化技术应用：INT4/INT8对anything-llm的影响" (yongjin360.com),
@@ -33,7 +36,11 @@
  *   - the quantiser's group scale is asymmetric min-max onto [0, 15]; k-means
  *     starts from the identity table 0..15, ties go to the lower index, an
  *     empty (or zero-weight) cluster keeps its value, and it runs a fixed
- *     number of E/M rounds.
+ *     number of E/M rounds;
+ *   - any3 / any2 ([PAPER]) are the same quantiser with Q = 8 / 4 table
+ *     values: min-max onto [0, Q-1], start table 0..Q-1, indices 0..Q-1; the
+ *     16-entry table row keeps the Q learned values first and zeros after
+ *     them, so the 4-bit layouts and kernels run such layers unchanged.
  *
  * Build: gcc -O2 -fPIC -shared -ffp-contract=off -pthread (see build.py).
  */
@@ -223,8 +230,10 @@ void orc_gemm(const uint16_t* x, const uint16_t* w, double* y, double* absdot,
 /* Group scale: beta = bf16(min), alpha = bf16((max - min) / 15) over each
  * contiguous group of g weights of a row, so that (w - beta) / alpha spans
  * [0, 15], the range of a 4-bit index. */
-void orc_group_scale(const double* W, int64_t N, int64_t K, int64_t g,
-                     uint16_t* alpha, uint16_t* beta)
+/* Group scale onto [0, levels - 1]: beta = bf16(min), alpha = bf16((max - min)
+ * / (levels - 1)). */
+void orc_group_scale_q(const double* W, int64_t N, int64_t K, int64_t g, int levels,
+                       uint16_t* alpha, uint16_t* beta)
 {
     int64_t groups = K / g;
     for (int64_t n = 0; n < N; ++n)
@@ -238,16 +247,23 @@ void orc_group_scale(const double* W, int64_t N, int64_t K, int64_t g,
                     hi = v;
             }
             beta[n * groups + j] = orc_f64_to_bf16(lo);
-            alpha[n * groups + j] = orc_f64_to_bf16((hi - lo) / 15.0);
+            alpha[n * groups + j] = orc_f64_to_bf16((hi - lo) / (double)(levels - 1));
         }
 }
 
-/* E-step: the index of the nearest table value (ties: the lower index). */
-static unsigned nearest(double v, const double* L)
+void orc_group_scale(const double* W, int64_t N, int64_t K, int64_t g,
+                     uint16_t* alpha, uint16_t* beta)
+{
+    orc_group_scale_q(W, N, K, g, 16, alpha, beta);
+}
+
+/* E-step: the index of the nearest of the Q table values (ties: the lower
+ * index). */
+static unsigned nearest(double v, const double* L, int Q)
 {
     unsigned best = 0;
     double bd = fabs(v - L[0]);
-    for (unsigned q = 1; q < 16; ++q) {
+    for (unsigned q = 1; q < (unsigned)Q; ++q) {
         double d = fabs(v - L[q]);
         if (d < bd) {
             bd = d;
@@ -270,16 +286,16 @@ static double objective(const double* ws, const double* wt, const uint8_t* idx,
 
 /* Weighted k-means over one row in the normalised domain.
  *   ws[k]: normalised weight w_s, wt[k]: its importance alpha * E|x|.
- *   L[16]: in = initial table, out = table after `iters` E/M rounds (fp64).
+ *   L[Q]: in = initial table, out = table after `iters` E/M rounds (fp64).
  *   idx[k]: out = assignment from the last E-step.
  *   trace (optional, 2*iters entries): objective after each E and each M step.
  * M-step: L_q = sum(wt * ws) / sum(wt) over the members of cluster q. */
-void orc_kmeans_row(const double* ws, const double* wt, int64_t K, int iters,
-                    double* L, uint8_t* idx, double* trace)
+void orc_kmeans_row_q(const double* ws, const double* wt, int64_t K, int iters, int Q,
+                      double* L, uint8_t* idx, double* trace)
 {
     for (int it = 0; it < iters; ++it) {
         for (int64_t k = 0; k < K; ++k)                     /* E-step */
-            idx[k] = (uint8_t)nearest(ws[k], L);
+            idx[k] = (uint8_t)nearest(ws[k], L, Q);
         if (trace)
             trace[2 * it] = objective(ws, wt, idx, L, K);
         double num[16] = {0}, den[16] = {0};                /* M-step */
@@ -287,7 +303,7 @@ void orc_kmeans_row(const double* ws, const double* wt, int64_t K, int iters,
             num[idx[k]] += wt[k] * ws[k];
             den[idx[k]] += wt[k];
         }
-        for (int q = 0; q < 16; ++q)
+        for (int q = 0; q < Q; ++q)
             if (den[q] > 0.0)
                 L[q] = num[q] / den[q];
         if (trace)
@@ -295,14 +311,20 @@ void orc_kmeans_row(const double* ws, const double* wt, int64_t K, int iters,
     }
     if (iters == 0)
         for (int64_t k = 0; k < K; ++k)
-            idx[k] = (uint8_t)nearest(ws[k], L);
+            idx[k] = (uint8_t)nearest(ws[k], L, Q);
+}
+
+void orc_kmeans_row(const double* ws, const double* wt, int64_t K, int iters,
+                    double* L, uint8_t* idx, double* trace)
+{
+    orc_kmeans_row_q(ws, wt, K, iters, 16, L, idx, trace);
 }
 
 typedef struct {
     const double* W;
     const double* Ex;
     int64_t N, K, g, n_begin, n_end;
-    int iters;
+    int iters, Q;
     uint8_t* idx;
     uint16_t* lut;
     uint16_t* alpha;
@@ -326,7 +348,7 @@ static void* quant_worker(void* arg)
         const double* row = q->W + n * K;
         uint16_t* a = q->alpha + n * groups;
         uint16_t* b = q->beta + n * groups;
-        orc_group_scale(row, 1, K, g, a, b);
+        orc_group_scale_q(row, 1, K, g, q->Q, a, b);
         for (int64_t k = 0; k < K; ++k) {
             double al = (double)orc_bf16_to_f32(a[k / g]);
             double be = (double)orc_bf16_to_f32(b[k / g]);
@@ -334,20 +356,20 @@ static void* quant_worker(void* arg)
             wt[k] = al * q->Ex[k];
         }
         double L[16];
-        for (int i = 0; i < 16; ++i)
-            L[i] = (double)i;                               /* int4 grid */
+        for (int i = 0; i < q->Q; ++i)
+            L[i] = (double)i;                               /* uniform integer grid */
         uint8_t* id = q->idx + n * K;
-        orc_kmeans_row(ws, wt, K, q->iters, L, id, NULL);
-        /* Store the table in bf16, then assign every weight to the stored
-         * values so that the indices match what is kept. */
+        orc_kmeans_row_q(ws, wt, K, q->iters, q->Q, L, id, NULL);
+        /* Store the table in bf16 (entries past Q: zero), then assign every
+         * weight to the stored values so that the indices match what is kept. */
         double Lq[16];
         for (int i = 0; i < 16; ++i) {
-            uint16_t h = orc_f64_to_bf16(L[i]);
+            uint16_t h = i < q->Q ? orc_f64_to_bf16(L[i]) : 0;
             q->lut[n * 16 + i] = h;
             Lq[i] = (double)orc_bf16_to_f32(h);
         }
         for (int64_t k = 0; k < K; ++k)
-            id[k] = (uint8_t)nearest(ws[k], Lq);
+            id[k] = (uint8_t)nearest(ws[k], Lq, q->Q);
     }
     free(ws);
     free(wt);
@@ -357,10 +379,12 @@ static void* quant_worker(void* arg)
 /* Full any4 quantisation of W[N][K] (fp64) with per-input-channel importance
  * Ex[K] = E|x|: group scale, then per-row weighted k-means.  Rows are
  * independent; threads split them.  Returns 0 on success. */
-int orc_kmeans_quantize(const double* W, const double* Ex, int64_t N, int64_t K, int64_t g,
-                        int iters, uint8_t* idx, uint16_t* lut, uint16_t* alpha,
-                        uint16_t* beta, int nthreads)
+int orc_kmeans_quantize_q(const double* W, const double* Ex, int64_t N, int64_t K, int64_t g,
+                          int iters, int Q, uint8_t* idx, uint16_t* lut, uint16_t* alpha,
+                          uint16_t* beta, int nthreads)
 {
+    if (Q < 2 || Q > 16)
+        return 2;
     if (nthreads < 1)
         nthreads = 1;
     if (nthreads > 256)
@@ -371,7 +395,7 @@ int orc_kmeans_quantize(const double* W, const double* Ex, int64_t N, int64_t K,
     quant_job jobs[256];
     for (int t = 0; t < nthreads; ++t) {
         jobs[t] = (quant_job){W, Ex, N, K, g, N * t / nthreads, N * (t + 1) / nthreads,
-                              iters, idx, lut, alpha, beta, 0};
+                              iters, Q, idx, lut, alpha, beta, 0};
         if (nthreads == 1)
             quant_worker(&jobs[t]);
         else
@@ -384,4 +408,11 @@ int orc_kmeans_quantize(const double* W, const double* Ex, int64_t N, int64_t K,
         if (jobs[t].failed)
             return 1;
     return 0;
+}
+
+int orc_kmeans_quantize(const double* W, const double* Ex, int64_t N, int64_t K, int64_t g,
+                        int iters, uint8_t* idx, uint16_t* lut, uint16_t* alpha,
+                        uint16_t* beta, int nthreads)
+{
+    return orc_kmeans_quantize_q(W, Ex, N, K, g, iters, 16, idx, lut, alpha, beta, nthreads);
 }

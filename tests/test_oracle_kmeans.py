@@ -12,7 +12,10 @@ convergence.  Pins:
     (the anything-llm INT4/INT8 article), computed here independently;
   * a row whose values sit near distinct integers converges in one round to
     zero error; a converged row is a fixed point; scaling E|x| by a power of
-    two leaves the table unchanged.
+    two leaves the table unchanged;
+  * any3 / any2 (8 / 4 table values): the same weighted Lloyd's algorithm
+    against scikit-learn, zero rounds as the uniform 3- / 2-bit grid, the
+    objective non-increasing, and the stored table and indices consistent.
 """
 import warnings
 
@@ -153,3 +156,71 @@ def test_thread_count_does_not_change_quantisation():
     r4 = oracle.kmeans_quantize(W, Ex, 128, 10, nthreads=4)
     for u, v in zip(r1, r4):
         assert np.array_equal(u, v)
+
+
+# ---- any3 / any2: the same quantiser with 8 / 4 table values ---------------
+@pytest.mark.parametrize("levels,seed,iters", [(8, 20, 3), (8, 21, 10), (4, 22, 1), (4, 23, 10)])
+def test_low_bit_matches_sklearn_weighted_lloyd(levels, seed, iters):
+    from sklearn.cluster import KMeans
+    rng = np.random.default_rng(seed)
+    K = 2048
+    ws = np.concatenate([rng.uniform(0, levels - 1, K // 2),
+                         np.clip(rng.normal((levels - 1) / 2, levels / 5, K - K // 2), 0,
+                                 levels - 1)])
+    wt = rng.lognormal(0, 1, K)
+    L, idx = oracle.kmeans_row(ws, wt, iters, levels=levels)
+    assert idx.max() < levels and np.bincount(idx, minlength=levels).min() > 0
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        km = KMeans(n_clusters=levels, init=np.arange(float(levels)).reshape(-1, 1), n_init=1,
+                    max_iter=iters, tol=0.0, algorithm="lloyd")
+        km.fit(ws.reshape(-1, 1), sample_weight=wt)
+    assert np.allclose(km.cluster_centers_.ravel(), L, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+def test_low_bit_zero_rounds_is_uniform_grid(bits):
+    """Zero rounds: min-max onto [0, 2^bits - 1] and the nearest grid point,
+    computed here independently; table entries past 2^bits are zero."""
+    Q = 1 << bits
+    rng = np.random.default_rng(30 + bits)
+    N, K, g = 6, 512, 128
+    W = rng.normal(0, 0.02, (N, K))
+    idx, lut, a, b = oracle.kmeans_quantize(W, np.ones(K), g, iters=0, nthreads=2, bits=bits)
+    grid = np.concatenate([np.arange(float(Q)), np.zeros(16 - Q)])
+    assert np.array_equal(lut, np.tile(workloads.to_bf16_bits(grid), (N, 1)))
+    # alpha = bf16((max - min) / (Q - 1)), beta = bf16(min): within bf16's
+    # half-ulp (2^-9 relative) of the exact values
+    Wg = W.reshape(N, K // g, g)
+    lo, hi = Wg.min(axis=2), Wg.max(axis=2)
+    assert np.all(np.abs(workloads.bf16_bits_to_f64(b) - lo) <= 2.0 ** -8 * np.abs(lo))
+    step = (hi - lo) / (Q - 1)
+    assert np.all(np.abs(workloads.bf16_bits_to_f64(a) - step) <= 2.0 ** -8 * step)
+    S = workloads.bf16_bits_to_f64(a).repeat(g, axis=1)
+    B = workloads.bf16_bits_to_f64(b).repeat(g, axis=1)
+    v = (W - B) / S
+    q = np.clip(np.ceil(v - 0.5), 0, Q - 1)
+    ok = np.abs(v - np.round(v)) != 0.5
+    assert np.array_equal(idx[ok], q[ok].astype(np.uint8))
+    assert idx.max() < Q
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+def test_low_bit_objective_and_consistency(bits):
+    Q = 1 << bits
+    rng = np.random.default_rng(40 + bits)
+    N, K, g = 4, 1024, 128
+    W = rng.normal(0, 0.02, (N, K))
+    Ex = rng.lognormal(0, 1, K)
+    idx, lut, a, b = oracle.kmeans_quantize(W, Ex, g, iters=10, nthreads=2, bits=bits)
+    A = workloads.bf16_bits_to_f64(a).repeat(g, axis=1)
+    B = workloads.bf16_bits_to_f64(b).repeat(g, axis=1)
+    ws = np.where(A != 0, (W - B) / np.where(A != 0, A, 1), 0)
+    Lq = workloads.bf16_bits_to_f64(lut)
+    assert np.all(lut[:, Q:] == 0) and idx.max() < Q
+    for n in range(N):
+        L, _, tr = oracle.kmeans_row(ws[n], A[n] * Ex, 10, trace=True, levels=Q)
+        assert np.all(np.diff(tr) <= 1e-9 * tr[0])
+        assert np.array_equal(lut[n, :Q], np.array([oracle.f64_to_bf16_scalar(v) for v in L]))
+        d = np.abs(ws[n][:, None] - Lq[n][None, :Q])
+        assert np.all(d[np.arange(K), idx[n]] <= d.min(axis=1))
