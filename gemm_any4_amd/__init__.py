@@ -66,7 +66,7 @@ def lib() -> ctypes.CDLL:
         L.any4_gemm_int4.restype = ctypes.c_int
         L.any4_gemm_int4.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
         L.any4_quantize.restype = ctypes.c_int
-        L.any4_quantize.argtypes = [P, P, P, P, P, P, I64, I64, I64, ctypes.c_int, P]
+        L.any4_quantize.argtypes = [P, P, P, P, P, P, I64, I64, I64, ctypes.c_int, ctypes.c_int, P]
         L.any4_status_string.restype = ctypes.c_char_p
         L.any4_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -149,9 +149,9 @@ def gemm_int4_raw(x_ptr, packed_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
 
 
 def quantize_raw(w_ptr, ex_ptr, idx_ptr, lut_ptr, alpha_ptr, beta_ptr, N, K, g, iters,
-                 stream=None) -> int:
+                 bits=4, stream=None) -> int:
     return lib().any4_quantize(w_ptr, ex_ptr, idx_ptr, lut_ptr, alpha_ptr, beta_ptr, N, K, g,
-                               iters, _stream(stream))
+                               iters, bits, _stream(stream))
 
 
 # --------------------------------------------------------------------------
@@ -267,8 +267,10 @@ def gemm_int4(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, beta: 
     return out
 
 
-def quantize(W: torch.Tensor, ex: torch.Tensor, g: int, iters: int = 10, stream=None):
-    """any4-quantise W fp32 [N, K] with channel importance ex fp32 [K] (E|x|).
+def quantize(W: torch.Tensor, ex: torch.Tensor, g: int, iters: int = 10, bits: int = 4,
+             stream=None):
+    """any4-quantise W fp32 [N, K] with channel importance ex fp32 [K] (E|x|);
+    bits = 3 or 2 for any3 / any2 (8 or 4 table values, indices below them).
 
     Returns (idx uint8 [N, K], lut bf16 [N, 16], alpha bf16 [N, K/g],
     beta bf16 [N, K/g]); pack idx with pack() before gemm()."""
@@ -287,5 +289,5 @@ def quantize(W: torch.Tensor, ex: torch.Tensor, g: int, iters: int = 10, stream=
     alpha = torch.empty((N, K // g), dtype=torch.bfloat16, device=dev)
     beta = torch.empty((N, K // g), dtype=torch.bfloat16, device=dev)
     check(quantize_raw(_ptr(W), _ptr(ex), _ptr(idx), _ptr(lut), _ptr(alpha), _ptr(beta), N, K, g,
-                       iters, stream))
+                       iters, bits, stream))
     return idx, lut, alpha, beta

@@ -1280,15 +1280,15 @@ __device__ __forceinline__ double bf16_to_f64(uint32_t h)
     return static_cast<double>(bf16_to_f32(h));
 }
 
-// index of the nearest of the 16 table values (ties: the lower index)
-__device__ __forceinline__ int nearest16(double v, const double (&L)[16])
+// index of the nearest of the first Q table values (ties: the lower index)
+__device__ __forceinline__ int nearest_q(double v, const double (&L)[16], int Q)
 {
     int best = 0;
     double bd = fabs(v - L[0]);
 #pragma unroll
     for (int q = 1; q < 16; ++q) {
         const double d = fabs(v - L[q]);
-        if (d < bd) {
+        if (q < Q && d < bd) {
             bd = d;
             best = q;
         }
@@ -1297,15 +1297,17 @@ __device__ __forceinline__ int nearest16(double v, const double (&L)[16])
 }
 
 // One thread per weight row, everything in binary64 and in the order below,
-// so that the result is a deterministic function of the inputs:
-//   1. per group of g weights: beta = bf16(min), alpha = bf16((max - min) / 15)
+// so that the result is a deterministic function of the inputs (Q = 16 table
+// values for any4, 8 for any3, 4 for any2):
+//   1. per group of g weights: beta = bf16(min), alpha = bf16((max - min) / (Q - 1))
 //   2. normalised weights ws = (w - beta) / alpha (0 where alpha = 0), their
 //      importance wt = alpha * ex[k]
-//   3. table L = 0, 1, .., 15; `iters` rounds of: every weight to its nearest
-//      table value, then L[q] = sum(wt * ws) / sum(wt) over the members of q
-//      in increasing k (products and sums rounded separately); empty
-//      clusters keep their value
-//   4. table stored in bf16; every weight assigned to the nearest stored value
+//   3. table L = 0, 1, .., Q-1; `iters` rounds of: every weight to its
+//      nearest table value, then L[q] = sum(wt * ws) / sum(wt) over the
+//      members of q in increasing k (products and sums rounded separately);
+//      empty clusters keep their value
+//   4. table stored in bf16 (entries from Q on: zero); every weight assigned
+//      to the nearest stored value
 // The per-thread sums live in LDS: [2][16][QT] doubles.
 constexpr int QT = 64;   // threads (rows) per workgroup
 
@@ -1315,7 +1317,7 @@ __global__ __launch_bounds__(QT) void k_quantize(const float* __restrict__ W,
                                                  uint16_t* __restrict__ lut,
                                                  uint16_t* __restrict__ alpha,
                                                  uint16_t* __restrict__ beta, int N, int K,
-                                                 int g, int iters)
+                                                 int g, int iters, int Q)
 {
     __shared__ double sums[2][16][QT];
     const int t = threadIdx.x;
@@ -1335,13 +1337,13 @@ __global__ __launch_bounds__(QT) void k_quantize(const float* __restrict__ W,
             hi = v > hi ? v : hi;
         }
         bn[j] = static_cast<uint16_t>(f64_to_bf16(lo));
-        an[j] = static_cast<uint16_t>(f64_to_bf16((hi - lo) / 15.0));
+        an[j] = static_cast<uint16_t>(f64_to_bf16((hi - lo) / static_cast<double>(Q - 1)));
     }
 
     double L[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q)
-        L[q] = q;
+        L[q] = q < Q ? q : 0;
     for (int it = 0; it < iters; ++it) {   // 3. weighted k-means
 #pragma unroll
         for (int q = 0; q < 16; ++q)
@@ -1352,21 +1354,21 @@ __global__ __launch_bounds__(QT) void k_quantize(const float* __restrict__ W,
             for (int k = j * g; k < (j + 1) * g; ++k) {
                 const double ws = al != 0.0 ? (static_cast<double>(row[k]) - be) / al : 0.0;
                 const double wt = __dmul_rn(al, static_cast<double>(ex[k]));
-                const int q = nearest16(ws, L);
+                const int q = nearest_q(ws, L, Q);
                 sums[0][q][t] = __dadd_rn(sums[0][q][t], __dmul_rn(wt, ws));
                 sums[1][q][t] = __dadd_rn(sums[1][q][t], wt);
             }
         }
 #pragma unroll
         for (int q = 0; q < 16; ++q)
-            if (sums[1][q][t] > 0.0)
+            if (q < Q && sums[1][q][t] > 0.0)
                 L[q] = sums[0][q][t] / sums[1][q][t];
     }
 
     double Lq[16];   // 4. the stored table and the final assignment
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-        const uint32_t h = f64_to_bf16(L[q]);
+        const uint32_t h = q < Q ? f64_to_bf16(L[q]) : 0u;
         lut[static_cast<size_t>(n) * 16 + q] = static_cast<uint16_t>(h);
         Lq[q] = bf16_to_f64(h);
     }
@@ -1376,7 +1378,7 @@ __global__ __launch_bounds__(QT) void k_quantize(const float* __restrict__ W,
         const double be = bf16_to_f64(bn[j]);
         for (int k = j * g; k < (j + 1) * g; ++k) {
             const double ws = al != 0.0 ? (static_cast<double>(row[k]) - be) / al : 0.0;
-            in[k] = static_cast<uint8_t>(nearest16(ws, Lq));
+            in[k] = static_cast<uint8_t>(nearest_q(ws, Lq, Q));
         }
     }
 }
@@ -1654,9 +1656,9 @@ any4_status any4_gemm_int4(const uint16_t* x, const uint8_t* packed, const uint1
 
 any4_status any4_quantize(const float* W, const float* ex, uint8_t* idx, uint16_t* lut,
                           uint16_t* alpha, uint16_t* beta, int64_t N, int64_t K, int64_t g,
-                          int iters, hipStream_t stream)
+                          int iters, int bits, hipStream_t stream)
 {
-    if (N < 0 || K < 0 || g <= 0 || K % g != 0 || iters < 0 ||
+    if (N < 0 || K < 0 || g <= 0 || K % g != 0 || iters < 0 || bits < 2 || bits > 4 ||
         static_cast<size_t>(N) * K >= (static_cast<size_t>(1) << 31))
         return ANY4_E_SHAPE;
     if (N == 0 || K == 0)
@@ -1669,7 +1671,7 @@ any4_status any4_quantize(const float* W, const float* ex, uint8_t* idx, uint16_
     (void)hipGetLastError();
     hipLaunchKernelGGL(k_quantize, dim3(static_cast<unsigned>((N + QT - 1) / QT)), dim3(QT), 0,
                        stream, W, ex, idx, lut, alpha, beta, static_cast<int>(N),
-                       static_cast<int>(K), static_cast<int>(g), iters);
+                       static_cast<int>(K), static_cast<int>(g), iters, 1 << bits);
     return launched();
 }
 

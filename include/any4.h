@@ -164,12 +164,16 @@ any4_status any4_gemm_int4(const uint16_t* x, const uint8_t* packed, const uint1
  * and beta arrays above (the explainer, section 二: step 1, group scaling and
  * the calibration statistic E|x|; step 2, the E-step / M-step iteration that
  * learns each row's 16 table values, weighting each weight by alpha * E|x|).
+ * bits = 3 or 2 gives any3 / any2 (the paper's abstract): Q = 8 or 4 table
+ * values instead of Q = 16, stored in the first Q entries of the 16-entry
+ * row (the rest zero), indices 0..Q-1, so such layers run through any4_pack,
+ * any4_dequant and any4_gemm unchanged (at 4 bits per stored index).
  * Per row, in binary64 and in this order:
- *   1. per group of g weights: beta = bf16(min), alpha = bf16((max - min) / 15)
- *      (the asymmetric range mapping that makes the start table 0..15 plain
- *      int4);
+ *   1. per group of g weights: beta = bf16(min), alpha = bf16((max - min) /
+ *      (Q - 1)) (the asymmetric range mapping that makes the start table
+ *      0..Q-1 the plain uniform grid);
  *   2. ws = (w - beta) / alpha (0 where alpha == 0), wt = alpha * ex[k];
- *   3. L = 0, 1, .., 15, then `iters` rounds of: assign every weight to its
+ *   3. L = 0, 1, .., Q-1, then `iters` rounds of: assign every weight to its
  *      nearest table value (ties: the lower index), then
  *      L[q] = sum(wt * ws) / sum(wt) over the members of q, summed in
  *      increasing k with products and sums rounded separately; a cluster
@@ -183,14 +187,14 @@ any4_status any4_gemm_int4(const uint16_t* x, const uint8_t* packed, const uint1
  *   idx    device, [N][K] uint8 (values 0..15), written; pack it with any4_pack.
  *   lut    device, [N][16] bf16, written.
  *   alpha, beta  device, [N][K/g] bf16, written.
- *   N >= 0, K >= 0, g > 0 with K % g == 0, iters >= 0, N*K < 2^31.
- *   N*K == 0 is a no-op.
+ *   N >= 0, K >= 0, g > 0 with K % g == 0, iters >= 0, bits in 2..4,
+ *   N*K < 2^31.  N*K == 0 is a no-op.
  * Errors: ANY4_E_SHAPE, ANY4_E_NULL, ANY4_E_ALIGN (W or ex not 4-byte aligned,
  * lut, alpha or beta not 2-byte aligned), ANY4_E_HIP.
  */
 any4_status any4_quantize(const float* W, const float* ex, uint8_t* idx, uint16_t* lut,
                           uint16_t* alpha, uint16_t* beta, int64_t N, int64_t K, int64_t g,
-                          int iters, hipStream_t stream);
+                          int iters, int bits, hipStream_t stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 const char* any4_status_string(any4_status s);

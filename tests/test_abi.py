@@ -119,6 +119,8 @@ def test_gemm_int4_errors():
 def test_quantize_errors():
     assert any4.quantize_raw(A, A, A, A, A, A, 4, 256, 96, 10, stream=0) == 2     # K % g
     assert any4.quantize_raw(A, A, A, A, A, A, 4, 256, 128, -1, stream=0) == 2    # iters
+    assert any4.quantize_raw(A, A, A, A, A, A, 4, 256, 128, 1, bits=1, stream=0) == 2
+    assert any4.quantize_raw(A, A, A, A, A, A, 4, 256, 128, 1, bits=5, stream=0) == 2
     assert any4.quantize_raw(A, A, A, A, A, A, -1, 256, 128, 1, stream=0) == 2
     assert any4.quantize_raw(A, None, A, A, A, A, 4, 256, 128, 1, stream=0) == 1
     assert any4.quantize_raw(A + 2, A, A, A, A, A, 4, 256, 128, 1, stream=0) == 3

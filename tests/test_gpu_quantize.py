@@ -1,4 +1,4 @@
-"""GPU parity of the any4 quantiser (any4_quantize) against the CPU oracle's
+"""GPU parity of the any4 quantiser (any4_quantize, also at 3 and 2 bits) against the CPU oracle's
 weighted k-means: the indices, tables, scales and offsets must be bit-identical
 (both sides work in binary64 in the same order), on small layers, on the
 degenerate cases (constant groups, a single round, no round), and on the first
@@ -22,12 +22,13 @@ def _gpu():
     any4.lib()
 
 
-def _quantize_both(W32, ex32, g, iters):
+def _quantize_both(W32, ex32, g, iters, bits=4):
     Wd = torch.from_numpy(W32).to(gu.DEV)
     exd = torch.from_numpy(ex32).to(gu.DEV)
-    idx, lut, a, b = any4.quantize(Wd, exd, g, iters)
+    idx, lut, a, b = any4.quantize(Wd, exd, g, iters, bits=bits)
     torch.cuda.synchronize()
-    ref = oracle.kmeans_quantize(W32.astype(np.float64), ex32.astype(np.float64), g, iters)
+    ref = oracle.kmeans_quantize(W32.astype(np.float64), ex32.astype(np.float64), g, iters,
+                                 bits=bits)
     got = (idx.cpu().numpy(), gu.host_b16(lut), gu.host_b16(a), gu.host_b16(b))
     return got, ref
 
@@ -91,3 +92,39 @@ def test_quantize_then_gemm():
     w_ref = oracle.dequant(oracle.pack(ridx), rlut, ra, rb, g)
     y_ref, ad = oracle.gemm(x, w_ref)
     gu.assert_within_bound(y, y_ref, ad, "quantise then gemm")
+
+
+@pytest.mark.parametrize("bits,N,K,g,iters", [(3, 100, 512, 128, 10), (2, 65, 1024, 256, 10),
+                                              (3, 33, 256, 128, 0), (2, 64, 8192, 128, 10)])
+def test_quantize_any3_any2_matches_oracle(bits, N, K, g, iters):
+    rng = np.random.default_rng(bits * 100 + N)
+    W = rng.normal(0.0, 0.02, size=(N, K))
+    W[rng.random((N, K)) < 0.001] *= 10.0
+    ex = rng.lognormal(0.0, 1.0, size=K)
+    got, ref = _quantize_both(W.astype(np.float32), ex.astype(np.float32), g, iters, bits)
+    _check(got, ref, f"any{bits} {N}x{K} g{g} iters{iters}")
+    assert got[0].max() < (1 << bits)
+
+
+@pytest.mark.parametrize("bits", [3, 2])
+def test_any3_any2_layer_through_gemm(bits):
+    """An any3 / any2 layer (indices below 8 / 4, table zero past them) runs
+    through pack, dequant and gemm: dequant bit-exact, gemm within the bound."""
+    rng = np.random.default_rng(50 + bits)
+    N, K, g = 300, 2048, 128
+    W = rng.normal(0.0, 0.02, size=(N, K)).astype(np.float32)
+    ex = rng.lognormal(0.0, 1.0, size=K).astype(np.float32)
+    idx, lut, a, b = any4.quantize(torch.from_numpy(W).to(gu.DEV), torch.from_numpy(ex).to(gu.DEV),
+                                   g, 10, bits=bits)
+    packed = any4.pack(idx)
+    ridx, rlut, ra, rb = oracle.kmeans_quantize(W.astype(np.float64), ex.astype(np.float64), g, 10,
+                                                bits=bits)
+    w_ref = oracle.dequant(oracle.pack(ridx), rlut, ra, rb, g)
+    w = any4.dequant(packed, lut, a, b, g)
+    x = workloads.to_bf16_bits(rng.standard_normal((16, K)))
+    for M in (1, 16):
+        y = any4.gemm(gu.dev_b16(x[:M]), packed, lut, a, b, g)
+        torch.cuda.synchronize()
+        y_ref, ad = oracle.gemm(x[:M], w_ref)
+        gu.assert_within_bound(y, y_ref, ad, f"any{bits} M={M}")
+    assert np.array_equal(gu.host_b16(w), w_ref)
