@@ -350,6 +350,9 @@ __device__ __forceinline__ void store_block(const f32x4_t* red, uint16_t* y, int
 //   [0, TABS)  pair tables: table b sits in 64 KB region b/2, half b%2, entry
 //              e at byte e*256 + (b%2)*128 + slot*4 (the x staging of the
 //              prologue and the partial sums of a group's end reuse it)
+//   ZERO       256 zero bytes at the start of the next 64 KB region: a dead
+//              tile (a chunk past K) reads its "table entries" here, so that
+//              an inf or NaN in a table entry no weight uses cannot reach y
 //   AB         [NBG][G <= 32][16 rows] (alpha | beta << 16) dwords
 //   LUTS       [NBG][16 rows][16] f16, each row scaled by 2^-s
 //   SCL        [NBG][16 rows] int: the row scale exponents s
@@ -362,8 +365,9 @@ constexpr int KM_MAX_BLK = 8;                        // row blocks per workgroup
 template <int NBG>
 struct KmCfg {
     static constexpr int TABS = ((NBG + 1) / 2) * 65536;
+    static constexpr int ZERO = TABS;   // 256 zero bytes: the table reads of dead tiles
     static constexpr int AB_BLK = KM_MAX_G * 16 * 4;
-    static constexpr int AB = TABS;
+    static constexpr int AB = ZERO + 256;
     static constexpr int LUTS = AB + NBG * AB_BLK;
     static constexpr int SCL = LUTS + NBG * 512;     // [NBG][16 rows] int: row scale exponents
     static constexpr int XS = SCL + NBG * 64;        // x as [M <= 2][K <= 4096] bf16
@@ -583,6 +587,8 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
 #pragma unroll
     for (int u = 0; u < R0; ++u)
         issue(0, u);
+    if (tid < 16)
+        lds_at<u32x4_t>(smem, Cfg::ZERO + tid * 16) = u32x4_t{0u, 0u, 0u, 0u};
     stage_store(lq, aq, bq);
     if constexpr (!XSTREAM) {
         // past x the region is zeroed: chunks past K read it (their weights
@@ -675,6 +681,9 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
                 const int s = u / NBG;
                 const int bb = u % NBG;
                 const u32x4_t p = pb[u % D];
+                // a chunk past K reads the zero zone instead of its table
+                const uint32_t sv =
+                    s1[bb >> 1] + (cbase + s < Kc ? 0u : Cfg::ZERO - (bb >> 1) * 65536u);
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4) {
                     if constexpr (I4) {
@@ -683,7 +692,7 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
 #pragma unroll
                         for (int jb = 0; jb < 4; ++jb)
                             bw[h][s4][jb] = lds_at<uint32_t>(
-                                smem, __builtin_amdgcn_perm(p[s4], s1[bb >> 1],
+                                smem, __builtin_amdgcn_perm(p[s4], sv,
                                                             0x0C020000u | ((4u + jb) << 8)) +
                                           (bb & 1) * 128);
                     }
@@ -787,8 +796,9 @@ template <int NBG, bool XL>
 struct KbCfg {
     static constexpr int GMAX = NBG == 1 ? 512 : NBG == 2 ? 256 : NBG == 3 ? 144 : 112;
     static constexpr int TABS = ((NBG + 1) / 2) * 65536;
+    static constexpr int ZERO = TABS;   // 256 zero bytes: the table reads of dead tiles
     static constexpr int AB_BLK = GMAX * 16 * 4;
-    static constexpr int AB = TABS;
+    static constexpr int AB = ZERO + 256;
     static constexpr int LUTS = AB + NBG * AB_BLK;
     static constexpr int SCL = LUTS + NBG * 512;
     static constexpr int XS = SCL + NBG * 64;
@@ -945,6 +955,8 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
 #pragma unroll
     for (int u = 0; u < R0; ++u)
         issue(0, 0, u);
+    if (tid < 16)
+        lds_at<u32x4_t>(smem, Cfg::ZERO + tid * 16) = u32x4_t{0u, 0u, 0u, 0u};
     stage_store(lq, aq, bq);
     if constexpr (XL) {
         // past x the region is zeroed (see k_gemm_km)
@@ -1040,18 +1052,21 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
                 const int st = sc + u / NBG;
                 const int bb = u % NBG;
                 const u32x4_t p = pb[u];
+                const int c = cbase + st;
+                const bool live = gc * NBG + bb < nblk && st < C && c < Kc;
                 if constexpr (!I4) {
+                    // a dead tile reads the zero zone instead of its table
+                    const uint32_t sv =
+                        s1[bb >> 1] + (live ? 0u : Cfg::ZERO - (bb >> 1) * 65536u);
 #pragma unroll
                     for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
                         for (int jb = 0; jb < 4; ++jb)
                             bw[h][s4][jb] = lds_at<uint32_t>(
-                                smem, __builtin_amdgcn_perm(p[s4], s1[bb >> 1],
+                                smem, __builtin_amdgcn_perm(p[s4], sv,
                                                             0x0C020000u | ((4u + jb) << 8)) +
                                           (bb & 1) * 128);
                 }
-                const int c = cbase + st;
-                const bool live = gc * NBG + bb < nblk && st < C && c < Kc;
                 const int grp =
                     min(static_cast<int>((static_cast<float>(c) + 0.5f) * inv_gc), G - 1);
                 const uint32_t pr =

@@ -362,6 +362,24 @@ def test_constant_table_rank1():
     gu.assert_within_bound(y, closed, ad, "rank-1")
 
 
+@pytest.mark.parametrize("M,N,K,g", [(1, 40, 512, 128), (16, 33, 1536, 128), (2, 20, 128 * 113, 128),
+                                     (5, 17, 128 * 41, 128)])
+def test_unused_non_finite_table_entry(M, N, K, g):
+    """A table entry no weight uses may be inf or NaN: the product is still the
+    finite oracle product (shapes with chunks past K in some waves)."""
+    inp = workloads.generic(M + N + K, M, N, K, g)
+    idx = np.maximum(inp.idx, 1)                      # entry 0 is never used
+    lut = inp.lut.copy()
+    lut[:, 0] = 0x7F80                                 # +inf
+    lut[1::2, 0] = 0x7FC0                              # NaN on odd rows
+    L = gu.Layer(workloads.Any4Inputs(N, K, g, idx, lut, inp.alpha, inp.beta, inp.x))
+    y = any4.gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all()
+    y_ref, ad = oracle.gemm(inp.x, L.w_ref())
+    gu.assert_within_bound(y, y_ref, ad, f"non-finite unused entry {M}x{N}x{K}")
+
+
 def test_zero_x_gives_exact_zero():
     L = gu.config_layer(0)
     x = torch.zeros((16, L.K), dtype=torch.bfloat16, device=gu.DEV)
