@@ -23,7 +23,8 @@ M=16, under "other_layers"; and for both layers with plain int4 weights
 (any4_gemm_int4 on the same codes, scales and offsets, no table), under
 "int4_no_table", which puts a number on what the table lookup costs; and
 at prefill batches M = 64, 256, 1024 on the up/gate layer (TFLOP/s against
-the bf16 matrix peak), under "prefill".
+the bf16 matrix peak), under "prefill"; and the GPU quantiser on a 4096x4096
+layer at 4, 3 and 2 bits, under "quantize".
 
 Prints one JSON line.  --traffic-probe instead runs a few launches of each M
 plus a device copy of known size, for hardware-counter collection.
@@ -202,6 +203,28 @@ def prefill(torch, any4, workloads, Ms) -> dict:
     return out
 
 
+def quantize_timing(torch, any4, N: int, K: int, g: int, iters: int = 10) -> dict:
+    """ms of any4_quantize (group scale + 10 rounds of weighted k-means, one
+    GPU thread per row) on an N x K layer, for 4, 3 and 2 bits."""
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    dev = torch.device("cuda:0")
+    W = (torch.randn(N, K, generator=gen) * 0.02).to(dev)
+    ex = torch.rand(K, generator=gen).add_(0.5).to(dev)
+    out = {"N": N, "K": K, "g": g, "iters": iters}
+    for bits in (4, 3, 2):
+        any4.quantize(W, ex, g, iters, bits=bits)   # warm
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        st = torch.cuda.current_stream()
+        e0.record(st)
+        any4.quantize(W, ex, g, iters, bits=bits)
+        e1.record(st)
+        torch.cuda.synchronize()
+        out[f"any{bits}_ms"] = e0.elapsed_time(e1)
+    return out
+
+
 def _graph(torch, launch, steps: int, Ms):
     """Record `steps` steps of launches (one per M in Ms) in a HIP graph."""
     s = torch.cuda.Stream()
@@ -348,6 +371,7 @@ def main() -> int:
                                 for c in (2, 3)}
     if not args.no_other_layers:
         out["prefill"] = prefill(torch, any4, workloads, (64, 256, 1024))
+        out["quantize"] = quantize_timing(torch, any4, 4096, 4096, 128)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
