@@ -23,7 +23,8 @@ M=16, under "other_layers"; and for both layers with plain int4 weights
 (any4_gemm_int4 on the same codes, scales and offsets, no table), under
 "int4_no_table", which puts a number on what the table lookup costs; and
 at prefill batches M = 64, 256, 1024 on the up/gate layer (TFLOP/s against
-the bf16 matrix peak), under "prefill"; and the GPU quantiser on a 4096x4096
+the bf16 matrix peak), under "prefill"; both layers with the codes taken to
+2 bits through any2_gemm, under "any2"; and the GPU quantiser on a 4096x4096
 layer at 4, 3 and 2 bits, under "quantize".
 
 Prints one JSON line.  --traffic-probe instead runs a few launches of each M
@@ -164,6 +165,49 @@ def other_layer(torch, any4, workloads, cfg: int, steps: int, int4: bool = False
         bts = algorithmic_bytes(M, c.N, c.K, c.g)
         out[str(M)] = {"us_per_launch": us, "bytes": bts,
                        "tbps": bts / (us * 1e-6) / 1e12,
+                       "pct_hbm_peak": 100.0 * bts / (us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+        del g
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
+def any2_layer(torch, any4, workloads, cfg: int, steps: int) -> dict:
+    """Per-launch µs of any2_gemm on config `cfg`'s layer with the codes taken
+    to 2 bits (idx & 3, packed four to a byte), rotating weight sets, graph
+    replays; bytes are the any2 algorithmic bytes (N*K/4 for the codes)."""
+    import numpy as np
+
+    c = workloads.CONFIGS[cfg]
+    dev = torch.device("cuda:0")
+    inp = workloads.generate(cfg)
+    wb = c.N * c.K // 4 + 4 * c.N * (c.K // c.g) + 32 * c.N
+    R = max(2, math.ceil(2 * CACHE_BYTES / wb) + 1)
+
+    def b16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
+            torch.bfloat16)
+
+    codes = torch.from_numpy(inp.idx & 3).to(dev)
+    p0 = any4.any2_pack(codes)
+    del codes
+    sets = [(p0.clone(), b16(inp.lut), b16(inp.alpha), b16(inp.beta)) for _ in range(R)]
+    x = b16(inp.x)
+    ys = {M: torch.empty((M, c.N), dtype=torch.bfloat16, device=dev) for M in MS}
+
+    def launch(i: int, M: int):
+        p, l, a, b = sets[i % R]
+        any4.any2_gemm(x[:M], p, l, a, b, c.g, out=ys[M])
+
+    out = {"N": c.N, "K": c.K, "g": c.g, "rotating_weight_sets": R}
+    for M in MS:
+        for i in range(5):
+            launch(i, M)
+        g = _graph(torch, launch, steps, (M,))
+        _time_graph(torch, g)
+        us = float(np.median([_time_graph(torch, g) * 1e3 / steps for _ in range(3)]))
+        bts = wb + 2 * M * c.K + 2 * M * c.N
+        out[str(M)] = {"us_per_launch": us, "bytes": bts, "tbps": bts / (us * 1e-6) / 1e12,
                        "pct_hbm_peak": 100.0 * bts / (us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
         del g
     del sets
@@ -370,6 +414,8 @@ def main() -> int:
                                                           min(K, 100), int4=True)
                                 for c in (2, 3)}
     if not args.no_other_layers:
+        out["any2"] = {f"config{c}": any2_layer(torch, any4, workloads, c, min(K, 100))
+                       for c in (2, 3)}
         out["prefill"] = prefill(torch, any4, workloads, (64, 256, 1024))
         out["quantize"] = quantize_timing(torch, any4, 4096, 4096, 128)
     if not args.no_cpu_baseline:

@@ -63,6 +63,13 @@ __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t off
 }
 
 // The same with the non-temporal hint, for data read exactly once (weights).
+// the 8 bytes of an any2 tile slot, non-temporal, in the low half of a u32x4
+__device__ __forceinline__ u32x4_t load8_nt(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 2);
+    return u32x4_t{v[0], v[1], 0u, 0u};
+}
 __device__ __forceinline__ u32x4_t load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
@@ -160,6 +167,93 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void k_dequant(const uint8_t* __rest
         dst[q] = out[q];
 }
 
+// ---- any2 (2-bit codes) -----------------------------------------------------
+// Tiles of 16 rows x 128 k, 512 bytes: byte 8l + i of tile (b, c) holds row
+// 16b + l%16, codes k = 128c + 32(l/16) + 4i .. +3 in bits 0-1, 2-3, 4-5, 6-7.
+// One 8-byte slot per lane of a wave64; each slot is exactly the 32 k of the
+// lane's four MFMA B operands.
+__global__ __launch_bounds__(PACK_THREADS) void k_pack2(const uint8_t* __restrict__ idx,
+                                                        uint8_t* __restrict__ packed, int N,
+                                                        int K, uint32_t slots)
+{
+    const uint32_t sidx = blockIdx.x * PACK_THREADS + threadIdx.x;   // 8-byte slot
+    if (sidx >= slots)
+        return;
+    const int Kc = K / TILE_K;
+    const uint32_t tile = sidx / 64;
+    const int l = static_cast<int>(sidx % 64);
+    const int b = static_cast<int>(tile / Kc);
+    const int c = static_cast<int>(tile % Kc);
+    const int n = b * TILE_ROWS + (l & 15);
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    u32x2_t out = {0u, 0u};
+    if (n < N) {
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
+            idx + static_cast<size_t>(n) * K + c * TILE_K + (l >> 4) * 32);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const u32x4_t v = src[h];   // 16 codes, one per byte
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t w = v[q] & 0x03030303u;   // codes 4q' .. 4q'+3 of this dword
+                const uint32_t byte = (w & 3u) | ((w >> 6) & 0xCu) | ((w >> 12) & 0x30u) |
+                                      ((w >> 18) & 0xC0u);
+                out[h] |= byte << (8 * q);
+            }
+        }
+    }
+    *reinterpret_cast<u32x2_t*>(packed + static_cast<size_t>(sidx) * 8) = out;
+}
+
+__global__ __launch_bounds__(64 * DQ_WAVES) void k_dequant2(const uint8_t* __restrict__ packed,
+                                                           const uint16_t* __restrict__ lut,
+                                                           const uint16_t* __restrict__ alpha,
+                                                           const uint16_t* __restrict__ beta,
+                                                           uint16_t* __restrict__ w, int N, int K,
+                                                           int g)
+{
+    __shared__ float sl[TILE_ROWS * 4];
+    const int Kc = K / TILE_K;
+    const int cgroups = (Kc + DQ_WAVES - 1) / DQ_WAVES;
+    const int b = blockIdx.x / cgroups;
+    const int c = (blockIdx.x % cgroups) * DQ_WAVES + (threadIdx.x >> 6);
+    if (threadIdx.x < TILE_ROWS * 4) {   // row t/4, entry t%4
+        const int t = threadIdx.x;
+        const int n = b * TILE_ROWS + (t >> 2);
+        sl[t] = n < N ? bf16_to_f32(lut[static_cast<size_t>(n) * 16 + (t & 3)]) : 0.f;
+    }
+    __syncthreads();
+    const int l = threadIdx.x & 63;
+    const int j = l & 15;
+    const int n = b * TILE_ROWS + j;
+    if (c >= Kc || n >= N)
+        return;
+    const int k0 = c * TILE_K + (l >> 4) * 32;
+    const int G = K / g;
+    const float a = bf16_to_f32(alpha[static_cast<size_t>(n) * G + k0 / g]);
+    const float bt = bf16_to_f32(beta[static_cast<size_t>(n) * G + k0 / g]);
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t p = *reinterpret_cast<const u32x2_t*>(
+        packed + (static_cast<size_t>(b) * Kc + c) * (TILE_BYTES / 2) + l * 8);
+    const float* L = sl + j * 4;
+    u32x4_t out[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {   // byte i: codes 4i .. 4i+3
+        const uint32_t byte = (p[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const float lo = fmaf(a, L[(byte >> (4 * t)) & 3u], bt);
+            const float hi = fmaf(a, L[(byte >> (4 * t + 2)) & 3u], bt);
+            const int d = 2 * i + t;
+            out[d >> 2][d & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+        }
+    }
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(w + static_cast<size_t>(n) * K + k0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        dst[q] = out[q];
+}
+
 // ---------------------------------------------------------------------------
 // gemm
 // ---------------------------------------------------------------------------
@@ -202,6 +296,14 @@ __global__ __launch_bounds__(256) void k_zero(uint16_t* __restrict__ y, size_t n
 // loop bodies are straight-line apart from uniform branches, so the ring
 // survives the loop.
 constexpr int GW = 8;                   // waves per workgroup
+
+// Weight formats of the GEMM kernels: the any4 table path, plain int4 (the
+// code is the value), and any2 (2-bit codes, four per byte, 512-byte tiles;
+// a byte looks up four table values at once).
+constexpr int FMT_ANY4 = 0;
+constexpr int FMT_INT4 = 1;
+constexpr int FMT_ANY2 = 2;
+constexpr int tile_bytes(int fmt) { return fmt == FMT_ANY2 ? TILE_BYTES / 2 : TILE_BYTES; }
 constexpr int GT = 64 * GW;
 constexpr int TAB_BYTES = 256 * 256;    // 256 entries x 2 tables x 32 slots x 4 B
 constexpr int MAX_G = 512;              // K/g: the alpha/beta staging of k_gemm_kb
@@ -263,6 +365,35 @@ __device__ __forceinline__ void build_table(uint8_t* smem, uint32_t lut_off, uin
                     v = Lw[q];
             tw[hi * 16 * 64] = __builtin_amdgcn_perm(v, ll, (hi & 1) ? 0x07060100u : 0x05040100u);
         }
+    }
+}
+
+// any2: the quad table of one row block.  Entry e (a byte of four 2-bit codes
+// c_s = (e >> 2s) & 3) holds (L[c0] | L[c1] << 16, L[c2] | L[c3] << 16): the
+// two B-operand dwords of those four weights.  16 slots per entry (slot =
+// row), 8 bytes each: entry e at byte e*256 (+128 for the second table of a
+// 64 KB region) + slot*8, so one 64-bit read decodes four weights.  Thread t
+// of the W*64 writes slot t % 16 of entries t / 16 + (64*W/16)*i.
+template <int W>
+__device__ __forceinline__ void build_table2(uint8_t* smem, uint32_t lut_off, uint32_t tab_off,
+                                             int tid)
+{
+    constexpr int EPT = 256 * 16 / (64 * W);   // entries per thread
+    const int st = tid & 15;
+    const uint32_t row = lut_off + st * 32;
+    const uint32_t A = lds_at<uint32_t>(smem, row);       // L0 | L1 << 16
+    const uint32_t B = lds_at<uint32_t>(smem, row + 4);   // L2 | L3 << 16
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const uint32_t e = static_cast<uint32_t>(tid >> 4) + i * (64 * W / 16);
+        // byte selector of v_perm(B, A): bytes 0-3 are A's, 4-7 are B's
+        auto sel = [](uint32_t qa, uint32_t qb) {
+            return (2 * qa) | ((2 * qa + 1) << 8) | ((2 * qb) << 16) | ((2 * qb + 1) << 24);
+        };
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t v = {__builtin_amdgcn_perm(B, A, sel(e & 3, (e >> 2) & 3)),
+                           __builtin_amdgcn_perm(B, A, sel((e >> 4) & 3, e >> 6))};
+        lds_at<u32x2_t>(smem, tab_off + e * 256 + st * 8) = v;
     }
 }
 
@@ -460,9 +591,12 @@ __device__ __forceinline__ u32x4_t deq_quad(const u32x4_t& q, float a, float b)
                    deq_pair(q[3], a, b)};
 }
 
-template <int MT, int NBG, bool I4>
+template <int MT, int NBG, int FMT>
 __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
 {
+    constexpr bool I4 = FMT == FMT_INT4;
+    constexpr bool A2 = FMT == FMT_ANY2;
+    constexpr uint32_t TB = tile_bytes(FMT);
     using Cfg = KmCfg<NBG>;
     constexpr int C = KM_C;
     constexpr int GS = Cfg::GS;
@@ -488,7 +622,7 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
     const int cbase = wave * C;
 
     const __amdgpu_buffer_rsrc_t rp =
-        make_rsrc(args.packed, static_cast<uint32_t>(NB) * Kc * TILE_BYTES);
+        make_rsrc(args.packed, static_cast<uint32_t>(NB) * Kc * TB);
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(args.lut, static_cast<uint32_t>(N) * 32);
     // alpha/beta are read with 16-byte loads: the range is rounded up to 16 B
     // (the 16-byte granule holding a valid byte never leaves that byte's page
@@ -535,7 +669,9 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
         }
     };
     auto build = [&](int bb) {
-        if constexpr (!I4)
+        if constexpr (A2)
+            build_table2<GW>(smem, Cfg::LUTS + bb * 512, (bb >> 1) * 65536 + (bb & 1) * 128, tid);
+        else if constexpr (!I4)
             build_table<GW>(smem, Cfg::LUTS + bb * 512, (bb >> 1) * 16384 + (bb & 1) * 32, tid);
     };
 
@@ -544,7 +680,7 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
     // XSTREAM, the x operands of chunk s of a group follow its first tile
     u32x4_t pb[D];
     u32x4_t xq[XSTREAM ? DS : 1][4];
-    const uint32_t tile_lane = static_cast<uint32_t>(lane) * 16;
+    const uint32_t tile_lane = static_cast<uint32_t>(lane) * (TB / 64);
     const uint32_t x_lane = j < M ? static_cast<uint32_t>(j * K + kq * 32) * 2 : OOR;
     auto issue = [&](int gi, int uu) {
         const int gg = gi + uu / GS;
@@ -555,9 +691,9 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
         // computed unconditionally and pushed out of range with one OR: a
         // select here would become a branch around the load
         const uint32_t uo =
-            (static_cast<uint32_t>(r + blk * Gs) * static_cast<uint32_t>(Kc) + c) * TILE_BYTES |
+            (static_cast<uint32_t>(r + blk * Gs) * static_cast<uint32_t>(Kc) + c) * TB |
             (static_cast<uint32_t>(!live) << 31);
-        pb[uu % D] = load16_nt(rp, off2(tile_lane, uo));
+        pb[uu % D] = A2 ? load8_nt(rp, off2(tile_lane, uo)) : load16_nt(rp, off2(tile_lane, uo));
         if constexpr (XSTREAM) {
             if (v % NBG == NBG - 1) {
                 const bool xl = gg < ngroups && c < Kc;
@@ -612,7 +748,8 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
     }
     __syncthreads();
 
-    const uint32_t slot4 = static_cast<uint32_t>(lane & 31) * 4;
+    // the lane's slot in a table entry (any2: 16 slots of 8 bytes)
+    const uint32_t slot4 = A2 ? static_cast<uint32_t>(lane & 15) * 8 : static_cast<uint32_t>(lane & 31) * 4;
     const uint32_t s1[2] = {slot4, slot4 | 0x10000u};   // region 0 / region 1
     uint32_t ab_c[C];   // LDS offset of this lane's (alpha, beta) pair, block 0
 #pragma unroll
@@ -688,6 +825,19 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
                 for (int s4 = 0; s4 < 4; ++s4) {
                     if constexpr (I4) {
                         bw[h][s4] = u32x4_t{p[s4], 0u, 0u, 0u};   // decoded later
+                    } else if constexpr (A2) {
+                        // bytes 2*s4 and 2*s4+1: four weights each, one 64-bit read
+                        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            const int bi = 2 * s4 + t;
+                            const u32x2_t q = lds_at<u32x2_t>(
+                                smem, __builtin_amdgcn_perm(p[bi >> 2], sv,
+                                                            0x0C020000u | ((4u + (bi & 3)) << 8)) +
+                                          (bb & 1) * 128);
+                            bw[h][s4][2 * t] = q[0];
+                            bw[h][s4][2 * t + 1] = q[1];
+                        }
                     } else {
 #pragma unroll
                         for (int jb = 0; jb < 4; ++jb)
@@ -812,9 +962,12 @@ struct KbCfg {
     static_assert(LDS <= 160 * 1024, "LDS of one CU");
 };
 
-template <int MT, int NBG, bool XL, bool I4>
+template <int MT, int NBG, bool XL, int FMT>
 __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
 {
+    constexpr bool I4 = FMT == FMT_INT4;
+    constexpr bool A2 = FMT == FMT_ANY2;
+    constexpr uint32_t TB = tile_bytes(FMT);
     using Cfg = KbCfg<NBG, XL>;
     constexpr int DS = Cfg::DS;
     constexpr int D = Cfg::D;
@@ -840,7 +993,7 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
     const float inv_gc = 1.0f / static_cast<float>(g / TILE_K);   // chunk -> group
 
     const __amdgpu_buffer_rsrc_t rp =
-        make_rsrc(args.packed, static_cast<uint32_t>(NB) * Kc * TILE_BYTES);
+        make_rsrc(args.packed, static_cast<uint32_t>(NB) * Kc * TB);
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(args.lut, static_cast<uint32_t>(N) * 32);
     // alpha/beta are read with 16-byte loads: the range is rounded up to 16 B
     // (the 16-byte granule holding a valid byte never leaves that byte's page
@@ -903,7 +1056,9 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
                 store_pairs(smem, Cfg::AB + ab_blk[h] * Cfg::AB_BLK, ab_pc[h], G, aq[h], bq[h]);
     };
     auto build = [&](int bb) {
-        if constexpr (!I4)
+        if constexpr (A2)
+            build_table2<GW>(smem, Cfg::LUTS + bb * 512, (bb >> 1) * 65536 + (bb & 1) * 128, tid);
+        else if constexpr (!I4)
             build_table<GW>(smem, Cfg::LUTS + bb * 512, (bb >> 1) * 16384 + (bb & 1) * 32, tid);
     };
 
@@ -912,7 +1067,7 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
     // group's CP steps the sequence continues with the next group.
     u32x4_t pb[D];
     u32x4_t xq[XL ? 1 : DS][4];
-    const uint32_t tile_lane = static_cast<uint32_t>(lane) * 16;
+    const uint32_t tile_lane = static_cast<uint32_t>(lane) * (TB / 64);
     const uint32_t x_lane = j < M ? static_cast<uint32_t>(j * K + kq * 32) * 2 : OOR;
     auto issue = [&](int gc, int sc, int uu) {
         int st = sc + uu / NBG;
@@ -926,9 +1081,9 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
         const int c = cbase + st;
         const bool live = blk < nblk && st < C && c < Kc;
         const uint32_t uo =
-            (static_cast<uint32_t>(r + blk * Gs) * static_cast<uint32_t>(Kc) + c) * TILE_BYTES |
+            (static_cast<uint32_t>(r + blk * Gs) * static_cast<uint32_t>(Kc) + c) * TB |
             (static_cast<uint32_t>(!live) << 31);
-        pb[uu % D] = load16_nt(rp, off2(tile_lane, uo));
+        pb[uu % D] = A2 ? load8_nt(rp, off2(tile_lane, uo)) : load16_nt(rp, off2(tile_lane, uo));
         if (!XL && bb == NBG - 1) {
             const bool xl = gg < ngroups && st < C && c < Kc;
             const uint32_t xc =
@@ -979,7 +1134,8 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
     }
     __syncthreads();
 
-    const uint32_t slot4 = static_cast<uint32_t>(lane & 31) * 4;
+    // the lane's slot in a table entry (any2: 16 slots of 8 bytes)
+    const uint32_t slot4 = A2 ? static_cast<uint32_t>(lane & 15) * 8 : static_cast<uint32_t>(lane & 31) * 4;
     const uint32_t s1[2] = {slot4, slot4 | 0x10000u};   // region 0 / region 1
     f32x4_t acc[NBG][NA];
 #pragma unroll
@@ -1058,14 +1214,27 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
                     // a dead tile reads the zero zone instead of its table
                     const uint32_t sv =
                         s1[bb >> 1] + (live ? 0u : Cfg::ZERO - (bb >> 1) * 65536u);
+                    if constexpr (A2) {
+                        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4)
-#pragma unroll
-                        for (int jb = 0; jb < 4; ++jb)
-                            bw[h][s4][jb] = lds_at<uint32_t>(
-                                smem, __builtin_amdgcn_perm(p[s4], sv,
-                                                            0x0C020000u | ((4u + jb) << 8)) +
+                        for (int bi = 0; bi < 8; ++bi) {   // four weights per byte
+                            const u32x2_t q = lds_at<u32x2_t>(
+                                smem, __builtin_amdgcn_perm(p[bi >> 2], sv,
+                                                            0x0C020000u | ((4u + (bi & 3)) << 8)) +
                                           (bb & 1) * 128);
+                            bw[h][bi >> 1][2 * (bi & 1)] = q[0];
+                            bw[h][bi >> 1][2 * (bi & 1) + 1] = q[1];
+                        }
+                    } else {
+#pragma unroll
+                        for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                            for (int jb = 0; jb < 4; ++jb)
+                                bw[h][s4][jb] = lds_at<uint32_t>(
+                                    smem, __builtin_amdgcn_perm(p[s4], sv,
+                                                                0x0C020000u | ((4u + jb) << 8)) +
+                                              (bb & 1) * 128);
+                    }
                 }
                 const int grp =
                     min(static_cast<int>((static_cast<float>(c) + 0.5f) * inv_gc), G - 1);
@@ -1139,9 +1308,10 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
 constexpr int BIG_BN = 64;
 constexpr int BIG_LD = TILE_K + 8;   // padded row length in bf16
 
-template <int BM>
+template <int BM, bool A2>
 __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
 {
+    constexpr uint32_t TB = A2 ? TILE_BYTES / 2 : TILE_BYTES;
     constexpr int MTW = BM / 32;   // 16-row m tiles per wave (the wave's BM/2 rows)
     __shared__ __attribute__((aligned(16))) uint16_t xs[BM * BIG_LD];
     __shared__ __attribute__((aligned(16))) uint16_t ws[BIG_BN * BIG_LD];
@@ -1191,8 +1361,14 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
     auto fetch = [&](int c) {
         if (wlive) {
             const int k0 = c * TILE_K + wk;
-            pk = *reinterpret_cast<const u32x4_t*>(
-                args.packed + (static_cast<size_t>(blk) * Kc + c) * TILE_BYTES + lane * 16);
+            const uint8_t* src = args.packed + (static_cast<size_t>(blk) * Kc + c) * TB + lane * (TB / 64);
+            if constexpr (A2) {
+                typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+                const u32x2_t v = *reinterpret_cast<const u32x2_t*>(src);
+                pk = u32x4_t{v[0], v[1], 0u, 0u};
+            } else {
+                pk = *reinterpret_cast<const u32x4_t*>(src);
+            }
             ab = args.alpha[static_cast<size_t>(wn) * G + k0 / g] |
                  (static_cast<uint32_t>(args.beta[static_cast<size_t>(wn) * G + k0 / g]) << 16);
         }
@@ -1216,12 +1392,26 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
                 const float a = bf16_to_f32(ab & 0xFFFFu);
                 const float bt = bf16_to_f32(ab >> 16);
                 const float* L = lt + wrow * 16;
+                if constexpr (A2) {   // 8 bytes of four 2-bit codes: dwords 2i, 2i+1
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const uint32_t byte = (pk[q >> 2] >> (8 * (q & 3))) & 0xFFu;
-                    const float lo = fmaf(a, L[byte & 15u], bt);
-                    const float hi = fmaf(a, L[byte >> 4], bt);
-                    out[q >> 2][q & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+                    for (int i = 0; i < 8; ++i) {
+                        const uint32_t byte = (pk[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            const float lo = fmaf(a, L[(byte >> (4 * t)) & 3u], bt);
+                            const float hi = fmaf(a, L[(byte >> (4 * t + 2)) & 3u], bt);
+                            const int d = 2 * i + t;
+                            out[d >> 2][d & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const uint32_t byte = (pk[q >> 2] >> (8 * (q & 3))) & 0xFFu;
+                        const float lo = fmaf(a, L[byte & 15u], bt);
+                        const float hi = fmaf(a, L[byte >> 4], bt);
+                        out[q >> 2][q & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+                    }
                 }
             }
             u32x4_t* dst = reinterpret_cast<u32x4_t*>(ws + wrow * BIG_LD + wk);
@@ -1423,7 +1613,7 @@ any4_status launched()
 
 constexpr int KM_GRID = 256;   // one workgroup per CU of an MI355X
 
-template <int MT, bool I4>
+template <int MT, int FMT>
 void launch_gemm(const GemmArgs& a, hipStream_t stream)
 {
     const int64_t NB = row_blocks(a.N);
@@ -1436,13 +1626,13 @@ void launch_gemm(const GemmArgs& a, hipStream_t stream)
     const dim3 gd(static_cast<unsigned>(grid));
     if (a.K <= KM_MAX_K) {
         if (nbg == 1)
-            hipLaunchKernelGGL((k_gemm_km<MT, 1, I4>), gd, dim3(GT), 0, stream, a);
+            hipLaunchKernelGGL((k_gemm_km<MT, 1, FMT>), gd, dim3(GT), 0, stream, a);
         else if (nbg == 2)
-            hipLaunchKernelGGL((k_gemm_km<MT, 2, I4>), gd, dim3(GT), 0, stream, a);
+            hipLaunchKernelGGL((k_gemm_km<MT, 2, FMT>), gd, dim3(GT), 0, stream, a);
         else if (nbg == 3)
-            hipLaunchKernelGGL((k_gemm_km<MT, 3, I4>), gd, dim3(GT), 0, stream, a);
+            hipLaunchKernelGGL((k_gemm_km<MT, 3, FMT>), gd, dim3(GT), 0, stream, a);
         else
-            hipLaunchKernelGGL((k_gemm_km<MT, 4, I4>), gd, dim3(GT), 0, stream, a);
+            hipLaunchKernelGGL((k_gemm_km<MT, 4, FMT>), gd, dim3(GT), 0, stream, a);
         return;
     }
     // alpha/beta of a group must fit the LDS staging of k_gemm_kb
@@ -1456,58 +1646,57 @@ void launch_gemm(const GemmArgs& a, hipStream_t stream)
     if (xl) {
         if constexpr (MT <= 2) {
             if (nbg == 1)
-                hipLaunchKernelGGL((k_gemm_kb<MT, 1, true, I4>), gd, dim3(GT), 0, stream, a);
+                hipLaunchKernelGGL((k_gemm_kb<MT, 1, true, FMT>), gd, dim3(GT), 0, stream, a);
             else
-                hipLaunchKernelGGL((k_gemm_kb<MT, 2, true, I4>), gd, dim3(GT), 0, stream, a);
+                hipLaunchKernelGGL((k_gemm_kb<MT, 2, true, FMT>), gd, dim3(GT), 0, stream, a);
         }
         return;
     }
     if (nbg == 1)
-        hipLaunchKernelGGL((k_gemm_kb<MT, 1, false, I4>), gd, dim3(GT), 0, stream, a);
+        hipLaunchKernelGGL((k_gemm_kb<MT, 1, false, FMT>), gd, dim3(GT), 0, stream, a);
     else if (nbg == 2)
-        hipLaunchKernelGGL((k_gemm_kb<MT, 2, false, I4>), gd, dim3(GT), 0, stream, a);
+        hipLaunchKernelGGL((k_gemm_kb<MT, 2, false, FMT>), gd, dim3(GT), 0, stream, a);
     else if (nbg == 3)
-        hipLaunchKernelGGL((k_gemm_kb<MT, 3, false, I4>), gd, dim3(GT), 0, stream, a);
+        hipLaunchKernelGGL((k_gemm_kb<MT, 3, false, FMT>), gd, dim3(GT), 0, stream, a);
     else
-        hipLaunchKernelGGL((k_gemm_kb<MT, 4, false, I4>), gd, dim3(GT), 0, stream, a);
+        hipLaunchKernelGGL((k_gemm_kb<MT, 4, false, FMT>), gd, dim3(GT), 0, stream, a);
 }
 
 }  // namespace
 
 // M = 1..16: the streaming kernels, instantiated for 1, 2, 4, 8 and 16 rows
-static void launch_decode(const GemmArgs& a, bool i4, hipStream_t stream)
+template <int FMT>
+static void launch_decode_fmt(const GemmArgs& a, hipStream_t stream)
 {
-    if (i4) {
-        if (a.M == 1)
-            launch_gemm<1, true>(a, stream);
-        else if (a.M == 2)
-            launch_gemm<2, true>(a, stream);
-        else if (a.M <= 4)
-            launch_gemm<4, true>(a, stream);
-        else if (a.M <= 8)
-            launch_gemm<8, true>(a, stream);
-        else
-            launch_gemm<16, true>(a, stream);
-    } else {
-        if (a.M == 1)
-            launch_gemm<1, false>(a, stream);
-        else if (a.M == 2)
-            launch_gemm<2, false>(a, stream);
-        else if (a.M <= 4)
-            launch_gemm<4, false>(a, stream);
-        else if (a.M <= 8)
-            launch_gemm<8, false>(a, stream);
-        else
-            launch_gemm<16, false>(a, stream);
-    }
+    if (a.M == 1)
+        launch_gemm<1, FMT>(a, stream);
+    else if (a.M == 2)
+        launch_gemm<2, FMT>(a, stream);
+    else if (a.M <= 4)
+        launch_gemm<4, FMT>(a, stream);
+    else if (a.M <= 8)
+        launch_gemm<8, FMT>(a, stream);
+    else
+        launch_gemm<16, FMT>(a, stream);
+}
+
+static void launch_decode(const GemmArgs& a, int fmt, hipStream_t stream)
+{
+    if (fmt == FMT_INT4)
+        launch_decode_fmt<FMT_INT4>(a, stream);
+    else if (fmt == FMT_ANY2)
+        launch_decode_fmt<FMT_ANY2>(a, stream);
+    else
+        launch_decode_fmt<FMT_ANY4>(a, stream);
 }
 
 // Argument checks and dispatch shared by any4_gemm (table lookup) and
 // any4_gemm_int4 (the 4-bit code itself is the value; lut unused).
-static any4_status gemm_call(bool i4, const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
+static any4_status gemm_call(int fmt, const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
                       const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
                       int64_t N, int64_t K, int64_t g, hipStream_t stream)
 {
+    const bool i4 = fmt == FMT_INT4;
     if (M < 0 || N < 0 || !group_ok(K, g) || K / (g > 0 ? g : 1) > MAX_G ||
         (M > 16 && (M + 63) / 64 > 65535))
         return ANY4_E_SHAPE;
@@ -1550,7 +1739,7 @@ static any4_status gemm_call(bool i4, const uint16_t* x, const uint8_t* packed, 
             s16.x = x + m0 * K;
             s16.y = y + m0 * N;
             s16.M = static_cast<int>(M - m0 < 16 ? M - m0 : 16);
-            launch_decode(s16, i4, stream);
+            launch_decode(s16, fmt, stream);
         }
         return launched();
     }
@@ -1558,15 +1747,21 @@ static any4_status gemm_call(bool i4, const uint16_t* x, const uint8_t* packed, 
         if (M <= 64) {
             const dim3 gd(static_cast<unsigned>((N + BIG_BN - 1) / BIG_BN),
                           static_cast<unsigned>((M + 63) / 64));
-            hipLaunchKernelGGL((k_gemm_big<64>), gd, dim3(256), 0, stream, a);
+            if (fmt == FMT_ANY2)
+                hipLaunchKernelGGL((k_gemm_big<64, true>), gd, dim3(256), 0, stream, a);
+            else
+                hipLaunchKernelGGL((k_gemm_big<64, false>), gd, dim3(256), 0, stream, a);
         } else {
             const dim3 gd(static_cast<unsigned>((N + BIG_BN - 1) / BIG_BN),
                           static_cast<unsigned>((M + 127) / 128));
-            hipLaunchKernelGGL((k_gemm_big<128>), gd, dim3(256), 0, stream, a);
+            if (fmt == FMT_ANY2)
+                hipLaunchKernelGGL((k_gemm_big<128, true>), gd, dim3(256), 0, stream, a);
+            else
+                hipLaunchKernelGGL((k_gemm_big<128, false>), gd, dim3(256), 0, stream, a);
         }
         return launched();
     }
-    launch_decode(a, i4, stream);
+    launch_decode(a, fmt, stream);
     return launched();
 }
 
@@ -1659,14 +1854,74 @@ any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* 
 {
     (void)workspace;
     (void)workspace_bytes;
-    return gemm_call(false, x, packed, lut, alpha, beta, y, M, N, K, g, stream);
+    return gemm_call(FMT_ANY4, x, packed, lut, alpha, beta, y, M, N, K, g, stream);
 }
 
 any4_status any4_gemm_int4(const uint16_t* x, const uint8_t* packed, const uint16_t* alpha,
                            const uint16_t* beta, uint16_t* y, int64_t M, int64_t N, int64_t K,
                            int64_t g, hipStream_t stream)
 {
-    return gemm_call(true, x, packed, nullptr, alpha, beta, y, M, N, K, g, stream);
+    return gemm_call(FMT_INT4, x, packed, nullptr, alpha, beta, y, M, N, K, g, stream);
+}
+
+size_t any2_packed_bytes(int64_t N, int64_t K)
+{
+    if (N < 0 || K < 0 || K % TILE_K != 0)
+        return 0;
+    return static_cast<size_t>(row_blocks(N)) * TILE_ROWS * static_cast<size_t>(K / 4);
+}
+
+any4_status any2_pack(const uint8_t* idx, uint8_t* packed, int64_t N, int64_t K,
+                      hipStream_t stream)
+{
+    if (N < 0 || K < 0 || K % TILE_K != 0)
+        return ANY4_E_SHAPE;
+    if (N == 0 || K == 0)
+        return ANY4_OK;
+    if (any2_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31) ||
+        static_cast<size_t>(N) * K >= (static_cast<size_t>(1) << 40))
+        return ANY4_E_SHAPE;
+    if (!idx || !packed)
+        return ANY4_E_NULL;
+    if (!aligned(idx, 16) || !aligned(packed, 16))
+        return ANY4_E_ALIGN;
+    const uint32_t slots = static_cast<uint32_t>(any2_packed_bytes(N, K) / 8);
+    const uint32_t blocks = (slots + PACK_THREADS - 1) / PACK_THREADS;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_pack2, dim3(blocks), dim3(PACK_THREADS), 0, stream, idx, packed,
+                       static_cast<int>(N), static_cast<int>(K), slots);
+    return launched();
+}
+
+any4_status any2_dequant(const uint8_t* packed, const uint16_t* lut, const uint16_t* alpha,
+                         const uint16_t* beta, uint16_t* w, int64_t N, int64_t K, int64_t g,
+                         hipStream_t stream)
+{
+    if (N < 0 || !group_ok(K, g))
+        return ANY4_E_SHAPE;
+    if (N == 0 || K == 0)
+        return ANY4_OK;
+    if (any4_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31))
+        return ANY4_E_SHAPE;
+    if (!packed || !lut || !alpha || !beta || !w)
+        return ANY4_E_NULL;
+    if (!aligned(packed, 16) || !aligned(w, 16) || !aligned(lut, 2) || !aligned(alpha, 2) ||
+        !aligned(beta, 2))
+        return ANY4_E_ALIGN;
+    const int64_t Kc = K / TILE_K;
+    const int64_t blocks = row_blocks(N) * ((Kc + DQ_WAVES - 1) / DQ_WAVES);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_dequant2, dim3(static_cast<unsigned>(blocks)), dim3(64 * DQ_WAVES), 0,
+                       stream, packed, lut, alpha, beta, w, static_cast<int>(N),
+                       static_cast<int>(K), static_cast<int>(g));
+    return launched();
+}
+
+any4_status any2_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
+                      const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
+                      int64_t N, int64_t K, int64_t g, hipStream_t stream)
+{
+    return gemm_call(FMT_ANY2, x, packed, lut, alpha, beta, y, M, N, K, g, stream);
 }
 
 any4_status any4_quantize(const float* W, const float* ex, uint8_t* idx, uint16_t* lut,

@@ -1,5 +1,6 @@
 /*
- * any4.h -- C ABI of libany4.so, the MI355X (gfx950) any4 dequantize-GEMM.
+ * any4.h -- C ABI of libany4.so, the MI355X (gfx950) any4 dequantize-GEMM
+ * (with plain int4, the any2 2-bit variant and the any4 quantiser).
  *
  * any4 (the 10100.com any4 explainer, section 二) stores each weight of a
  * row as a 4-bit index into that row's 16-entry bf16 lookup table; each
@@ -158,6 +159,40 @@ any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* 
 any4_status any4_gemm_int4(const uint16_t* x, const uint8_t* packed, const uint16_t* alpha,
                            const uint16_t* beta, uint16_t* y, int64_t M, int64_t N, int64_t K,
                            int64_t g, hipStream_t stream);
+
+/*
+ * any2 -- the 2-bit variant at 2 bits per stored weight (the paper's abstract
+ * names any2): each weight is a 2-bit code into its row's table, of which
+ * only entries 0..3 are read (a [N][16] bf16 table as everywhere else, e.g.
+ * any4_quantize with bits = 2; entries 4..15 are ignored).  Codes are packed
+ * four to a byte in tiles of 16 rows x 128 k (any2_packed_bytes(N, K)
+ * bytes):
+ *     tile (b, c) covers rows 16b..16b+15 and k 128c..128c+127 and starts at
+ *     byte (b * K/128 + c) * 512;
+ *     byte 8*l + i of a tile (lane l = 0..63, i = 0..7) holds, for row
+ *     n = 16b + (l % 16) and k = 128c + 32*(l / 16) + 4i,
+ *         code[n][k+s] in bits 2s..2s+1 (s = 0..3);
+ *     rows n >= N are zero bytes.
+ * Equivalently: row-major bytes P[n][j] = sum_s code[n][4j+s] << 2s, padded to
+ * a multiple of 16 rows, viewed as [N/16][16][K/128][4][8] and stored as
+ * [N/16][K/128][4][16][8].
+ * any2_pack, any2_dequant and any2_gemm take the same arguments and follow
+ * the same conventions, checks and errors as any4_pack, any4_dequant and
+ * any4_gemm (no workspace argument), with idx read as codes 0..3 (bits
+ * above 1 ignored):
+ *     w[n][k] = bf16_rne( fp32( alpha[n][k/g] * lut[n][code[n][k]] + beta[n][k/g] ) )
+ *     y[m][n] = bf16_rne( sum_k x[m][k] * w[n][k] )   (same bound as any4_gemm)
+ * Returns of any2_packed_bytes: ceil(N/16) * 16 * K/4, or 0 as any4_packed_bytes.
+ */
+size_t any2_packed_bytes(int64_t N, int64_t K);
+any4_status any2_pack(const uint8_t* idx, uint8_t* packed, int64_t N, int64_t K,
+                      hipStream_t stream);
+any4_status any2_dequant(const uint8_t* packed, const uint16_t* lut, const uint16_t* alpha,
+                         const uint16_t* beta, uint16_t* w, int64_t N, int64_t K, int64_t g,
+                         hipStream_t stream);
+any4_status any2_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
+                      const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
+                      int64_t N, int64_t K, int64_t g, hipStream_t stream);
 
 /*
  * any4_quantize -- the any4 quantiser: turns weights into the idx, lut, alpha

@@ -166,6 +166,56 @@ def untile(t, N: int, K: int) -> np.ndarray:
     return np.ascontiguousarray(P).reshape(NB * TILE_ROWS, K // 2)[:N].copy()
 
 
+# --------------------------------------------------------------------------
+# any2: 2-bit codes, four per byte (the any4 paper's abstract names any2)
+# --------------------------------------------------------------------------
+def pack2(idx) -> np.ndarray:
+    """idx u8 [N, K] (codes 0..3; higher bits ignored) -> [N, K/4] bytes:
+    byte j of a row holds codes 4j .. 4j+3 in bits 0-1, 2-3, 4-5, 6-7."""
+    idx = _c(idx, np.uint8)
+    N, K = idx.shape
+    assert K % 4 == 0
+    q = (idx & 3).reshape(N, K // 4, 4).astype(np.uint8)
+    return (q[:, :, 0] | (q[:, :, 1] << 2) | (q[:, :, 2] << 4) | (q[:, :, 3] << 6)).astype(np.uint8)
+
+
+def unpack2(packed, K: int) -> np.ndarray:
+    packed = _c(packed, np.uint8)
+    N = packed.shape[0]
+    out = np.empty((N, K // 4, 4), np.uint8)
+    for s in range(4):
+        out[:, :, s] = (packed >> (2 * s)) & 3
+    return out.reshape(N, K)
+
+
+def tiled2_bytes(N: int, K: int) -> int:
+    """Bytes of the any2 tile layout: rows padded to a multiple of 16, K/4 bytes each."""
+    return -(-N // TILE_ROWS) * TILE_ROWS * (K // 4)
+
+
+def tile2(packed2) -> np.ndarray:
+    """Row-major any2 bytes [N, K/4] -> the any2 tile layout (flat uint8):
+    512-byte tiles of 16 rows x 128 k.  Pad the rows to a multiple of 16, view
+    the bytes as [N/16][16 rows][K/128][4 quarters][8 bytes] and store them in
+    the order [blocks][chunks][quarters][rows][bytes]."""
+    packed2 = _c(packed2, np.uint8)
+    N, K4 = packed2.shape
+    K = 4 * K4
+    assert K % TILE_K == 0
+    NB = -(-N // TILE_ROWS)
+    P = np.zeros((NB * TILE_ROWS, K4), np.uint8)
+    P[:N] = packed2
+    t = P.reshape(NB, TILE_ROWS, K // TILE_K, 4, 8).transpose(0, 2, 3, 1, 4)
+    return np.ascontiguousarray(t).reshape(-1)
+
+
+def untile2(t, N: int, K: int) -> np.ndarray:
+    """Inverse of tile2 (padding rows dropped)."""
+    NB = -(-N // TILE_ROWS)
+    t = _c(t, np.uint8).reshape(NB, K // TILE_K, 4, TILE_ROWS, 8).transpose(0, 3, 1, 2, 4)
+    return np.ascontiguousarray(t).reshape(NB * TILE_ROWS, K // 4)[:N]
+
+
 def dequant_one(alpha: int, lut_value: int, beta: int) -> int:
     return int(_load().orc_dequant_one(alpha, lut_value, beta))
 

@@ -57,3 +57,47 @@ def test_one_tile_is_contiguous_per_lane():
     for l in range(64):
         n, k = l % 16, 32 * (l // 16)
         assert t[16 * l] == ((n + k) % 16) | (((n + k + 1) % 16) << 4)
+
+
+# ---- any2: 2-bit codes, 512-byte tiles of 16 rows x 128 k -------------------
+def _tile2_by_definition(idx: np.ndarray) -> np.ndarray:
+    """byte 8*l + i of tile (b, c) = sum_s (idx[n][k + s] & 3) << 2s with
+    n = 16b + l % 16 and k = 128c + 32*(l // 16) + 4i; zero for n >= N."""
+    N, K = idx.shape
+    NB, Kc = -(-N // 16), K // 128
+    out = np.zeros(NB * Kc * 512, np.uint8)
+    for b in range(NB):
+        for c in range(Kc):
+            for l in range(64):
+                n = 16 * b + l % 16
+                if n >= N:
+                    continue
+                for i in range(8):
+                    k = 128 * c + 32 * (l // 16) + 4 * i
+                    v = 0
+                    for s in range(4):
+                        v |= (int(idx[n, k + s]) & 3) << (2 * s)
+                    out[(b * Kc + c) * 512 + 8 * l + i] = v
+    return out
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (16, 128), (17, 256), (37, 384)])
+def test_tile2_matches_the_per_byte_definition(N, K):
+    rng = np.random.default_rng(N * 7 + K)
+    idx = rng.integers(0, 256, size=(N, K), dtype=np.uint8)   # bits above 1 are ignored
+    t = oracle.tile2(oracle.pack2(idx))
+    assert t.size == oracle.tiled2_bytes(N, K)
+    assert np.array_equal(t, _tile2_by_definition(idx))
+
+
+@pytest.mark.parametrize("N,K", [(5, 128), (33, 640)])
+def test_pack2_round_trip(N, K):
+    rng = np.random.default_rng(N + 3 * K)
+    idx = rng.integers(0, 4, size=(N, K), dtype=np.uint8)
+    p = oracle.pack2(idx)
+    assert np.array_equal(oracle.unpack2(p, K), idx)
+    assert np.array_equal(oracle.untile2(oracle.tile2(p), N, K), p)
+    # all 256 byte values decode to their four 2-bit fields
+    b = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    u = oracle.unpack2(b, 1024).reshape(256, 4)
+    assert np.array_equal(u[:, 0] | (u[:, 1] << 2) | (u[:, 2] << 4) | (u[:, 3] << 6), b[0])
