@@ -4,21 +4,30 @@
 // into its row's 16-entry bf16 table (section 二), each contiguous group of g
 // weights of a row has a scale alpha and an offset beta (step 1, "分组缩放"), so
 // w = alpha * LUT_row[idx] + beta; the matmul y = x * W^T runs at decode batch
-// sizes 1..16 (section 三).  The C ABI is declared in include/any4.h.
+// sizes 1..16 (section 三).  Also here: the same product for plain int4 and for
+// any2 (2-bit codes, the any4 paper's abstract), larger batches, and the
+// quantiser that learns the tables (step 2, E-step / M-step).  The C ABI is
+// declared in include/any4.h.
 //
-// Packed tile layout (written by k_pack, read by k_dequant and k_gemm)
+// Packed tile layout (written by k_pack, read by k_dequant and the GEMMs)
 //   The weights are cut into tiles of 16 rows x 128 k.  A tile is 1 KB and is
 //   one 16-byte load per lane of a wave64: lane l holds row (l % 16) of the
 //   tile, k in [32*(l/16), 32*(l/16) + 32), two indices per byte, the even k
 //   in the low nibble.  Tiles are stored row-block major: tile (b, c) of row
 //   block b (rows 16b..16b+15) and k-chunk c (k 128c..128c+127) starts at byte
-//   (b * K/128 + c) * 1024.  Rows past N are zero padding.
+//   (b * K/128 + c) * 1024.  Rows past N are zero padding.  any2 tiles are the
+//   same with four 2-bit codes per byte: 512 bytes, an 8-byte load per lane.
 //
 // Kernels
-//   k_pack     idx[N][K] u8 -> tiles, 16 output bytes per thread.
-//   k_dequant  w = bf16(fma(alpha, LUT[idx], beta)), one tile slot per thread.
-//   k_gemm     y = x * W^T with v_mfma_f32_16x16x32_bf16; see the comment above
-//              the kernel.
+//   k_pack, k_pack2        idx[N][K] u8 -> tiles, one tile slot per thread.
+//   k_dequant, k_dequant2  w = bf16(fma(alpha, LUT[idx], beta)), one slot per thread.
+//   k_gemm_km, k_gemm_kb   y = x * W^T for M <= 16 (K <= 4096 / any K): the
+//                          weights stream once, decoded through table lookups
+//                          in LDS into v_mfma_f32_16x16x32_bf16 operands; see
+//                          the comments above the kernels.
+//   k_gemm_big             M > 48: tiles dequantised into LDS, then MFMAs.
+//   k_quantize             group scale + weighted k-means, one thread per row.
+//   k_zero                 y = 0 when K = 0.
 #include <hip/hip_runtime.h>
 
 #include "any4.h"
