@@ -15,7 +15,11 @@ region.
 value = algorithmic bytes of all timed launches / timed wall time (TB/s),
 where the algorithmic bytes of one launch are
     N*K/2 (indices) + 4*N*K/g (alpha, beta) + 32*N (tables) + 2*M*K (x) + 2*M*N (y).
-Per-M launch durations come from graphs of that M alone (same events).
+Per-M launch durations come from graphs of that M alone (same events); the
+per-launch distribution (p10 / p50 / p90) from 100 eager launches, each
+bracketed by HIP events; and `read_probe` is any4_read_probe (one read of
+the same packed weights with the GEMM's loads) timed like the GEMM: the
+streaming-read ceiling each per-M figure is also given as a percentage of.
 
 The same graph timing is also reported, outside `value`, for the other
 layer shape, the MLP down projection N=4096, K=14336, g=1024, at M=1 and
@@ -383,6 +387,40 @@ def main() -> int:
             "pct_hbm_peak": 100.0 * bts / (us * 1e-6) / (HBM_PEAK_GBS * 1e9),
         }
 
+    # per-launch distribution: eager launches, each bracketed by HIP events
+    st = torch.cuda.current_stream()
+    for M in MS:
+        ts = []
+        for i in range(100):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            launch(i, M)
+            e1.record(st)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in ts])
+        per_m[str(M)]["per_launch_events_us"] = {
+            "p10": float(np.percentile(us, 10)), "p50": float(np.percentile(us, 50)),
+            "p90": float(np.percentile(us, 90)), "launches": len(us)}
+
+    # streaming-read ceiling: the read probe over the same rotating packed
+    # buffers, graph-timed like the GEMM
+    pbytes = sets[0][0].numel()
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def probe(i: int, M: int):
+        any4.check(any4.read_probe_raw(sets[i % R][0].data_ptr(), pbytes, flag.data_ptr(),
+                                       torch.cuda.current_stream().cuda_stream))
+
+    gp = _graph(torch, probe, K, (1,))
+    _time_graph(torch, gp)
+    probe_us = float(np.median([_time_graph(torch, gp) * 1e3 / K for _ in range(3)]))
+    del gp
+    probe_tbps = pbytes / (probe_us * 1e-6) / 1e12
+    for M in MS:
+        per_m[str(M)]["pct_of_read_probe"] = 100.0 * per_m[str(M)]["tbps"] / probe_tbps
+
     step_bytes = sum(algorithmic_bytes(M, N_, K_, G_) for M in MS)
     value = step_bytes * K / (total_ms * 1e-3) / 1e12
     dom = max(MS, key=lambda M: per_m[str(M)]["us_per_launch"])
@@ -403,6 +441,10 @@ def main() -> int:
                    "parallelism": "single GPU", "timing": "HIP graph replay, HIP events"},
         "roofline": roofline,
         "per_m": per_m,
+        "read_probe": {"bytes": pbytes, "us_per_launch": probe_us, "tbps": probe_tbps,
+                       "pct_hbm_peak": 100.0 * probe_tbps * 1e3 / HBM_PEAK_GBS,
+                       "what": "any4_read_probe over the packed weights of the same "
+                               "rotating sets: the streaming-read ceiling of one launch"},
         "host_wall_s": wall,
     }
     if not args.no_other_layers:

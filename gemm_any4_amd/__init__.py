@@ -34,7 +34,7 @@ _STATUS_NAMES = {0: "ANY4_OK", 1: "ANY4_E_NULL", 2: "ANY4_E_SHAPE", 3: "ANY4_E_A
 # every symbol include/any4.h declares
 EXPORTS = ("any4_packed_bytes", "any4_pack", "any4_dequant", "any4_gemm_workspace_size",
            "any4_gemm", "any4_gemm_int4", "any4_quantize", "any4_status_string",
-           "any2_packed_bytes", "any2_pack", "any2_dequant", "any2_gemm")
+           "any2_packed_bytes", "any2_pack", "any2_dequant", "any2_gemm", "any4_read_probe")
 
 _lib = None
 
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.any2_dequant.argtypes = [P, P, P, P, P, I64, I64, I64, P]
         L.any2_gemm.restype = ctypes.c_int
         L.any2_gemm.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
+        L.any4_read_probe.restype = ctypes.c_int
+        L.any4_read_probe.argtypes = [P, SZ, P, P]
         L.any4_status_string.restype = ctypes.c_char_p
         L.any4_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -389,3 +391,8 @@ def any2_gemm(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: t
     check(any2_gemm_raw(_ptr(x), _ptr(packed), _ptr(lut), _ptr(alpha), _ptr(beta), _ptr(out),
                         M, N, K, g, stream))
     return out
+
+
+def read_probe_raw(buf_ptr, nbytes: int, out_ptr, stream=None) -> int:
+    """The streaming-read probe (a measurement aid; see include/any4.h)."""
+    return lib().any4_read_probe(buf_ptr, nbytes, out_ptr, _stream(stream))

@@ -231,6 +231,18 @@ any4_status any4_quantize(const float* W, const float* ex, uint8_t* idx, uint16_
                           uint16_t* alpha, uint16_t* beta, int64_t N, int64_t K, int64_t g,
                           int iters, int bits, hipStream_t stream);
 
+/*
+ * any4_read_probe -- a measurement aid, not part of the method: reads `bytes`
+ * of device memory at `buf` once, with the GEMM kernels' loads (16 bytes per
+ * lane, 1 KB per wave, non-temporal, 16 loads in flight per wave, one
+ * workgroup of 8 waves per CU), and writes at most one word to `out`.  Its
+ * duration is the streaming-read ceiling that the GEMM's bandwidth is
+ * compared with.  bytes: a multiple of 1024, below 2 GiB (0: no-op).
+ * Errors: ANY4_E_SHAPE, ANY4_E_NULL, ANY4_E_ALIGN (buf not 16-byte or out
+ * not 4-byte aligned), ANY4_E_HIP.
+ */
+any4_status any4_read_probe(const void* buf, size_t bytes, uint32_t* out, hipStream_t stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char* any4_status_string(any4_status s);
 

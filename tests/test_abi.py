@@ -140,3 +140,10 @@ def test_any2_errors_and_sizes():
     assert any4.any2_gemm_raw(A, A, None, A, A, A, 1, 16, 128, 128, stream=0) == 1
     assert any4.any2_gemm_raw(A, A, A, A + 2, A, A, 1, 16, 128, 128, stream=0) == 3
     assert any4.any2_gemm_raw(None, None, None, None, None, None, 0, 16, 128, 128, stream=0) == 0
+
+
+def test_read_probe_errors():
+    assert any4.read_probe_raw(A, 1000, A, stream=0) == 2
+    assert any4.read_probe_raw(None, 1024, A, stream=0) == 1
+    assert any4.read_probe_raw(A + 8, 1024, A, stream=0) == 3
+    assert any4.read_probe_raw(None, 0, None, stream=0) == 0
