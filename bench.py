@@ -28,7 +28,8 @@ M=16, under "other_layers"; and for both layers with plain int4 weights
 "int4_no_table", which puts a number on what the table lookup costs; and
 at prefill batches M = 64, 256, 1024 on the up/gate layer (TFLOP/s against
 the bf16 matrix peak), under "prefill"; both layers with the codes taken to
-2 bits through any2_gemm, under "any2"; and the GPU quantiser on a 4096x4096
+2 bits through any2_gemm, under "any2"; the 70B decoder-layer shapes and their
+layer total, under "decoder_layer_70b"; and the GPU quantiser on a 4096x4096
 layer at 4, 3 and 2 bits, under "quantize".
 
 Prints one JSON line.  --traffic-probe instead runs a few launches of each M
@@ -216,6 +217,59 @@ def any2_layer(torch, any4, workloads, cfg: int, steps: int) -> dict:
         del g
     del sets
     torch.cuda.empty_cache()
+    return out
+
+
+def decoder_layer(torch, any4, workloads, steps: int) -> dict:
+    """The 70B decoder-layer shapes (q/k/v/o 8192x8192, up/gate 28672x8192,
+    down 8192x28672, g = 128) at M = 1, 4, 16, graph-timed over rotating
+    weight sets, and the layer total 4*t(qkvo) + 2*t(up/gate) + t(down).
+    Speed does not depend on the values, so the weights here are seeded
+    random codes and tables drawn on the device (the parity tests use the
+    quantiser's weights for these shapes)."""
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device="cpu").manual_seed(4)
+    g = workloads.CONFIG4_G
+    Ms = workloads.CONFIG4_MS
+    out = {"g": g, "M": list(Ms)}
+    for name, spec in workloads.CONFIG4_LAYERS.items():
+        N, K = spec["N"], spec["K"]
+        wb = weight_bytes(N, K, g)
+        R = max(2, math.ceil(2 * CACHE_BYTES / wb) + 1)
+        idx = torch.randint(0, 16, (N, K), generator=gen, dtype=torch.uint8).to(dev)
+        p0 = any4.pack(idx)
+        del idx
+        lut = torch.randn(N, 16, generator=gen).to(torch.bfloat16).to(dev)
+        al = (torch.rand(N, K // g, generator=gen) * 0.015 + 0.005).to(torch.bfloat16).to(dev)
+        be = (torch.randn(N, K // g, generator=gen) * 0.002).to(torch.bfloat16).to(dev)
+        sets = [(p0.clone(), lut, al, be) for _ in range(R)]
+        del p0
+        x = torch.randn(max(Ms), K, generator=gen).to(torch.bfloat16).to(dev)
+        ys = {M: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for M in Ms}
+
+        def launch(i: int, M: int):
+            p, l, a, b = sets[i % R]
+            any4.gemm(x[:M], p, l, a, b, g, out=ys[M])
+
+        res = {"N": N, "K": K, "rotating_weight_sets": R}
+        for M in Ms:
+            for i in range(3):
+                launch(i, M)
+            gr = _graph(torch, launch, steps, (M,))
+            _time_graph(torch, gr)
+            us = float(np.median([_time_graph(torch, gr) * 1e3 / steps for _ in range(3)]))
+            bts = algorithmic_bytes(M, N, K, g)
+            res[str(M)] = {"us_per_launch": us, "tbps": bts / (us * 1e-6) / 1e12,
+                           "pct_hbm_peak": 100.0 * bts / (us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+            del gr
+        out[name] = res
+        del sets, x, ys
+        torch.cuda.empty_cache()
+    out["layer_total_us"] = {
+        str(M): 4 * out["qkvo"][str(M)]["us_per_launch"] + 2 * out["up_gate"][str(M)]["us_per_launch"]
+        + out["down"][str(M)]["us_per_launch"] for M in Ms}
     return out
 
 
@@ -459,6 +513,7 @@ def main() -> int:
         out["any2"] = {f"config{c}": any2_layer(torch, any4, workloads, c, min(K, 100))
                        for c in (2, 3)}
         out["prefill"] = prefill(torch, any4, workloads, (64, 256, 1024))
+        out["decoder_layer_70b"] = decoder_layer(torch, any4, workloads, min(K, 50))
         out["quantize"] = quantize_timing(torch, any4, 4096, 4096, 128)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

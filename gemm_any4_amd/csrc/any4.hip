@@ -1679,8 +1679,10 @@ void launch_gemm(const GemmArgs& a, hipStream_t stream)
     while (nbg > 1 && G > (nbg == 4 ? KbCfg<4, false>::GMAX
                                     : nbg == 3 ? KbCfg<3, false>::GMAX : KbCfg<2, false>::GMAX))
         --nbg;
-    // x in LDS: M <= 2, at most two blocks per group, and x small enough
-    const bool xl = MT <= 2 && nbg <= 2 &&
+    // x in LDS: M <= 2, one block per group, and x small enough (measured:
+    // with two blocks per group the staging costs more than it saves, e.g.
+    // 16.2 against 14.6 us on 8192x8192 at M = 1)
+    const bool xl = MT <= 2 && nbg == 1 &&
                     static_cast<int64_t>(a.M) * a.K * 2 <= KbCfg<1, true>::XMAX;
     if (xl) {
         if constexpr (MT <= 2) {
