@@ -936,7 +936,7 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
 // tile of every block of the group).  The loop body is unrolled over DS
 // steps (the ring depth); a group's steps are padded to a multiple of DS
 // with dead steps (out-of-range loads, and a uniform branch skips their
-// decode).  x: with XL (M <= 2 and x small enough) the whole of x is copied
+// decode).  x: with XL (M <= 2, one block per group, x small enough) x is copied
 // to LDS in the prologue and each chunk's operands are read from there by
 // the lanes of rows m < M; otherwise x travels in the ring, its operand
 // loads for a chunk following the chunk's last tile.  alpha and beta of a
@@ -953,6 +953,7 @@ constexpr int KB_XL_PIECES = 7;   // 16-byte pieces of x per thread (XL): 56 KB
 
 template <int NBG, bool XL>
 struct KbCfg {
+    static_assert(!XL || NBG == 1, "x in LDS goes with one block per group");
     static constexpr int GMAX = NBG == 1 ? 512 : NBG == 2 ? 256 : NBG == 3 ? 144 : 112;
     static constexpr int TABS = ((NBG + 1) / 2) * 65536;
     static constexpr int ZERO = TABS;   // 256 zero bytes: the table reads of dead tiles
@@ -964,8 +965,7 @@ struct KbCfg {
     static constexpr int XMAX = XL ? KB_XL_PIECES * GT * 16 : 0;   // bytes of x in LDS
     static constexpr int LDS = XS + XMAX;
     // ring depth in chunks: x in the ring costs 16 VGPRs per chunk
-    static constexpr int DS = XL ? (NBG == 1 ? 10 : NBG == 2 ? 6 : NBG == 3 ? 4 : 3)
-                                 : (NBG == 1 ? 6 : NBG == 2 ? 4 : 2);
+    static constexpr int DS = XL ? 10 : (NBG == 1 ? 6 : NBG == 2 ? 4 : 2);
     static constexpr int D = DS * NBG;                             // ... in tiles
     static_assert(D % 2 == 0, "tiles are decoded in pairs");
     static_assert(LDS <= 160 * 1024, "LDS of one CU");
@@ -1685,12 +1685,8 @@ void launch_gemm(const GemmArgs& a, hipStream_t stream)
     const bool xl = MT <= 2 && nbg == 1 &&
                     static_cast<int64_t>(a.M) * a.K * 2 <= KbCfg<1, true>::XMAX;
     if (xl) {
-        if constexpr (MT <= 2) {
-            if (nbg == 1)
-                hipLaunchKernelGGL((k_gemm_kb<MT, 1, true, FMT>), gd, dim3(GT), 0, stream, a);
-            else
-                hipLaunchKernelGGL((k_gemm_kb<MT, 2, true, FMT>), gd, dim3(GT), 0, stream, a);
-        }
+        if constexpr (MT <= 2)
+            hipLaunchKernelGGL((k_gemm_kb<MT, 1, true, FMT>), gd, dim3(GT), 0, stream, a);
         return;
     }
     if (nbg == 1)
