@@ -374,6 +374,64 @@ def traffic_probe(torch, any4, workloads, sets_arg: int) -> int:
     return 0
 
 
+def _counter_per_dispatch(path: str, counter: str) -> list:
+    """[kernel name, value] per dispatch of one rocprofv3 counter CSV, in
+    dispatch order (values of one dispatch over several rows are summed)."""
+    import csv
+    per = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            e = per.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0.0])
+            e[1] += float(r["Counter_Value"])
+    return [per[d] for d in sorted(per)]
+
+
+def traffic_summary(fetch_csv: str, write_csv: str) -> int:
+    """Write the committed traffic summary from the counter files of two
+    `--traffic-probe` runs (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE):
+    HBM bytes per launch of each M, each counter scaled by what it reads for
+    the COPY_BYTES device copy that ends the probe."""
+    import re
+    fetch = _counter_per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_csv, "WRITE_SIZE")
+    for rows in (fetch, write):
+        if not rows or "copyBuffer" not in rows[-1][0]:
+            raise SystemExit("the last dispatch of a traffic probe is the calibration copy")
+    fscale = COPY_BYTES / (fetch[-1][1] * 1024)
+    wscale = COPY_BYTES / (write[-1][1] * 1024)
+    pat = re.compile(r"(k_gemm_k[mb]<(\d+),[^>]*>)")
+
+    def by_m(rows):
+        out = {}
+        for name, v in rows:
+            m = pat.search(name)
+            if m:
+                out.setdefault(int(m.group(2)), (m.group(1), []))[1].append(v)
+        return out
+
+    f_m, w_m = by_m(fetch), by_m(write)
+    per_m = {}
+    for M in MS:
+        name, fv = f_m[M]
+        wv = w_m[M][1]
+        fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
+        hbm = fk * 1024 * fscale + wk * 1024 * wscale
+        alg = algorithmic_bytes(M, N_, K_, G_)
+        per_m[str(M)] = {"kernel": name, "dispatches": len(fv), "fetch_kib_raw": round(fk, 2),
+                         "write_kib": round(wk, 2), "hbm_bytes_per_launch": round(hbm),
+                         "algorithmic_bytes": alg, "ratio": hbm / alg}
+    t = {"kernel_source_sha256_16": kernel_source_hash(),
+         "workload": f"N={N_} K={K_} g={G_}", "copy_bytes": COPY_BYTES,
+         "fetch_scale": fscale, "write_scale": wscale, "per_m": per_m}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1)
+        f.write("\n")
+    print(json.dumps(t))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -384,11 +442,15 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-layers", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary from two --traffic-probe counter files")
     args = ap.parse_args()
+    if args.traffic_summary:
+        return traffic_summary(*args.traffic_summary)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the any4 GEMM runs on a single MI355X; "
-              "multi-GPU runs are not part of this build (use --gpus 1).", file=sys.stderr)
+              "multi-GPU runs are not supported (use --gpus 1).", file=sys.stderr)
         return 2
 
     import numpy as np
