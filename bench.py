@@ -28,7 +28,8 @@ M=16, under "other_layers"; and for both layers with plain int4 weights
 "int4_no_table", which puts a number on what the table lookup costs; and
 at prefill batches M = 64, 256, 1024 on the up/gate layer (TFLOP/s against
 the bf16 matrix peak), under "prefill"; both layers with the codes taken to
-2 bits through any2_gemm, under "any2"; the 70B decoder-layer shapes and their
+2 bits through any2_gemm and to 3 bits through any3_gemm, under "any2" and
+"any3"; the 70B decoder-layer shapes and their
 layer total, under "decoder_layer_70b"; and the GPU quantiser on a 4096x4096
 layer at 4, 3 and 2 bits, under "quantize".
 
@@ -177,24 +178,27 @@ def other_layer(torch, any4, workloads, cfg: int, steps: int, int4: bool = False
     return out
 
 
-def any2_layer(torch, any4, workloads, cfg: int, steps: int) -> dict:
-    """Per-launch µs of any2_gemm on config `cfg`'s layer with the codes taken
-    to 2 bits (idx & 3, packed four to a byte), rotating weight sets, graph
-    replays; bytes are the any2 algorithmic bytes (N*K/4 for the codes)."""
+def lowbit_layer(torch, any4, workloads, cfg: int, steps: int, bits: int = 2) -> dict:
+    """Per-launch µs of any2_gemm (bits = 2) or any3_gemm (bits = 3) on config
+    `cfg`'s layer with the codes taken to that many bits (idx & 3 or idx & 7,
+    in that format's tiles), rotating weight sets, graph replays; bytes are the
+    format's algorithmic bytes (N*K*bits/8 for the codes)."""
     import numpy as np
 
     c = workloads.CONFIGS[cfg]
     dev = torch.device("cuda:0")
     inp = workloads.generate(cfg)
-    wb = c.N * c.K // 4 + 4 * c.N * (c.K // c.g) + 32 * c.N
+    wb = c.N * c.K * bits // 8 + 4 * c.N * (c.K // c.g) + 32 * c.N
     R = max(2, math.ceil(2 * CACHE_BYTES / wb) + 1)
 
     def b16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
             torch.bfloat16)
 
-    codes = torch.from_numpy(inp.idx & 3).to(dev)
-    p0 = any4.any2_pack(codes)
+    codes = torch.from_numpy(inp.idx & ((1 << bits) - 1)).to(dev)
+    pack, gemm = (any4.any2_pack, any4.any2_gemm) if bits == 2 else (any4.any3_pack,
+                                                                     any4.any3_gemm)
+    p0 = pack(codes)
     del codes
     sets = [(p0.clone(), b16(inp.lut), b16(inp.alpha), b16(inp.beta)) for _ in range(R)]
     x = b16(inp.x)
@@ -202,7 +206,7 @@ def any2_layer(torch, any4, workloads, cfg: int, steps: int) -> dict:
 
     def launch(i: int, M: int):
         p, l, a, b = sets[i % R]
-        any4.any2_gemm(x[:M], p, l, a, b, c.g, out=ys[M])
+        gemm(x[:M], p, l, a, b, c.g, out=ys[M])
 
     out = {"N": c.N, "K": c.K, "g": c.g, "rotating_weight_sets": R}
     for M in MS:
@@ -572,7 +576,9 @@ def main() -> int:
                                                           min(K, 100), int4=True)
                                 for c in (2, 3)}
     if not args.no_other_layers:
-        out["any2"] = {f"config{c}": any2_layer(torch, any4, workloads, c, min(K, 100))
+        out["any2"] = {f"config{c}": lowbit_layer(torch, any4, workloads, c, min(K, 100), 2)
+                       for c in (2, 3)}
+        out["any3"] = {f"config{c}": lowbit_layer(torch, any4, workloads, c, min(K, 100), 3)
                        for c in (2, 3)}
         out["prefill"] = prefill(torch, any4, workloads, (64, 256, 1024))
         out["decoder_layer_70b"] = decoder_layer(torch, any4, workloads, min(K, 50))

@@ -34,7 +34,8 @@ _STATUS_NAMES = {0: "ANY4_OK", 1: "ANY4_E_NULL", 2: "ANY4_E_SHAPE", 3: "ANY4_E_A
 # every symbol include/any4.h declares
 EXPORTS = ("any4_packed_bytes", "any4_pack", "any4_dequant", "any4_gemm_workspace_size",
            "any4_gemm", "any4_gemm_int4", "any4_quantize", "any4_status_string",
-           "any2_packed_bytes", "any2_pack", "any2_dequant", "any2_gemm", "any4_read_probe")
+           "any2_packed_bytes", "any2_pack", "any2_dequant", "any2_gemm",
+           "any3_packed_bytes", "any3_pack", "any3_dequant", "any3_gemm", "any4_read_probe")
 
 _lib = None
 
@@ -68,14 +69,15 @@ def lib() -> ctypes.CDLL:
         L.any4_gemm_int4.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
         L.any4_quantize.restype = ctypes.c_int
         L.any4_quantize.argtypes = [P, P, P, P, P, P, I64, I64, I64, ctypes.c_int, ctypes.c_int, P]
-        L.any2_packed_bytes.restype = SZ
-        L.any2_packed_bytes.argtypes = [I64, I64]
-        L.any2_pack.restype = ctypes.c_int
-        L.any2_pack.argtypes = [P, P, I64, I64, P]
-        L.any2_dequant.restype = ctypes.c_int
-        L.any2_dequant.argtypes = [P, P, P, P, P, I64, I64, I64, P]
-        L.any2_gemm.restype = ctypes.c_int
-        L.any2_gemm.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
+        for v in ("any2", "any3"):
+            getattr(L, v + "_packed_bytes").restype = SZ
+            getattr(L, v + "_packed_bytes").argtypes = [I64, I64]
+            getattr(L, v + "_pack").restype = ctypes.c_int
+            getattr(L, v + "_pack").argtypes = [P, P, I64, I64, P]
+            getattr(L, v + "_dequant").restype = ctypes.c_int
+            getattr(L, v + "_dequant").argtypes = [P, P, P, P, P, I64, I64, I64, P]
+            getattr(L, v + "_gemm").restype = ctypes.c_int
+            getattr(L, v + "_gemm").argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
         L.any4_read_probe.restype = ctypes.c_int
         L.any4_read_probe.argtypes = [P, SZ, P, P]
         L.any4_status_string.restype = ctypes.c_char_p
@@ -305,19 +307,34 @@ def quantize(W: torch.Tensor, ex: torch.Tensor, g: int, iters: int = 10, bits: i
 
 
 # --------------------------------------------------------------------------
-# any2: 2-bit codes, four per byte (tile layout in include/any4.h)
+# any2 (2-bit codes, four per byte) and any3 (3-bit codes, 12 bytes per 32):
+# tile layouts in include/any4.h
 # --------------------------------------------------------------------------
 def any2_packed_bytes(N: int, K: int) -> int:
     return int(lib().any2_packed_bytes(N, K))
+
+
+def any3_packed_bytes(N: int, K: int) -> int:
+    return int(lib().any3_packed_bytes(N, K))
 
 
 def any2_pack_raw(idx_ptr, packed_ptr, N, K, stream=None) -> int:
     return lib().any2_pack(idx_ptr, packed_ptr, N, K, _stream(stream))
 
 
+def any3_pack_raw(idx_ptr, packed_ptr, N, K, stream=None) -> int:
+    return lib().any3_pack(idx_ptr, packed_ptr, N, K, _stream(stream))
+
+
 def any2_dequant_raw(packed_ptr, lut_ptr, alpha_ptr, beta_ptr, w_ptr, N, K, g,
                      stream=None) -> int:
     return lib().any2_dequant(packed_ptr, lut_ptr, alpha_ptr, beta_ptr, w_ptr, N, K, g,
+                              _stream(stream))
+
+
+def any3_dequant_raw(packed_ptr, lut_ptr, alpha_ptr, beta_ptr, w_ptr, N, K, g,
+                     stream=None) -> int:
+    return lib().any3_dequant(packed_ptr, lut_ptr, alpha_ptr, beta_ptr, w_ptr, N, K, g,
                               _stream(stream))
 
 
@@ -327,32 +344,39 @@ def any2_gemm_raw(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, 
                            _stream(stream))
 
 
-def any2_pack(idx: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """idx uint8 [N, K] (codes 0..3) -> packed uint8 [any2_packed_bytes(N, K)]."""
+def any3_gemm_raw(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
+                  stream=None) -> int:
+    return lib().any3_gemm(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
+                           _stream(stream))
+
+
+_LOWBIT = {2: (any2_packed_bytes, any2_pack_raw, any2_dequant_raw, any2_gemm_raw),
+           3: (any3_packed_bytes, any3_pack_raw, any3_dequant_raw, any3_gemm_raw)}
+
+
+def _lowbit_pack(bits: int, idx: torch.Tensor, out, stream) -> torch.Tensor:
+    nbytes_of, pack_raw_, _, _ = _LOWBIT[bits]
     _u8(idx, "idx")
     N, K = idx.shape
     if K % 128:
         raise ValueError("K must be a multiple of 128")
-    nbytes = any2_packed_bytes(N, K)
+    nbytes = nbytes_of(N, K)
     if out is None:
         out = torch.empty((nbytes,), dtype=torch.uint8, device=idx.device)
     _u8(out, "packed")
     if out.numel() != nbytes:
         raise ValueError(f"packed must hold {nbytes} bytes")
-    check(any2_pack_raw(_ptr(idx), _ptr(out), N, K, stream))
+    check(pack_raw_(_ptr(idx), _ptr(out), N, K, stream))
     return out
 
 
-def _check_packed2(packed: torch.Tensor, N: int, K: int) -> None:
+def _check_lowbit_packed(bits: int, packed: torch.Tensor, N: int, K: int) -> None:
     _u8(packed, "packed")
-    if packed.numel() != any2_packed_bytes(N, K):
-        raise ValueError(f"packed must hold any2_packed_bytes({N}, {K}) bytes")
+    if packed.numel() != _LOWBIT[bits][0](N, K):
+        raise ValueError(f"packed must hold any{bits}_packed_bytes({N}, {K}) bytes")
 
 
-def any2_dequant(packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor,
-                 beta: torch.Tensor, g: int, out: torch.Tensor | None = None,
-                 stream=None) -> torch.Tensor:
-    """bf16 weights [N, K] of an any2 layer (N from lut, K = alpha.shape[1] * g)."""
+def _lowbit_dequant(bits: int, packed, lut, alpha, beta, g: int, out, stream) -> torch.Tensor:
     _b16(lut, "lut"), _b16(alpha, "alpha"), _b16(beta, "beta")
     if lut.dim() != 2 or lut.shape[1] != 16:
         raise ValueError("lut must be [N, 16]")
@@ -360,21 +384,18 @@ def any2_dequant(packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor,
     if g <= 0 or alpha.dim() != 2 or alpha.shape[0] != N or beta.shape != alpha.shape:
         raise ValueError("alpha/beta must be [N, K/g]")
     K = alpha.shape[1] * g
-    _check_packed2(packed, N, K)
+    _check_lowbit_packed(bits, packed, N, K)
     if out is None:
         out = torch.empty((N, K), dtype=torch.bfloat16, device=lut.device)
     _b16(out, "w")
     if out.shape != (N, K):
         raise ValueError("w must be [N, K]")
-    check(any2_dequant_raw(_ptr(packed), _ptr(lut), _ptr(alpha), _ptr(beta), _ptr(out), N, K, g,
+    check(_LOWBIT[bits][2](_ptr(packed), _ptr(lut), _ptr(alpha), _ptr(beta), _ptr(out), N, K, g,
                            stream))
     return out
 
 
-def any2_gemm(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor,
-              beta: torch.Tensor, g: int, out: torch.Tensor | None = None,
-              stream=None) -> torch.Tensor:
-    """y [M, N] = x [M, K] * W^T with W an any2 layer (N from lut)."""
+def _lowbit_gemm(bits: int, x, packed, lut, alpha, beta, g: int, out, stream) -> torch.Tensor:
     _b16(x, "x"), _b16(lut, "lut"), _b16(alpha, "alpha"), _b16(beta, "beta")
     M, K = x.shape
     if lut.dim() != 2 or lut.shape[1] != 16:
@@ -382,15 +403,53 @@ def any2_gemm(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: t
     N = lut.shape[0]
     if g <= 0 or K % g or alpha.shape != (N, K // g) or beta.shape != (N, K // g):
         raise ValueError("alpha/beta must be [N, K/g]")
-    _check_packed2(packed, N, K)
+    _check_lowbit_packed(bits, packed, N, K)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _b16(out, "y")
     if out.shape != (M, N):
         raise ValueError("y must be [M, N]")
-    check(any2_gemm_raw(_ptr(x), _ptr(packed), _ptr(lut), _ptr(alpha), _ptr(beta), _ptr(out),
-                        M, N, K, g, stream))
+    check(_LOWBIT[bits][3](_ptr(x), _ptr(packed), _ptr(lut), _ptr(alpha), _ptr(beta), _ptr(out),
+                           M, N, K, g, stream))
     return out
+
+
+def any2_pack(idx: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """idx uint8 [N, K] (codes 0..3) -> packed uint8 [any2_packed_bytes(N, K)]."""
+    return _lowbit_pack(2, idx, out, stream)
+
+
+def any3_pack(idx: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """idx uint8 [N, K] (codes 0..7) -> packed uint8 [any3_packed_bytes(N, K)]."""
+    return _lowbit_pack(3, idx, out, stream)
+
+
+def any2_dequant(packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor,
+                 beta: torch.Tensor, g: int, out: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """bf16 weights [N, K] of an any2 layer (N from lut, K = alpha.shape[1] * g)."""
+    return _lowbit_dequant(2, packed, lut, alpha, beta, g, out, stream)
+
+
+def any3_dequant(packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor,
+                 beta: torch.Tensor, g: int, out: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """bf16 weights [N, K] of an any3 layer (N from lut, K = alpha.shape[1] * g)."""
+    return _lowbit_dequant(3, packed, lut, alpha, beta, g, out, stream)
+
+
+def any2_gemm(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor,
+              beta: torch.Tensor, g: int, out: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """y [M, N] = x [M, K] * W^T with W an any2 layer (N from lut)."""
+    return _lowbit_gemm(2, x, packed, lut, alpha, beta, g, out, stream)
+
+
+def any3_gemm(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor,
+              beta: torch.Tensor, g: int, out: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
+    """y [M, N] = x [M, K] * W^T with W an any3 layer (N from lut)."""
+    return _lowbit_gemm(3, x, packed, lut, alpha, beta, g, out, stream)
 
 
 def read_probe_raw(buf_ptr, nbytes: int, out_ptr, stream=None) -> int:

@@ -83,6 +83,13 @@ __device__ __forceinline__ u32x4_t load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t 
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
 }
+// the 12 bytes of an any3 tile slot, non-temporal, in the low three dwords
+__device__ __forceinline__ u32x4_t load12_nt(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+    const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 2);
+    return u32x4_t{v[0], v[1], v[2], 0u};
+}
 
 // ---------------------------------------------------------------------------
 // pack
@@ -263,6 +270,111 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void k_dequant2(const uint8_t* __res
         dst[q] = out[q];
 }
 
+// ---- any3 (3-bit codes) -----------------------------------------------------
+// Tiles of 16 rows x 128 k, 768 bytes: the 12-byte slot of lane l (bytes
+// 12l .. 12l+11 of tile (b, c)) holds row 16b + l%16, codes
+// k = 128c + 32(l/16) + 0..31 as 16 pair indices P_i = code[2i] | code[2i+1] << 3.
+// Byte j < 12 holds P_j in bits 0-5 and, in bits 6-7, bits 2(j/4)..2(j/4)+1
+// of P_{12 + j%4}.  Dword s < 3 of a slot is thus the pair bytes of the
+// lane's MFMA B operand s, and the fourth operand's pair bytes are gathered
+// from the top bits.
+
+// any3: the pair indices 12..15 of a 12-byte slot, one per byte, gathered
+// from bits 6-7 of the slot's bytes (pair 12 + t: bits 0-1 from byte t, 2-3
+// from byte 4 + t, 4-5 from byte 8 + t); bits 6-7 of the result are zero.
+__device__ __forceinline__ uint32_t any3_top_pairs(const u32x4_t& p)
+{
+    return ((p[0] >> 6) & 0x03030303u) | ((p[1] >> 4) & 0x0C0C0C0Cu) |
+           ((p[2] >> 2) & 0x30303030u);
+}
+
+__device__ __forceinline__ uint32_t pack3_pair(uint32_t codes2)   // two code bytes -> P
+{
+    return (codes2 & 7u) | ((codes2 >> 5) & 0x38u);
+}
+
+__global__ __launch_bounds__(PACK_THREADS) void k_pack3(const uint8_t* __restrict__ idx,
+                                                        uint8_t* __restrict__ packed, int N,
+                                                        int K, uint32_t slots)
+{
+    const uint32_t sidx = blockIdx.x * PACK_THREADS + threadIdx.x;   // 12-byte slot
+    if (sidx >= slots)
+        return;
+    const int Kc = K / TILE_K;
+    const uint32_t tile = sidx / 64;
+    const int l = static_cast<int>(sidx % 64);
+    const int b = static_cast<int>(tile / Kc);
+    const int c = static_cast<int>(tile % Kc);
+    const int n = b * TILE_ROWS + (l & 15);
+    uint32_t out[3] = {0u, 0u, 0u};
+    if (n < N) {
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
+            idx + static_cast<size_t>(n) * K + c * TILE_K + (l >> 4) * 32);
+        const u32x4_t v0 = src[0], v1 = src[1];
+        const uint32_t w[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        uint32_t P[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)   // codes 2i, 2i+1: bytes 2(i%2), +1 of dword i/2
+            P[i] = pack3_pair(w[i >> 1] >> (16 * (i & 1)));
+#pragma unroll
+        for (int jb = 0; jb < 12; ++jb) {
+            const uint32_t byte = P[jb] | (((P[12 + (jb & 3)] >> (2 * (jb >> 2))) & 3u) << 6);
+            out[jb >> 2] |= byte << (8 * (jb & 3));
+        }
+    }
+    uint32_t* dst = reinterpret_cast<uint32_t*>(packed + static_cast<size_t>(sidx) * 12);
+    dst[0] = out[0];
+    dst[1] = out[1];
+    dst[2] = out[2];
+}
+
+__global__ __launch_bounds__(64 * DQ_WAVES) void k_dequant3(const uint8_t* __restrict__ packed,
+                                                           const uint16_t* __restrict__ lut,
+                                                           const uint16_t* __restrict__ alpha,
+                                                           const uint16_t* __restrict__ beta,
+                                                           uint16_t* __restrict__ w, int N, int K,
+                                                           int g)
+{
+    __shared__ float sl[TILE_ROWS * 8];
+    const int Kc = K / TILE_K;
+    const int cgroups = (Kc + DQ_WAVES - 1) / DQ_WAVES;
+    const int b = blockIdx.x / cgroups;
+    const int c = (blockIdx.x % cgroups) * DQ_WAVES + (threadIdx.x >> 6);
+    if (threadIdx.x < TILE_ROWS * 8) {   // row t/8, entry t%8
+        const int t = threadIdx.x;
+        const int n = b * TILE_ROWS + (t >> 3);
+        sl[t] = n < N ? bf16_to_f32(lut[static_cast<size_t>(n) * 16 + (t & 7)]) : 0.f;
+    }
+    __syncthreads();
+    const int l = threadIdx.x & 63;
+    const int j = l & 15;
+    const int n = b * TILE_ROWS + j;
+    if (c >= Kc || n >= N)
+        return;
+    const int k0 = c * TILE_K + (l >> 4) * 32;
+    const int G = K / g;
+    const float a = bf16_to_f32(alpha[static_cast<size_t>(n) * G + k0 / g]);
+    const float bt = bf16_to_f32(beta[static_cast<size_t>(n) * G + k0 / g]);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(
+        packed + (static_cast<size_t>(b) * Kc + c) * (TILE_BYTES * 3 / 4) + l * 12);
+    const u32x4_t p = {src[0], src[1], src[2], 0u};
+    const uint32_t top = any3_top_pairs(p);
+    const float* L = sl + j * 8;
+    u32x4_t out[4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {   // pair i: codes 2i, 2i+1
+        const uint32_t d = i < 12 ? p[i >> 2] : top;
+        const uint32_t P = (d >> (8 * (i & 3))) & 0x3Fu;
+        const float lo = fmaf(a, L[P & 7u], bt);
+        const float hi = fmaf(a, L[P >> 3], bt);
+        out[i >> 2][i & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    }
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(w + static_cast<size_t>(n) * K + k0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        dst[q] = out[q];
+}
+
 // ---------------------------------------------------------------------------
 // gemm
 // ---------------------------------------------------------------------------
@@ -307,12 +419,18 @@ __global__ __launch_bounds__(256) void k_zero(uint16_t* __restrict__ y, size_t n
 constexpr int GW = 8;                   // waves per workgroup
 
 // Weight formats of the GEMM kernels: the any4 table path, plain int4 (the
-// code is the value), and any2 (2-bit codes, four per byte, 512-byte tiles;
-// a byte looks up four table values at once).
+// code is the value), any2 (2-bit codes, four per byte, 512-byte tiles; a
+// byte looks up four table values at once) and any3 (3-bit codes, a 6-bit
+// pair index per byte plus four pairs spread over the bytes' top bits,
+// 768-byte tiles; looked up like any4 pairs).
 constexpr int FMT_ANY4 = 0;
 constexpr int FMT_INT4 = 1;
 constexpr int FMT_ANY2 = 2;
-constexpr int tile_bytes(int fmt) { return fmt == FMT_ANY2 ? TILE_BYTES / 2 : TILE_BYTES; }
+constexpr int FMT_ANY3 = 3;
+constexpr int tile_bytes(int fmt)
+{
+    return fmt == FMT_ANY2 ? TILE_BYTES / 2 : fmt == FMT_ANY3 ? TILE_BYTES * 3 / 4 : TILE_BYTES;
+}
 constexpr int GT = 64 * GW;
 constexpr int TAB_BYTES = 256 * 256;    // 256 entries x 2 tables x 32 slots x 4 B
 constexpr int MAX_G = 512;              // K/g: the alpha/beta staging of k_gemm_kb
@@ -344,7 +462,11 @@ __device__ __forceinline__ T& lds_at(uint8_t* smem, uint32_t byte_addr)
 // in LDS at `lut_off` as [16 rows][16] 16-bit values.  Thread t of the W*64
 // writes slot t % 32 (row (t % 32) % 16) of the entries lo + 16*hi,
 // lo = (t / 32) % 16, for its share of the 16 hi.
-template <int W>
+//
+// any3 (A3): entry e holds (L[e & 7], L[(e >> 3) & 7]): the low 6 bits of the
+// byte are the pair of 3-bit codes and bits 6-7 select one of four identical
+// copies, so a byte whose top bits carry other data needs no masking.
+template <int W, bool A3 = false>
 __device__ __forceinline__ void build_table(uint8_t* smem, uint32_t lut_off, uint32_t tab_dw,
                                             int tid)
 {
@@ -355,10 +477,18 @@ __device__ __forceinline__ void build_table(uint8_t* smem, uint32_t lut_off, uin
     const uint32_t row = lut_off + (st & 15) * 32;
     const u32x4_t q0 = lds_at<u32x4_t>(smem, row);
     const u32x4_t q1 = lds_at<u32x4_t>(smem, row + 16);
-    const uint32_t ll = lds_at<uint16_t>(smem, row + 2 * lo);
+    const uint32_t ll = lds_at<uint16_t>(smem, row + 2 * (A3 ? lo & 7 : lo));
     const uint32_t Lw[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
     uint32_t* tw = reinterpret_cast<uint32_t*>(smem) + tab_dw + lo * 64 + st;
-    if constexpr (HPT == 16) {
+    if constexpr (A3) {
+        static_assert(HPT == 16, "one thread per (slot, lo) pair");
+        // entry hi << 4 | lo: the second code is (2*hi + lo/8) & 7, the
+        // half (lo/8) of dword hi & 3 of the row
+        const uint32_t sel = (lo >> 3) ? 0x07060100u : 0x05040100u;
+#pragma unroll
+        for (int hi = 0; hi < 16; ++hi)
+            tw[hi * 16 * 64] = __builtin_amdgcn_perm(Lw[hi & 3], ll, sel);
+    } else if constexpr (HPT == 16) {
 #pragma unroll
         for (int hi = 0; hi < 16; ++hi)
             tw[hi * 16 * 64] =
@@ -605,6 +735,7 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
 {
     constexpr bool I4 = FMT == FMT_INT4;
     constexpr bool A2 = FMT == FMT_ANY2;
+    constexpr bool A3 = FMT == FMT_ANY3;
     constexpr uint32_t TB = tile_bytes(FMT);
     using Cfg = KmCfg<NBG>;
     constexpr int C = KM_C;
@@ -681,7 +812,8 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
         if constexpr (A2)
             build_table2<GW>(smem, Cfg::LUTS + bb * 512, (bb >> 1) * 65536 + (bb & 1) * 128, tid);
         else if constexpr (!I4)
-            build_table<GW>(smem, Cfg::LUTS + bb * 512, (bb >> 1) * 16384 + (bb & 1) * 32, tid);
+            build_table<GW, A3>(smem, Cfg::LUTS + bb * 512, (bb >> 1) * 16384 + (bb & 1) * 32,
+                                tid);
     };
 
     // ---- ring: tile v of group gi is chunk cbase + v / NBG of block
@@ -702,7 +834,9 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
         const uint32_t uo =
             (static_cast<uint32_t>(r + blk * Gs) * static_cast<uint32_t>(Kc) + c) * TB |
             (static_cast<uint32_t>(!live) << 31);
-        pb[uu % D] = A2 ? load8_nt(rp, off2(tile_lane, uo)) : load16_nt(rp, off2(tile_lane, uo));
+        pb[uu % D] = A2   ? load8_nt(rp, off2(tile_lane, uo))
+                     : A3 ? load12_nt(rp, off2(tile_lane, uo))
+                          : load16_nt(rp, off2(tile_lane, uo));
         if constexpr (XSTREAM) {
             if (v % NBG == NBG - 1) {
                 const bool xl = gg < ngroups && c < Kc;
@@ -827,6 +961,8 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
                 const int s = u / NBG;
                 const int bb = u % NBG;
                 const u32x4_t p = pb[u % D];
+                // the pair bytes of the four B operands (any3: the fourth from the top bits)
+                const u32x4_t pd = A3 ? u32x4_t{p[0], p[1], p[2], any3_top_pairs(p)} : p;
                 // a chunk past K reads the zero zone instead of its table
                 const uint32_t sv =
                     s1[bb >> 1] + (cbase + s < Kc ? 0u : Cfg::ZERO - (bb >> 1) * 65536u);
@@ -851,7 +987,7 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
 #pragma unroll
                         for (int jb = 0; jb < 4; ++jb)
                             bw[h][s4][jb] = lds_at<uint32_t>(
-                                smem, __builtin_amdgcn_perm(p[s4], sv,
+                                smem, __builtin_amdgcn_perm(pd[s4], sv,
                                                             0x0C020000u | ((4u + jb) << 8)) +
                                           (bb & 1) * 128);
                     }
@@ -976,6 +1112,7 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
 {
     constexpr bool I4 = FMT == FMT_INT4;
     constexpr bool A2 = FMT == FMT_ANY2;
+    constexpr bool A3 = FMT == FMT_ANY3;
     constexpr uint32_t TB = tile_bytes(FMT);
     using Cfg = KbCfg<NBG, XL>;
     constexpr int DS = Cfg::DS;
@@ -1068,7 +1205,8 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
         if constexpr (A2)
             build_table2<GW>(smem, Cfg::LUTS + bb * 512, (bb >> 1) * 65536 + (bb & 1) * 128, tid);
         else if constexpr (!I4)
-            build_table<GW>(smem, Cfg::LUTS + bb * 512, (bb >> 1) * 16384 + (bb & 1) * 32, tid);
+            build_table<GW, A3>(smem, Cfg::LUTS + bb * 512, (bb >> 1) * 16384 + (bb & 1) * 32,
+                                tid);
     };
 
     // ---- ring.  Tile u of a body whose first step is (group gc, padded step
@@ -1092,7 +1230,9 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
         const uint32_t uo =
             (static_cast<uint32_t>(r + blk * Gs) * static_cast<uint32_t>(Kc) + c) * TB |
             (static_cast<uint32_t>(!live) << 31);
-        pb[uu % D] = A2 ? load8_nt(rp, off2(tile_lane, uo)) : load16_nt(rp, off2(tile_lane, uo));
+        pb[uu % D] = A2   ? load8_nt(rp, off2(tile_lane, uo))
+                     : A3 ? load12_nt(rp, off2(tile_lane, uo))
+                          : load16_nt(rp, off2(tile_lane, uo));
         if (!XL && bb == NBG - 1) {
             const bool xl = gg < ngroups && st < C && c < Kc;
             const uint32_t xc =
@@ -1217,6 +1357,7 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
                 const int st = sc + u / NBG;
                 const int bb = u % NBG;
                 const u32x4_t p = pb[u];
+                const u32x4_t pd = A3 ? u32x4_t{p[0], p[1], p[2], any3_top_pairs(p)} : p;
                 const int c = cbase + st;
                 const bool live = gc * NBG + bb < nblk && st < C && c < Kc;
                 if constexpr (!I4) {
@@ -1240,7 +1381,7 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
 #pragma unroll
                             for (int jb = 0; jb < 4; ++jb)
                                 bw[h][s4][jb] = lds_at<uint32_t>(
-                                    smem, __builtin_amdgcn_perm(p[s4], sv,
+                                    smem, __builtin_amdgcn_perm(pd[s4], sv,
                                                                 0x0C020000u | ((4u + jb) << 8)) +
                                               (bb & 1) * 128);
                     }
@@ -1317,10 +1458,12 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
 constexpr int BIG_BN = 64;
 constexpr int BIG_LD = TILE_K + 8;   // padded row length in bf16
 
-template <int BM, bool A2>
+template <int BM, int FMT>
 __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
 {
-    constexpr uint32_t TB = A2 ? TILE_BYTES / 2 : TILE_BYTES;
+    constexpr bool A2 = FMT == FMT_ANY2;
+    constexpr bool A3 = FMT == FMT_ANY3;
+    constexpr uint32_t TB = tile_bytes(FMT);
     constexpr int MTW = BM / 32;   // 16-row m tiles per wave (the wave's BM/2 rows)
     __shared__ __attribute__((aligned(16))) uint16_t xs[BM * BIG_LD];
     __shared__ __attribute__((aligned(16))) uint16_t ws[BIG_BN * BIG_LD];
@@ -1375,6 +1518,9 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
                 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
                 const u32x2_t v = *reinterpret_cast<const u32x2_t*>(src);
                 pk = u32x4_t{v[0], v[1], 0u, 0u};
+            } else if constexpr (A3) {
+                const uint32_t* v = reinterpret_cast<const uint32_t*>(src);
+                pk = u32x4_t{v[0], v[1], v[2], 0u};
             } else {
                 pk = *reinterpret_cast<const u32x4_t*>(src);
             }
@@ -1412,6 +1558,15 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
                             const int d = 2 * i + t;
                             out[d >> 2][d & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
                         }
+                    }
+                } else if constexpr (A3) {   // 16 pair indices: dwords 0-2, then the top bits
+                    const uint32_t top = any3_top_pairs(pk);
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const uint32_t P = ((q < 12 ? pk[q >> 2] : top) >> (8 * (q & 3))) & 0x3Fu;
+                        const float lo = fmaf(a, L[P & 7u], bt);
+                        const float hi = fmaf(a, L[P >> 3], bt);
+                        out[q >> 2][q & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
                     }
                 } else {
 #pragma unroll
@@ -1723,12 +1878,28 @@ static void launch_decode(const GemmArgs& a, int fmt, hipStream_t stream)
         launch_decode_fmt<FMT_INT4>(a, stream);
     else if (fmt == FMT_ANY2)
         launch_decode_fmt<FMT_ANY2>(a, stream);
+    else if (fmt == FMT_ANY3)
+        launch_decode_fmt<FMT_ANY3>(a, stream);
     else
         launch_decode_fmt<FMT_ANY4>(a, stream);
 }
 
-// Argument checks and dispatch shared by any4_gemm (table lookup) and
-// any4_gemm_int4 (the 4-bit code itself is the value; lut unused).
+template <int BM>
+static void launch_big(const GemmArgs& a, int fmt, hipStream_t stream)
+{
+    const dim3 gd(static_cast<unsigned>((a.N + BIG_BN - 1) / BIG_BN),
+                  static_cast<unsigned>((a.M + BM - 1) / BM));
+    if (fmt == FMT_ANY2)
+        hipLaunchKernelGGL((k_gemm_big<BM, FMT_ANY2>), gd, dim3(256), 0, stream, a);
+    else if (fmt == FMT_ANY3)
+        hipLaunchKernelGGL((k_gemm_big<BM, FMT_ANY3>), gd, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_gemm_big<BM, FMT_ANY4>), gd, dim3(256), 0, stream, a);
+}
+
+// Argument checks and dispatch shared by any4_gemm (table lookup),
+// any4_gemm_int4 (the 4-bit code itself is the value; lut unused), any2_gemm
+// and any3_gemm.
 static any4_status gemm_call(int fmt, const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
                       const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
                       int64_t N, int64_t K, int64_t g, hipStream_t stream)
@@ -1781,24 +1952,73 @@ static any4_status gemm_call(int fmt, const uint16_t* x, const uint8_t* packed, 
         return launched();
     }
     if (M > 16) {
-        if (M <= 64) {
-            const dim3 gd(static_cast<unsigned>((N + BIG_BN - 1) / BIG_BN),
-                          static_cast<unsigned>((M + 63) / 64));
-            if (fmt == FMT_ANY2)
-                hipLaunchKernelGGL((k_gemm_big<64, true>), gd, dim3(256), 0, stream, a);
-            else
-                hipLaunchKernelGGL((k_gemm_big<64, false>), gd, dim3(256), 0, stream, a);
-        } else {
-            const dim3 gd(static_cast<unsigned>((N + BIG_BN - 1) / BIG_BN),
-                          static_cast<unsigned>((M + 127) / 128));
-            if (fmt == FMT_ANY2)
-                hipLaunchKernelGGL((k_gemm_big<128, true>), gd, dim3(256), 0, stream, a);
-            else
-                hipLaunchKernelGGL((k_gemm_big<128, false>), gd, dim3(256), 0, stream, a);
-        }
+        // the tiled kernel; int4 is its 4-bit path with no table (lut null)
+        if (M <= 64)
+            launch_big<64>(a, fmt, stream);
+        else
+            launch_big<128>(a, fmt, stream);
         return launched();
     }
     launch_decode(a, fmt, stream);
+    return launched();
+}
+
+// any2 / any3 pack and dequant: checks as any4_pack / any4_dequant, then
+// the kernel of the format (bits = 2 or 3).
+static any4_status lowbit_pack(int bits, const uint8_t* idx, uint8_t* packed, int64_t N,
+                               int64_t K, hipStream_t stream)
+{
+    if (N < 0 || K < 0 || K % TILE_K != 0)
+        return ANY4_E_SHAPE;
+    if (N == 0 || K == 0)
+        return ANY4_OK;
+    if (any4_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31) ||
+        static_cast<size_t>(N) * K >= (static_cast<size_t>(1) << 40))
+        return ANY4_E_SHAPE;
+    if (!idx || !packed)
+        return ANY4_E_NULL;
+    if (!aligned(idx, 16) || !aligned(packed, 16))
+        return ANY4_E_ALIGN;
+    const size_t slot_bytes = bits == 2 ? 8 : 12;
+    const size_t nbytes = bits == 2 ? any2_packed_bytes(N, K) : any3_packed_bytes(N, K);
+    const uint32_t slots = static_cast<uint32_t>(nbytes / slot_bytes);
+    const uint32_t blocks = (slots + PACK_THREADS - 1) / PACK_THREADS;
+    (void)hipGetLastError();
+    if (bits == 2)
+        hipLaunchKernelGGL(k_pack2, dim3(blocks), dim3(PACK_THREADS), 0, stream, idx, packed,
+                           static_cast<int>(N), static_cast<int>(K), slots);
+    else
+        hipLaunchKernelGGL(k_pack3, dim3(blocks), dim3(PACK_THREADS), 0, stream, idx, packed,
+                           static_cast<int>(N), static_cast<int>(K), slots);
+    return launched();
+}
+
+static any4_status lowbit_dequant(int bits, const uint8_t* packed, const uint16_t* lut,
+                                  const uint16_t* alpha, const uint16_t* beta, uint16_t* w,
+                                  int64_t N, int64_t K, int64_t g, hipStream_t stream)
+{
+    if (N < 0 || !group_ok(K, g))
+        return ANY4_E_SHAPE;
+    if (N == 0 || K == 0)
+        return ANY4_OK;
+    if (any4_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31))
+        return ANY4_E_SHAPE;
+    if (!packed || !lut || !alpha || !beta || !w)
+        return ANY4_E_NULL;
+    if (!aligned(packed, 16) || !aligned(w, 16) || !aligned(lut, 2) || !aligned(alpha, 2) ||
+        !aligned(beta, 2))
+        return ANY4_E_ALIGN;
+    const int64_t Kc = K / TILE_K;
+    const dim3 gd(static_cast<unsigned>(row_blocks(N) * ((Kc + DQ_WAVES - 1) / DQ_WAVES)));
+    (void)hipGetLastError();
+    if (bits == 2)
+        hipLaunchKernelGGL(k_dequant2, gd, dim3(64 * DQ_WAVES), 0, stream, packed, lut, alpha,
+                           beta, w, static_cast<int>(N), static_cast<int>(K),
+                           static_cast<int>(g));
+    else
+        hipLaunchKernelGGL(k_dequant3, gd, dim3(64 * DQ_WAVES), 0, stream, packed, lut, alpha,
+                           beta, w, static_cast<int>(N), static_cast<int>(K),
+                           static_cast<int>(g));
     return launched();
 }
 
@@ -1929,50 +2149,37 @@ size_t any2_packed_bytes(int64_t N, int64_t K)
     return static_cast<size_t>(row_blocks(N)) * TILE_ROWS * static_cast<size_t>(K / 4);
 }
 
+size_t any3_packed_bytes(int64_t N, int64_t K)
+{
+    if (N < 0 || K < 0 || K % TILE_K != 0)
+        return 0;
+    return static_cast<size_t>(row_blocks(N)) * TILE_ROWS * static_cast<size_t>(K / 8 * 3);
+}
+
 any4_status any2_pack(const uint8_t* idx, uint8_t* packed, int64_t N, int64_t K,
                       hipStream_t stream)
 {
-    if (N < 0 || K < 0 || K % TILE_K != 0)
-        return ANY4_E_SHAPE;
-    if (N == 0 || K == 0)
-        return ANY4_OK;
-    if (any2_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31) ||
-        static_cast<size_t>(N) * K >= (static_cast<size_t>(1) << 40))
-        return ANY4_E_SHAPE;
-    if (!idx || !packed)
-        return ANY4_E_NULL;
-    if (!aligned(idx, 16) || !aligned(packed, 16))
-        return ANY4_E_ALIGN;
-    const uint32_t slots = static_cast<uint32_t>(any2_packed_bytes(N, K) / 8);
-    const uint32_t blocks = (slots + PACK_THREADS - 1) / PACK_THREADS;
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(k_pack2, dim3(blocks), dim3(PACK_THREADS), 0, stream, idx, packed,
-                       static_cast<int>(N), static_cast<int>(K), slots);
-    return launched();
+    return lowbit_pack(2, idx, packed, N, K, stream);
+}
+
+any4_status any3_pack(const uint8_t* idx, uint8_t* packed, int64_t N, int64_t K,
+                      hipStream_t stream)
+{
+    return lowbit_pack(3, idx, packed, N, K, stream);
 }
 
 any4_status any2_dequant(const uint8_t* packed, const uint16_t* lut, const uint16_t* alpha,
                          const uint16_t* beta, uint16_t* w, int64_t N, int64_t K, int64_t g,
                          hipStream_t stream)
 {
-    if (N < 0 || !group_ok(K, g))
-        return ANY4_E_SHAPE;
-    if (N == 0 || K == 0)
-        return ANY4_OK;
-    if (any4_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31))
-        return ANY4_E_SHAPE;
-    if (!packed || !lut || !alpha || !beta || !w)
-        return ANY4_E_NULL;
-    if (!aligned(packed, 16) || !aligned(w, 16) || !aligned(lut, 2) || !aligned(alpha, 2) ||
-        !aligned(beta, 2))
-        return ANY4_E_ALIGN;
-    const int64_t Kc = K / TILE_K;
-    const int64_t blocks = row_blocks(N) * ((Kc + DQ_WAVES - 1) / DQ_WAVES);
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(k_dequant2, dim3(static_cast<unsigned>(blocks)), dim3(64 * DQ_WAVES), 0,
-                       stream, packed, lut, alpha, beta, w, static_cast<int>(N),
-                       static_cast<int>(K), static_cast<int>(g));
-    return launched();
+    return lowbit_dequant(2, packed, lut, alpha, beta, w, N, K, g, stream);
+}
+
+any4_status any3_dequant(const uint8_t* packed, const uint16_t* lut, const uint16_t* alpha,
+                         const uint16_t* beta, uint16_t* w, int64_t N, int64_t K, int64_t g,
+                         hipStream_t stream)
+{
+    return lowbit_dequant(3, packed, lut, alpha, beta, w, N, K, g, stream);
 }
 
 any4_status any2_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
@@ -1980,6 +2187,13 @@ any4_status any2_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* 
                       int64_t N, int64_t K, int64_t g, hipStream_t stream)
 {
     return gemm_call(FMT_ANY2, x, packed, lut, alpha, beta, y, M, N, K, g, stream);
+}
+
+any4_status any3_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
+                      const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
+                      int64_t N, int64_t K, int64_t g, hipStream_t stream)
+{
+    return gemm_call(FMT_ANY3, x, packed, lut, alpha, beta, y, M, N, K, g, stream);
 }
 
 any4_status any4_quantize(const float* W, const float* ex, uint8_t* idx, uint16_t* lut,

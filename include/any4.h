@@ -1,6 +1,6 @@
 /*
  * any4.h -- C ABI of libany4.so, the MI355X (gfx950) any4 dequantize-GEMM
- * (with plain int4, the any2 2-bit variant and the any4 quantiser).
+ * (with plain int4, the any2 and any3 variants and the any4 quantiser).
  *
  * any4 (the 10100.com any4 explainer, section 二) stores each weight of a
  * row as a 4-bit index into that row's 16-entry bf16 lookup table; each
@@ -191,6 +191,40 @@ any4_status any2_dequant(const uint8_t* packed, const uint16_t* lut, const uint1
                          const uint16_t* beta, uint16_t* w, int64_t N, int64_t K, int64_t g,
                          hipStream_t stream);
 any4_status any2_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
+                      const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
+                      int64_t N, int64_t K, int64_t g, hipStream_t stream);
+
+/*
+ * any3 -- the 3-bit variant at 3 bits per stored weight (the paper's abstract
+ * names any3): each weight is a 3-bit code into its row's table, of which
+ * only entries 0..7 are read (entries 8..15 are ignored; any4_quantize with
+ * bits = 3 writes such tables).  Codes are stored in tiles of 16 rows x 128 k
+ * (any3_packed_bytes(N, K) bytes):
+ *     tile (b, c) covers rows 16b..16b+15 and k 128c..128c+127 and starts at
+ *     byte (b * K/128 + c) * 768;
+ *     the 12 bytes 12*l .. 12*l+11 of a tile (lane l = 0..63) hold row
+ *     n = 16b + (l % 16), k = 128c + 32*(l / 16) + 0..31, as 16 pair indices
+ *         P_i = code[n][k+2i] | code[n][k+2i+1] << 3      (i = 0..15);
+ *     byte j (j = 0..11) holds P_j in bits 0-5, and in bits 6-7 the two bits
+ *     2*(j/4), 2*(j/4)+1 of P_{12 + j%4};
+ *     rows n >= N are zero bytes.
+ * (So dwords 0-2 of a lane's 12 bytes carry the pair indices of its first
+ * three 32-k MFMA operands one per byte, and the fourth operand's are
+ * gathered from the bytes' top bits: one load of 12 bytes per lane.)
+ * any3_pack, any3_dequant and any3_gemm take the same arguments and follow
+ * the same conventions, checks and errors as any2_pack, any2_dequant and
+ * any2_gemm, with idx read as codes 0..7 (bits above 2 ignored):
+ *     w[n][k] = bf16_rne( fp32( alpha[n][k/g] * lut[n][code[n][k]] + beta[n][k/g] ) )
+ *     y[m][n] = bf16_rne( sum_k x[m][k] * w[n][k] )   (same bound as any4_gemm)
+ * Returns of any3_packed_bytes: ceil(N/16) * 16 * 3K/8, or 0 as any4_packed_bytes.
+ */
+size_t any3_packed_bytes(int64_t N, int64_t K);
+any4_status any3_pack(const uint8_t* idx, uint8_t* packed, int64_t N, int64_t K,
+                      hipStream_t stream);
+any4_status any3_dequant(const uint8_t* packed, const uint16_t* lut, const uint16_t* alpha,
+                         const uint16_t* beta, uint16_t* w, int64_t N, int64_t K, int64_t g,
+                         hipStream_t stream);
+any4_status any3_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
                       const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
                       int64_t N, int64_t K, int64_t g, hipStream_t stream);
 

@@ -216,6 +216,49 @@ def untile2(t, N: int, K: int) -> np.ndarray:
     return np.ascontiguousarray(t).reshape(NB * TILE_ROWS, K // 4)[:N]
 
 
+# --------------------------------------------------------------------------
+# any3: 3-bit codes in the GPU library's 768-byte tiles (the any4 paper's
+# abstract names any3; the storage is this library's own, specified in
+# include/any4.h)
+# --------------------------------------------------------------------------
+def tiled3_bytes(N: int, K: int) -> int:
+    """Bytes of the any3 tile layout: rows padded to a multiple of 16, 3K/8 bytes each."""
+    return -(-N // TILE_ROWS) * TILE_ROWS * (K // 8 * 3)
+
+
+def tile3(idx) -> np.ndarray:
+    """Codes [N, K] (0..7; higher bits ignored) -> the any3 tile layout (flat
+    uint8).  Per lane slot (row n, 32 consecutive k): pair indices
+    P_i = c[2i] | c[2i+1] << 3 for i = 0..15; byte j < 12 is P_j plus, in bits
+    6-7, bits 2(j//4) and 2(j//4)+1 of P_{12 + j%4}.  Slots are ordered
+    [row blocks][K/128 chunks][4 quarters of 32 k][16 rows]."""
+    idx = _c(idx, np.uint8)
+    N, K = idx.shape
+    assert K % TILE_K == 0
+    NB = -(-N // TILE_ROWS)
+    codes = np.zeros((NB * TILE_ROWS, K), np.uint8)
+    codes[:N] = idx & 7
+    q = codes.reshape(NB, TILE_ROWS, K // TILE_K, 4, 16, 2)
+    P = q[..., 0] | (q[..., 1] << 3)                      # [NB][16][Kc][4][16 pairs]
+    j = np.arange(12)
+    top = (P[..., 12 + j % 4] >> (2 * (j // 4))) & 3      # the top-bit parts, byte by byte
+    B = (P[..., :12] | (top << 6)).astype(np.uint8)       # [NB][16][Kc][4][12]
+    return np.ascontiguousarray(B.transpose(0, 2, 3, 1, 4)).reshape(-1)
+
+
+def untile3(t, N: int, K: int) -> np.ndarray:
+    """Inverse of tile3: the codes [N, K] (padding rows dropped)."""
+    NB = -(-N // TILE_ROWS)
+    B = _c(t, np.uint8).reshape(NB, K // TILE_K, 4, TILE_ROWS, 12).transpose(0, 3, 1, 2, 4)
+    P = np.empty(B.shape[:-1] + (16,), np.uint8)
+    P[..., :12] = B & 63
+    for t4 in range(4):
+        P[..., 12 + t4] = ((B[..., t4] >> 6) | ((B[..., 4 + t4] >> 6) << 2) |
+                           ((B[..., 8 + t4] >> 6) << 4))
+    codes = np.stack([P & 7, P >> 3], axis=-1)            # [NB][16][Kc][4][16][2]
+    return np.ascontiguousarray(codes).reshape(NB * TILE_ROWS, K)[:N]
+
+
 def dequant_one(alpha: int, lut_value: int, beta: int) -> int:
     return int(_load().orc_dequant_one(alpha, lut_value, beta))
 

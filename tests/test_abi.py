@@ -15,7 +15,7 @@ def _declared_functions():
     with open(os.path.join(ROOT, "include", "any4.h")) as f:
         src = f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(any[24]_[a-z0-9_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(any[234]_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_binding_exports():
@@ -140,6 +140,25 @@ def test_any2_errors_and_sizes():
     assert any4.any2_gemm_raw(A, A, None, A, A, A, 1, 16, 128, 128, stream=0) == 1
     assert any4.any2_gemm_raw(A, A, A, A + 2, A, A, 1, 16, 128, 128, stream=0) == 3
     assert any4.any2_gemm_raw(None, None, None, None, None, None, 0, 16, 128, 128, stream=0) == 0
+
+
+def test_any3_errors_and_sizes():
+    assert any4.any3_packed_bytes(16, 128) == 768
+    assert any4.any3_packed_bytes(17, 256) == 32 * 96
+    assert any4.any3_packed_bytes(5, 100) == 0
+    assert any4.any3_packed_bytes(-1, 128) == 0
+    assert any4.any3_pack_raw(A, A, 4, 64, stream=0) == 2
+    assert any4.any3_pack_raw(None, A, 4, 128, stream=0) == 1
+    assert any4.any3_pack_raw(A + 1, A, 4, 128, stream=0) == 3
+    assert any4.any3_pack_raw(None, None, 0, 128, stream=0) == 0
+    assert any4.any3_dequant_raw(A, A, A, A, A, 4, 256, 192, stream=0) == 2
+    assert any4.any3_dequant_raw(A, None, A, A, A, 4, 256, 128, stream=0) == 1
+    assert any4.any3_dequant_raw(A, A, A, A, A + 8, 4, 256, 128, stream=0) == 3
+    assert any4.any3_gemm_raw(A, A, A, A, A, A, 1, 16, 384, 256, stream=0) == 2
+    assert any4.any3_gemm_raw(A, A, A, A, A, A, 17 + 65535 * 64, 16, 128, 128, stream=0) == 2
+    assert any4.any3_gemm_raw(A, A, None, A, A, A, 1, 16, 128, 128, stream=0) == 1
+    assert any4.any3_gemm_raw(A, A, A, A + 2, A, A, 1, 16, 128, 128, stream=0) == 3
+    assert any4.any3_gemm_raw(None, None, None, None, None, None, 0, 16, 128, 128, stream=0) == 0
 
 
 def test_read_probe_errors():

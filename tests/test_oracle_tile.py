@@ -101,3 +101,62 @@ def test_pack2_round_trip(N, K):
     b = np.arange(256, dtype=np.uint8).reshape(1, 256)
     u = oracle.unpack2(b, 1024).reshape(256, 4)
     assert np.array_equal(u[:, 0] | (u[:, 1] << 2) | (u[:, 2] << 4) | (u[:, 3] << 6), b[0])
+
+
+# ---- any3: 3-bit codes, 768-byte tiles of 16 rows x 128 k -------------------
+def _tile3_by_bits(idx: np.ndarray) -> np.ndarray:
+    """The any3 layout of include/any4.h, bit by bit: code bit e of
+    code[n][k] (n = 16b + l % 16, k = 128c + 32*(l // 16) + r) is bit
+    q = 3*(r % 2) + e of pair i = r // 2; pair i < 12 keeps bit q in byte i,
+    bit q; pair 12 + t keeps bit q in byte 4*(q // 2) + t, bit 6 + q % 2."""
+    N, K = idx.shape
+    NB, Kc = -(-N // 16), K // 128
+    out = np.zeros(NB * Kc * 768, np.uint8)
+    for n in range(N):
+        b, row = divmod(n, 16)
+        for k in range(K):
+            c, kk = divmod(k, 128)
+            l = 16 * (kk // 32) + row
+            r = kk % 32
+            i = r // 2
+            for e in range(3):
+                if not (int(idx[n, k]) >> e) & 1:
+                    continue
+                q = 3 * (r % 2) + e
+                if i < 12:
+                    byte, bit = i, q
+                else:
+                    byte, bit = 4 * (q // 2) + (i - 12), 6 + q % 2
+                out[(b * Kc + c) * 768 + 12 * l + byte] |= np.uint8(1 << bit)
+    return out
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (16, 128), (17, 256), (20, 384)])
+def test_tile3_matches_the_per_bit_definition(N, K):
+    rng = np.random.default_rng(N * 11 + K)
+    idx = rng.integers(0, 256, size=(N, K), dtype=np.uint8)   # bits above 2 are ignored
+    t = oracle.tile3(idx)
+    assert t.size == oracle.tiled3_bytes(N, K) == -(-N // 16) * 16 * K * 3 // 8
+    assert np.array_equal(t, _tile3_by_bits(idx & 7))
+
+
+@pytest.mark.parametrize("N,K", [(5, 128), (33, 640), (16, 4096)])
+def test_tile3_round_trip(N, K):
+    rng = np.random.default_rng(N + 5 * K)
+    idx = rng.integers(0, 8, size=(N, K), dtype=np.uint8)
+    assert np.array_equal(oracle.untile3(oracle.tile3(idx), N, K), idx)
+
+
+def test_tile3_worked_slot():
+    """Row 0 with code[k] = k % 8, worked by hand from the layout: the pairs
+    of lane 0 are 8, 26, 44, 62 (repeated), so pairs 12..15 are 8, 26, 44,
+    62 and their top-bit parts are (0, 2, 0), (2, 2, 1), (0, 3, 2) and
+    (2, 3, 3) for bytes (j, 4+j, 8+j)."""
+    idx = (np.arange(128) % 8).astype(np.uint8)[None, :]
+    t = oracle.tile3(idx)
+    assert list(t[:12]) == [8, 154, 44, 190, 136, 154, 236, 254, 8, 90, 172, 254]
+    # rows 1..15 are padding: their slots (lanes 1..15, 17..31, ...) are zero
+    slots = t.reshape(4, 16, 12)
+    assert not slots[:, 1:, :].any()
+    # the four quarters of row 0 hold the same codes (k % 8 repeats every 32)
+    assert all(np.array_equal(slots[q, 0], slots[0, 0]) for q in range(4))
