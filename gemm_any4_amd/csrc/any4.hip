@@ -5,9 +5,9 @@
 // weights of a row has a scale alpha and an offset beta (step 1, "分组缩放"), so
 // w = alpha * LUT_row[idx] + beta; the matmul y = x * W^T runs at decode batch
 // sizes 1..16 (section 三).  Also here: the same product for plain int4 and for
-// any2 (2-bit codes, the any4 paper's abstract), larger batches, and the
-// quantiser that learns the tables (step 2, E-step / M-step).  The C ABI is
-// declared in include/any4.h.
+// any2 and any3 (2- and 3-bit codes, the any4 paper's abstract), larger
+// batches, and the quantiser that learns the tables (step 2, E-step /
+// M-step).  The C ABI is declared in include/any4.h.
 //
 // Packed tile layout (written by k_pack, read by k_dequant and the GEMMs)
 //   The weights are cut into tiles of 16 rows x 128 k.  A tile is 1 KB and is
@@ -16,11 +16,14 @@
 //   in the low nibble.  Tiles are stored row-block major: tile (b, c) of row
 //   block b (rows 16b..16b+15) and k-chunk c (k 128c..128c+127) starts at byte
 //   (b * K/128 + c) * 1024.  Rows past N are zero padding.  any2 tiles are the
-//   same with four 2-bit codes per byte: 512 bytes, an 8-byte load per lane.
+//   same with four 2-bit codes per byte: 512 bytes, an 8-byte load per lane;
+//   any3 tiles hold 16 six-bit pair indices per lane in 12 bytes: 768 bytes,
+//   a 12-byte load per lane.
 //
 // Kernels
-//   k_pack, k_pack2        idx[N][K] u8 -> tiles, one tile slot per thread.
-//   k_dequant, k_dequant2  w = bf16(fma(alpha, LUT[idx], beta)), one slot per thread.
+//   k_pack, k_pack2, k_pack3        idx[N][K] u8 -> tiles, one tile slot per thread.
+//   k_dequant, k_dequant2, k_dequant3  w = bf16(fma(alpha, LUT[idx], beta)), one slot
+//                          per thread.
 //   k_gemm_km, k_gemm_kb   y = x * W^T for M <= 16 (K <= 4096 / any K): the
 //                          weights stream once, decoded through table lookups
 //                          in LDS into v_mfma_f32_16x16x32_bf16 operands; see
@@ -281,11 +284,20 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void k_dequant2(const uint8_t* __res
 
 // any3: the pair indices 12..15 of a 12-byte slot, one per byte, gathered
 // from bits 6-7 of the slot's bytes (pair 12 + t: bits 0-1 from byte t, 2-3
-// from byte 4 + t, 4-5 from byte 8 + t); bits 6-7 of the result are zero.
+// from byte 4 + t, 4-5 from byte 8 + t).  Bits 6-7 of each result byte are
+// left undefined (every reader masks them or ignores them): two bit-field
+// inserts place the three parts at bits 2-7, one shift moves them down.
+// (a & mask) | (b & ~mask) as one v_bfi_b32: written out in C, the compiler
+// folds the two inserts below into three masks and an or3 (two more VALU)
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b)
+{
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(mask), "v"(a), "v"(b));
+    return r;
+}
 __device__ __forceinline__ uint32_t any3_top_pairs(const u32x4_t& p)
 {
-    return ((p[0] >> 6) & 0x03030303u) | ((p[1] >> 4) & 0x0C0C0C0Cu) |
-           ((p[2] >> 2) & 0x30303030u);
+    return bfi(0xC0C0C0C0u, p[2], bfi(0x30303030u, p[1] >> 2, p[0] >> 4)) >> 2;
 }
 
 __device__ __forceinline__ uint32_t pack3_pair(uint32_t codes2)   // two code bytes -> P
