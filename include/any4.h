@@ -124,10 +124,13 @@ size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
  *     y[m][n] = bf16_rne( sum_k x[m][k] * w[n][k] )
  * with w[n][k] exactly the any4_dequant value (every weight is dequantised to
  * that bf16 inside the kernel; the weights are never written to memory).  The
- * products and the sum are fp32 (matrix-core accumulation), so the result is
+ * products are exact and the sum is fp32 (matrix-core accumulation), so y
+ * differs from the fp64 product y_ref with those bf16 weights by the fp32
+ * summation error and y's own rounding to bf16 (at most 2^-8 * |y|); that is
  * within
  *     |y - y_ref| <= 2e-3 * sum_k |x[m][k] * w[n][k]| + 1e-3
- * of the fp64 product with those bf16 weights.  Runs are deterministic (same
+ * whenever |y| <= sum_k |x[m][k] * w[n][k]| / 2 (sums with cancellation, as
+ * for activations and weights of both signs).  Runs are deterministic (same
  * inputs, same bits): the summation order depends only on the shape.
  *   x                         device, [M][K] bf16, read-only.
  *   packed, lut, alpha, beta  device, read-only.
