@@ -16,6 +16,12 @@ Tensors
   y       bf16   [M, N]
   w       bf16   [N, K]
 (bf16 tensors may also be given as int16/uint16 bit patterns.)
+
+Calls: pack, dequant, gemm (any4); gemm_int4 (plain int4, no table);
+any2_pack / any2_dequant / any2_gemm and any3_pack / any3_dequant / any3_gemm
+(2- and 3-bit codes in their own tile layouts); quantize (the weighted
+k-means quantiser at 4, 3 or 2 bits); each also as a ``*_raw`` function on
+device pointers that returns the C status.
 """
 from __future__ import annotations
 
