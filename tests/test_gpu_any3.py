@@ -59,7 +59,8 @@ def test_any3_dequant_bitexact(N, K, g):
                                      (2, 40, 512, 128), (4, 16 * 300 + 5, 1024, 256),
                                      (8, 33, 384, 128), (1, 4096 // 4, 14336, 1024),
                                      (16, 300, 14336, 1024), (3, 17, 8192 + 128, 128),
-                                     (32, 70, 512, 128), (100, 65, 1024, 128)])
+                                     (32, 70, 512, 128), (100, 65, 1024, 128),
+                                     (1, 17, 128, 128), (16, 300, 128, 128)])
 def test_any3_gemm(M, N, K, g):
     L = Layer3(M * 17 + N + K, M, N, K, g)
     y = any4.any3_gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g)
