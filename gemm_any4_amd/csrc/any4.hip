@@ -1462,13 +1462,19 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
 // of lane t % 64: row t % 16, k 32 * ((t % 64) / 16) .. + 31) exactly as
 // any4_dequant does, into W's LDS tile, the threads copy x's BM x 128 tile
 // (rows >= M read as zero), and after a barrier each wave multiplies its
-// (BM/2) x 32 part with 16x16x32 bf16 MFMAs.
+// (BM/2) x 32 part with 16x16x32 bf16 MFMAs.  The global data of a chunk is
+// fetched two chunks ahead (measured: 16% faster at M = 64 than one chunk
+// ahead, 4-5% at M = 256 and 1024; a deeper ring costs occupancy).  A
+// 128 x 128 variant with double-buffered LDS and one barrier per chunk was
+// slower (346 against 305 us at M = 1024): one workgroup per CU leaves one
+// wave per SIMD to hide the LDS latency.
 //
 // LDS: XS [BM][128 + 8] bf16, WS [64][128 + 8] bf16 (rows padded by 16 B so
 // that the 16 rows of an operand read fall in different banks), LT [64][16]
 // fp32 (the table rows of the workgroup's 64 weight rows).
 constexpr int BIG_BN = 64;
 constexpr int BIG_LD = TILE_K + 8;   // padded row length in bf16
+constexpr int BIG_PF = 2;            // chunks of global data in flight per thread
 
 template <int BM, int FMT>
 __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
@@ -1516,110 +1522,130 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
     const int j = lane & 15;
     const int kq = lane >> 4;
 
-    // chunk c's global data, fetched one chunk ahead into registers: this
-    // thread's packed slot, its group's alpha and beta, and its x pieces
+    // chunk c's global data, fetched BIG_PF chunks ahead into a register ring:
+    // this thread's packed slot, its group's alpha and beta, and its x
+    // pieces.  Bounds-checked buffer loads with the offset pushed out of range
+    // (rows past N or M, chunks past K) instead of branches, so that the
+    // compiler's wait counts follow the ring.
+    constexpr int PF = BIG_PF;
     constexpr int XP = BM * 16 / 256;   // 16-byte x pieces per thread
-    u32x4_t pk = {0u, 0u, 0u, 0u};
-    uint32_t ab = 0;
-    u32x4_t xv[XP];
-    auto fetch = [&](int c) {
-        if (wlive) {
-            const int k0 = c * TILE_K + wk;
-            const uint8_t* src = args.packed + (static_cast<size_t>(blk) * Kc + c) * TB + lane * (TB / 64);
-            if constexpr (A2) {
-                typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-                const u32x2_t v = *reinterpret_cast<const u32x2_t*>(src);
-                pk = u32x4_t{v[0], v[1], 0u, 0u};
-            } else if constexpr (A3) {
-                const uint32_t* v = reinterpret_cast<const uint32_t*>(src);
-                pk = u32x4_t{v[0], v[1], v[2], 0u};
-            } else {
-                pk = *reinterpret_cast<const u32x4_t*>(src);
-            }
-            ab = args.alpha[static_cast<size_t>(wn) * G + k0 / g] |
-                 (static_cast<uint32_t>(args.beta[static_cast<size_t>(wn) * G + k0 / g]) << 16);
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc(args.packed, static_cast<uint32_t>((N + TILE_ROWS - 1) / TILE_ROWS) * Kc * TB);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(args.alpha, static_cast<uint32_t>(N) * G * 2);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(args.beta, static_cast<uint32_t>(N) * G * 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(args.x, static_cast<uint32_t>(M) * K * 2);
+    u32x4_t pk[PF];
+    uint32_t ab[PF];
+    u32x4_t xv[PF][XP];
+    auto fetch = [&](int c, int sl) {
+        const uint32_t dead = static_cast<uint32_t>(!wlive || c >= Kc) << 31;
+        const uint32_t po =
+            ((static_cast<uint32_t>(blk) * Kc + c) * TB + lane * (TB / 64)) | dead;
+        if constexpr (A2) {
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rp, po, 0, 0);
+            pk[sl] = u32x4_t{v[0], v[1], 0u, 0u};
+        } else if constexpr (A3) {
+            typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+            const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(rp, po, 0, 0);
+            pk[sl] = u32x4_t{v[0], v[1], v[2], 0u};
+        } else {
+            pk[sl] = load16(rp, po);
         }
+        const uint32_t ao =
+            ((static_cast<uint32_t>(wn) * G + static_cast<uint32_t>(c * TILE_K + wk) / g) * 2) |
+            dead;
+        ab[sl] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(ra, ao, 0, 0)) |
+                 (static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rb, ao, 0, 0)) << 16);
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
             const int piece = tid + i * 256;
             const int m = m0 + (piece >> 4);
-            xv[i] = u32x4_t{0u, 0u, 0u, 0u};
-            if (m < M)
-                xv[i] = *reinterpret_cast<const u32x4_t*>(
-                    args.x + static_cast<size_t>(m) * K + c * TILE_K + (piece & 15) * 8);
+            const uint32_t xo =
+                ((static_cast<uint32_t>(m) * K + c * TILE_K + (piece & 15) * 8) * 2) |
+                (static_cast<uint32_t>(m >= M || c >= Kc) << 31);
+            xv[sl][i] = load16(rx, xo);
         }
     };
-    fetch(0);
-    for (int c = 0; c < Kc; ++c) {
-        __syncthreads();   // the previous chunk's tiles are consumed (and lt is written)
-        // weights: 32 per thread, exactly the any4_dequant values
-        {
-            u32x4_t out[4] = {};
-            if (wlive) {
-                const float a = bf16_to_f32(ab & 0xFFFFu);
-                const float bt = bf16_to_f32(ab >> 16);
-                const float* L = lt + wrow * 16;
-                if constexpr (A2) {   // 8 bytes of four 2-bit codes: dwords 2i, 2i+1
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const uint32_t byte = (pk[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+    for (int sl = 0; sl < PF; ++sl)
+        fetch(sl, sl);
+    for (int c0 = 0; c0 < Kc; c0 += PF) {
 #pragma unroll
-                        for (int t = 0; t < 2; ++t) {
-                            const float lo = fmaf(a, L[(byte >> (4 * t)) & 3u], bt);
-                            const float hi = fmaf(a, L[(byte >> (4 * t + 2)) & 3u], bt);
-                            const int d = 2 * i + t;
-                            out[d >> 2][d & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+        for (int sl = 0; sl < PF; ++sl) {
+            const int c = c0 + sl;   // chunks past K (the last round) add zeros
+            __syncthreads();   // the previous chunk's tiles are consumed (and lt is written)
+            // weights: 32 per thread, exactly the any4_dequant values
+            {
+                u32x4_t out[4] = {};
+                if (wlive && c < Kc) {
+                    const float a = bf16_to_f32(ab[sl] & 0xFFFFu);
+                    const float bt = bf16_to_f32(ab[sl] >> 16);
+                    const float* L = lt + wrow * 16;
+                    const u32x4_t p = pk[sl];
+                    if constexpr (A2) {   // 8 bytes of four 2-bit codes: dwords 2i, 2i+1
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const uint32_t byte = (p[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+#pragma unroll
+                            for (int t = 0; t < 2; ++t) {
+                                const float lo = fmaf(a, L[(byte >> (4 * t)) & 3u], bt);
+                                const float hi = fmaf(a, L[(byte >> (4 * t + 2)) & 3u], bt);
+                                const int d = 2 * i + t;
+                                out[d >> 2][d & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+                            }
+                        }
+                    } else if constexpr (A3) {   // 16 pair indices: dwords 0-2, then the top bits
+                        const uint32_t top = any3_top_pairs(p);
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) {
+                            const uint32_t P =
+                                ((q < 12 ? p[q >> 2] : top) >> (8 * (q & 3))) & 0x3Fu;
+                            const float lo = fmaf(a, L[P & 7u], bt);
+                            const float hi = fmaf(a, L[P >> 3], bt);
+                            out[q >> 2][q & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+                        }
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) {
+                            const uint32_t byte = (p[q >> 2] >> (8 * (q & 3))) & 0xFFu;
+                            const float lo = fmaf(a, L[byte & 15u], bt);
+                            const float hi = fmaf(a, L[byte >> 4], bt);
+                            out[q >> 2][q & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
                         }
                     }
-                } else if constexpr (A3) {   // 16 pair indices: dwords 0-2, then the top bits
-                    const uint32_t top = any3_top_pairs(pk);
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        const uint32_t P = ((q < 12 ? pk[q >> 2] : top) >> (8 * (q & 3))) & 0x3Fu;
-                        const float lo = fmaf(a, L[P & 7u], bt);
-                        const float hi = fmaf(a, L[P >> 3], bt);
-                        out[q >> 2][q & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
-                    }
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        const uint32_t byte = (pk[q >> 2] >> (8 * (q & 3))) & 0xFFu;
-                        const float lo = fmaf(a, L[byte & 15u], bt);
-                        const float hi = fmaf(a, L[byte >> 4], bt);
-                        out[q >> 2][q & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
-                    }
                 }
+                u32x4_t* dst = reinterpret_cast<u32x4_t*>(ws + wrow * BIG_LD + wk);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    dst[q] = out[q];
             }
-            u32x4_t* dst = reinterpret_cast<u32x4_t*>(ws + wrow * BIG_LD + wk);
+            // x: BM rows x 128 k
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                dst[q] = out[q];
-        }
-        // x: BM rows x 128 k
+            for (int i = 0; i < XP; ++i) {
+                const int piece = tid + i * 256;
+                *reinterpret_cast<u32x4_t*>(xs + (piece >> 4) * BIG_LD + (piece & 15) * 8) =
+                    xv[sl][i];
+            }
+            fetch(c + PF, sl);
+            __syncthreads();
 #pragma unroll
-        for (int i = 0; i < XP; ++i) {
-            const int piece = tid + i * 256;
-            *reinterpret_cast<u32x4_t*>(xs + (piece >> 4) * BIG_LD + (piece & 15) * 8) = xv[i];
-        }
-        if (c + 1 < Kc)
-            fetch(c + 1);
-        __syncthreads();
-#pragma unroll
-        for (int ks = 0; ks < TILE_K / 32; ++ks) {
-            const int k = ks * 32 + kq * 8;
-            u32x4_t bf[2];
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-                bf[nt] = *reinterpret_cast<const u32x4_t*>(ws + (wc + nt * 16 + j) * BIG_LD + k);
-#pragma unroll
-            for (int mt = 0; mt < MTW; ++mt) {
-                const u32x4_t af =
-                    *reinterpret_cast<const u32x4_t*>(xs + (wm + mt * 16 + j) * BIG_LD + k);
+            for (int ks = 0; ks < TILE_K / 32; ++ks) {
+                const int k = ks * 32 + kq * 8;
+                u32x4_t bf[2];
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, af), __builtin_bit_cast(bf16x8_t, bf[nt]),
-                        acc[mt][nt], 0, 0, 0);
+                    bf[nt] = *reinterpret_cast<const u32x4_t*>(ws + (wc + nt * 16 + j) * BIG_LD + k);
+#pragma unroll
+                for (int mt = 0; mt < MTW; ++mt) {
+                    const u32x4_t af =
+                        *reinterpret_cast<const u32x4_t*>(xs + (wm + mt * 16 + j) * BIG_LD + k);
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt)
+                        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, af), __builtin_bit_cast(bf16x8_t, bf[nt]),
+                            acc[mt][nt], 0, 0, 0);
+                }
             }
         }
     }
