@@ -1820,6 +1820,468 @@ __global__ __launch_bounds__(64 * PROBE_WAVES) void k_read_probe(const uint8_t* 
         out[0] = 1u;
 }
 
+// ---- k_gemm_st: the whole ring in flight from the first instruction --------
+//
+// The decode kernel for M <= 16.  A workgroup of NW waves (NW = blockDim/64,
+// at most 16, chosen by the host) owns row blocks r, r+Gs, r+2Gs, ... and
+// decodes them NBG at a time (a group); wave w owns chunks [w*cw, (w+1)*cw)
+// of K (cw a multiple of R, chosen by the host) and walks them R at a time
+// (a body), each step decoding that chunk's tile of every block of the
+// group against the same x operands.
+//
+// A streaming read of this size only reaches HBM's bandwidth when every wave
+// has its loads in flight from the start (MI355X, 29.4 MB in one launch:
+// 5.45-5.5 us with all loads issued at once, 6.0-6.2 us with an 8-deep ring
+// refilled as tiles are consumed).  So the ring holds a whole body (R*NBG
+// tiles); for the decode shapes that is every tile the wave reads, and it
+// is issued in the prologue right behind the small staging loads (table
+// rows, alpha/beta, x for XL).  The staging data lands in LDS as soon as it
+// arrives and the NBG pair tables are built with 16-byte writes while the
+// tiles are still on their way.
+//
+// Decode, dequantisation and x operands as in k_gemm_km (pair tables of 32
+// slots, each weight formed as bf16(fp32(alpha*L + beta)) from the row's
+// 2^-s scaled f16 table values).  A dead tile (a block past the workgroup's
+// last, a chunk past K) reads the 256 zero bytes at ZERO instead of its
+// table, with alpha = beta = 0.
+//
+// LDS (byte offsets from st_layout):
+//   [0, ZERO)  pair tables: table b in 64 KB region b/2, half b%2, entry e at
+//              e*256 + (b%2)*128 + slot*4; the partial sums reuse it
+//   ZERO       256 zero bytes (64 KB aligned: the table reads of dead tiles)
+//   AB         [NBG][G][16 rows] (alpha | beta << 16) dwords
+//   LUTS       [NBG][4 row quads][16 entries][4 rows] f16, each row scaled by 2^-s
+//   SCL        [NBG][16 rows] int: the row scale exponents s
+//   XS, XZ     (XL) x as [M][K] bf16, then 256 zero bytes (x of dead chunks)
+struct StLayout {
+    uint32_t zero, ab, luts, scl, xs, xz, total;
+};
+
+__host__ __device__ inline StLayout st_layout(int nbg, int G, int M, int K, bool xl)
+{
+    StLayout L;
+    L.zero = static_cast<uint32_t>((nbg + 1) / 2) * 65536u;
+    L.ab = L.zero + 256;
+    L.luts = L.ab + static_cast<uint32_t>(nbg) * G * 64;
+    L.scl = L.luts + nbg * 512;
+    L.xs = L.scl + nbg * 64;
+    L.xz = L.xs + (xl ? ((static_cast<uint32_t>(M) * K * 2 + 15u) & ~15u) : 0u);
+    L.total = L.xz + (xl ? 256u : 0u);
+    return L;
+}
+
+constexpr int ST_MAX_WAVES = 16;
+constexpr int ST_LDS = 160 * 1024;   // one workgroup per CU: all of its LDS
+constexpr int ST_XP = 4;   // 16-byte pieces of x per thread (XL)
+
+struct StArgs {
+    GemmArgs a;
+    int cw;        // chunks per wave (a multiple of R)
+    StLayout L;
+    unsigned long long* ts;   // per-wave timestamps (probe builds only), or null
+};
+
+template <int MT, int NBG, int R, bool XL, bool MG, int LB, int PRE, int D, int FMT>
+__global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
+{
+    constexpr bool I4 = FMT == FMT_INT4;
+    constexpr bool A2 = FMT == FMT_ANY2;
+    constexpr bool A3 = FMT == FMT_ANY3;
+    constexpr uint32_t TB = tile_bytes(FMT);
+    constexpr int TPW = R * NBG;   // tiles in a body
+    static_assert(TPW % D == 0, "the ring depth divides a body");
+    static_assert(XL || TPW - D >= NBG - 1, "x of a step is not overwritten before its step");
+    constexpr bool XSTREAM = !XL;
+    // static (not dynamic) LDS: its base is the constant 0, so table addresses
+    // need no add
+    __shared__ __attribute__((aligned(16))) uint8_t smem[ST_LDS];
+    const GemmArgs& args = sa.a;
+    const StLayout L = sa.L;
+
+    const int M = args.M, N = args.N, K = args.K, g = args.g;
+    const int NT = blockDim.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int NW = NT >> 6;
+    const int j = lane & 15;
+    const int kq = lane >> 4;
+    const int Kc = K / TILE_K;
+    const int NB = (N + TILE_ROWS - 1) / TILE_ROWS;
+    const int G = K / g;
+    const int gc = g / TILE_K;   // chunks per group
+    const int Gs = gridDim.x;
+    const int r = blockIdx.x;
+    const int nblk = r < NB ? (NB - 1 - r) / Gs + 1 : 0;
+    const int ngroups = MG ? (nblk + NBG - 1) / NBG : 1;
+    const int cw = sa.cw;
+    const int bpg = cw / R;        // bodies per group
+    const int c0 = wave * cw;
+#ifdef ANY4_PROBE_TS
+    unsigned long long* ts = sa.ts ? sa.ts + (static_cast<size_t>(r) * NW + wave) * 8 : nullptr;
+    auto stamp = [&](int i) {
+        if (ts && lane == 0)
+            ts[i] = __builtin_amdgcn_s_memtime();
+    };
+#else
+    auto stamp = [](int) {};
+#endif
+    stamp(0);
+
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(args.packed, static_cast<uint32_t>(NB) * Kc * TB);
+    // plain int4 has no table (its pointer may be null): nothing is read through rl
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(args.lut, I4 ? 0u : static_cast<uint32_t>(N) * 32);
+    const uint32_t ab_range = (static_cast<uint32_t>(N) * G * 2 + 15u) & ~15u;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(args.alpha, ab_range);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(args.beta, ab_range);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(args.x, static_cast<uint32_t>(M) * K * 2);
+
+    // ---- staging of group gi.  Table rows: thread t < 32*NBG fetches 16 B
+    // (8 entries of row (t%32)/2) of block t/32.  alpha/beta: item q = t + h*NT
+    // (h < 2) is piece q % 2G of block q / 2G, 16 B of each tensor.
+    const int ab_per = 2 * G;
+    int ab_blk[2], ab_pc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int q = tid + h * NT;
+        ab_blk[h] = q / ab_per;
+        ab_pc[h] = q - ab_blk[h] * ab_per;
+    }
+    auto stage_load = [&](int gi, u32x4_t& lq, u32x4_t (&aq)[2], u32x4_t (&bq)[2]) {
+        {
+            const int blk = gi * NBG + (tid >> 5);
+            const bool live = tid < 32 * NBG && blk < nblk;
+            const uint32_t o = (static_cast<uint32_t>(r + blk * Gs) * 512 + (tid & 31) * 16) |
+                               (static_cast<uint32_t>(!live) << 31);
+            if constexpr (I4)
+                lq = u32x4_t{0u, 0u, 0u, 0u};
+            else
+                lq = load16(rl, o);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int blk = gi * NBG + ab_blk[h];
+            const bool live = ab_blk[h] < NBG && blk < nblk;
+            const uint32_t o = (static_cast<uint32_t>(r + blk * Gs) * (G * 32) + ab_pc[h] * 16) |
+                               (static_cast<uint32_t>(!live) << 31);
+            aq[h] = load16(ra, o);
+            bq[h] = load16(rb, o);
+        }
+    };
+    auto stage_store = [&](const u32x4_t& lq, const u32x4_t (&aq)[2], const u32x4_t (&bq)[2]) {
+        const int sc = I4 ? 0 : lut_scale(lq);   // all lanes: lanes 2i, 2i+1 hold one row
+        const u32x4_t lh = I4 ? lq : lut_to_f16(lq, sc);
+        if (tid < 32 * NBG) {
+            // by row quad, entry, row: a build thread reads one entry of four
+            // rows with one 8-byte read, eight entries with two 16-byte reads
+            const int row = (tid & 31) >> 1;
+            const uint32_t base = L.luts + (tid >> 5) * 512 + (row >> 2) * 128 + (row & 3) * 2;
+            const int e0 = (tid & 1) * 8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                lds_at<uint16_t>(smem, base + (e0 + i) * 8) =
+                    static_cast<uint16_t>(lh[i >> 1] >> (16 * (i & 1)));
+            if ((tid & 1) == 0)
+                lds_at<int>(smem, L.scl + (tid >> 1) * 4) = sc;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            if (ab_blk[h] < NBG)
+                store_pairs(smem, L.ab + ab_blk[h] * G * 64, ab_pc[h], G, aq[h], bq[h]);
+    };
+    // Pair tables of the group with 16-byte writes.  Item it = (block b, half
+    // h, hi, slot quad q) writes slots 4q..4q+3 (rows 4(q%4)..+3) of the
+    // entries hi<<4 | lo, lo = 8h..8h+7; the 8 lanes of one entry write its
+    // 128 contiguous bytes, and the table values come from three LDS reads.
+    auto build_item = [&](int it, auto&& hook) {
+        const int q = it & 7;
+        const int hi = (it >> 3) & 15;
+        const int h = (it >> 7) & 1;
+        const int b = it >> 8;
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const uint32_t src = L.luts + b * 512 + (q & 3) * 128;
+        // any4: entry hi<<4 | lo is (L[lo], L[hi]).  any3: the byte's low 6
+        // bits are two 3-bit codes and bits 6-7 pick one of four identical
+        // copies, so entry e is (L[e & 7], L[(e >> 3) & 7]): for lo = 8h + i
+        // that is (L[i], L[(2hi + h) & 7]).
+        const uint32_t bsrc = A3 ? ((2 * hi + h) & 7) * 8 : hi * 8;
+        const uint32_t asrc = A3 ? 0u : h * 64;
+        const u32x2_t B = lds_at<u32x2_t>(smem, src + bsrc);         // second value, 4 rows
+        const u32x4_t Q0 = lds_at<u32x4_t>(smem, src + asrc);        // first values of lo, lo+1
+        const u32x4_t Q1 = lds_at<u32x4_t>(smem, src + asrc + 16);   // lo+2, lo+3
+        const u32x4_t Q2 = lds_at<u32x4_t>(smem, src + asrc + 32);
+        const u32x4_t Q3 = lds_at<u32x4_t>(smem, src + asrc + 48);
+        const uint32_t Aw[16] = {Q0[0], Q0[1], Q0[2], Q0[3], Q1[0], Q1[1], Q1[2], Q1[3],
+                                 Q2[0], Q2[1], Q2[2], Q2[3], Q3[0], Q3[1], Q3[2], Q3[3]};
+        const uint32_t dst = (b >> 1) * 65536 + (b & 1) * 128 + (hi * 16 + h * 8) * 256 + q * 16;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t a0 = Aw[2 * i], a1 = Aw[2 * i + 1];
+            const u32x4_t v = {__builtin_amdgcn_perm(B[0], a0, 0x05040100u),
+                               __builtin_amdgcn_perm(B[0], a0, 0x07060302u),
+                               __builtin_amdgcn_perm(B[1], a1, 0x05040100u),
+                               __builtin_amdgcn_perm(B[1], a1, 0x07060302u)};
+            lds_at<u32x4_t>(smem, dst + i * 256) = v;
+            hook(i);
+        }
+    };
+    // any2: quad tables.  Entry e (a byte of four 2-bit codes c_s = (e >> 2s) & 3)
+    // holds, per row, (L[c0] | L[c1] << 16, L[c2] | L[c3] << 16); 16 slots of
+    // 8 bytes (slot = row), entry e at e*256 (+128 for the second table of a
+    // 64 KB region).  Item it = (block, entry, slot pair q) writes rows 2q, 2q+1.
+    auto build_item2 = [&](int it) {
+        const int q = it & 7;
+        const int e = (it >> 3) & 255;
+        const int b = it >> 11;
+        const uint32_t src = L.luts + b * 512 + (q >> 1) * 128 + (q & 1) * 4;
+        uint32_t c[4];   // (L[c_s] of row 2q, of row 2q+1)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            c[t] = lds_at<uint32_t>(smem, src + ((e >> (2 * t)) & 3) * 8);
+        const u32x4_t v = {__builtin_amdgcn_perm(c[1], c[0], 0x05040100u),
+                           __builtin_amdgcn_perm(c[3], c[2], 0x05040100u),
+                           __builtin_amdgcn_perm(c[1], c[0], 0x07060302u),
+                           __builtin_amdgcn_perm(c[3], c[2], 0x07060302u)};
+        lds_at<u32x4_t>(smem, (b >> 1) * 65536 + (b & 1) * 128 + e * 256 + q * 16) = v;
+    };
+    auto build = [&]() {
+        if constexpr (A2) {
+            for (int it = tid; it < NBG * 2048; it += NT)
+                build_item2(it);
+        } else if constexpr (!I4) {
+            for (int it = tid; it < NBG * 256; it += NT)
+                build_item(it, [](int) {});
+        }
+    };
+
+    // ---- ring.  Tile u of body k: step s = u / NBG (chunk c0 + (k % bpg)*R + s)
+    // of block (k / bpg)*NBG + u % NBG; it sits in ring slot u % D (D divides
+    // a body).  x (XSTREAM): a step's operands are loaded with its first tile.
+    u32x4_t pb[D];
+    u32x4_t xq[XSTREAM ? R : 1][4];
+    const uint32_t tile_lane = static_cast<uint32_t>(lane) * (TB / 64);
+    const uint32_t x_lane = j < M ? static_cast<uint32_t>(j * K + kq * 32) * 2 : OOR;
+    auto issue = [&](int k, int u) {
+        const int gi = k / bpg;
+        const int s = (k - gi * bpg) * R + u / NBG;
+        const int blk = gi * NBG + u % NBG;
+        const int c = c0 + s;
+        const bool live = gi < ngroups && blk < nblk && c < Kc;
+        const uint32_t uo = (static_cast<uint32_t>(r + blk * Gs) * static_cast<uint32_t>(Kc) + c) * TB |
+                            (static_cast<uint32_t>(!live) << 31);
+        pb[u % D] = A2   ? load8_nt(rp, off2(tile_lane, uo))
+                    : A3 ? load12_nt(rp, off2(tile_lane, uo))
+                         : load16_nt(rp, off2(tile_lane, uo));
+        if constexpr (XSTREAM) {
+            if (u % NBG == 0) {
+                const bool xl = gi < ngroups && c < Kc;
+                const uint32_t xc = static_cast<uint32_t>(c) * TILE_K * 2 | (static_cast<uint32_t>(!xl) << 31);
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+                    xq[u / NBG][s4] = load16(rx, off2(x_lane, xc) + s4 * 16);
+            }
+        }
+    };
+    // the tile D places after tile u of body k
+    auto issue_next = [&](int k, int u) {
+        if (u + D < TPW)
+            issue(k, u + D);
+        else
+            issue(k + 1, u + D - TPW);
+    };
+
+    // ---- prologue: staging loads, x (XL), the first PRE ring tiles; the rest
+    // of the ring once the staging data is in (requested behind the whole
+    // ring, it would queue behind every tile of the chip)
+    u32x4_t lq, aq[2], bq[2];
+    stage_load(0, lq, aq, bq);
+    u32x4_t xc16[XL ? ST_XP : 1];
+    const uint32_t xbytes = static_cast<uint32_t>(M) * K * 2;
+    if constexpr (XL) {
+#pragma unroll
+        for (int i = 0; i < ST_XP; ++i) {
+            const uint32_t o = static_cast<uint32_t>(tid + i * NT) * 16;
+            xc16[i] = load16(rx, o < xbytes ? o : OOR);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < (PRE < D ? PRE : D); ++u)
+        issue(0, u);
+    stamp(1);
+    if (tid < 16)
+        lds_at<u32x4_t>(smem, L.zero + tid * 16) = u32x4_t{0u, 0u, 0u, 0u};
+    if constexpr (XL) {
+        if (tid < 16)
+            lds_at<u32x4_t>(smem, L.xz + tid * 16) = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < ST_XP; ++i) {
+            const uint32_t o = static_cast<uint32_t>(tid + i * NT) * 16;
+            if (o < xbytes)
+                lds_at<u32x4_t>(smem, L.xs + o) = xc16[i];
+        }
+    }
+    stage_store(lq, aq, bq);
+    stamp(2);
+    __syncthreads();
+    stamp(3);
+    // the tables' 16-byte writes and the rest of the ring's loads, interleaved,
+    // so that neither the LDS nor the texture unit waits for the other
+    if (!I4 && !A2 && NT >= NBG * 256) {
+        if (tid < NBG * 256) {   // uniform: NBG * 256 is a multiple of 64
+            build_item(tid, [&](int i) {
+                if (PRE + i < D)
+                    issue(0, PRE + i);
+            });
+#pragma unroll
+            for (int u = PRE + 8; u < D; ++u)
+                issue(0, u);
+        } else {
+#pragma unroll
+            for (int u = PRE; u < D; ++u)
+                issue(0, u);
+        }
+    } else {
+#pragma unroll
+        for (int u = PRE; u < D; ++u)
+            issue(0, u);
+        build();
+    }
+    __syncthreads();
+    stamp(4);
+
+    // the lane's slot in a table entry (any2: 16 slots of 8 bytes)
+    const uint32_t slot4 = A2 ? static_cast<uint32_t>(lane & 15) * 8 : static_cast<uint32_t>(lane & 31) * 4;
+    f32x4_t acc[NBG];
+#pragma unroll
+    for (int b = 0; b < NBG; ++b)
+        acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    int rsc[NBG];
+    auto load_scales = [&]() {
+#pragma unroll
+        for (int b = 0; b < NBG; ++b)
+            rsc[b] = I4 ? 0 : lds_at<int>(smem, L.scl + (b * 16 + j) * 4);
+    };
+    load_scales();
+    const int jr = j < M ? j : M - 1;
+
+    u32x4_t lqn, aqn[2], bqn[2];
+    const int total = ngroups * bpg;
+    for (int k = 0; k < total; ++k) {
+        const int gi = k / bpg;
+        const int kb = k - gi * bpg;
+        if constexpr (MG) {
+            if (kb == 0)
+                stage_load(gi + 1, lqn, aqn, bqn);
+        }
+#pragma unroll
+        for (int s = 0; s < R; ++s) {
+            const int c = c0 + kb * R + s;
+            const int grp = min(c / gc, G - 1);
+            u32x4_t xv[4];
+            if constexpr (XL) {
+                const uint32_t xo = c < Kc ? L.xs + (static_cast<uint32_t>(jr) * K + c * TILE_K + kq * 32) * 2
+                                           : L.xz + kq * 64;
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+                    xv[s4] = lds_at<u32x4_t>(smem, xo + s4 * 16);
+            }
+#pragma unroll
+            for (int b = 0; b < NBG; ++b) {
+                const int u = s * NBG + b;
+                const bool live = gi * NBG + b < nblk && c < Kc;
+                const u32x4_t p = pb[u % D];
+                const uint32_t sv = slot4 | (live ? static_cast<uint32_t>(b >> 1) << 16 : L.zero);
+                u32x4_t bw[4];
+                if constexpr (A2) {
+                    // bytes 2*s4 and 2*s4+1: four weights each, one 64-bit read
+                    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+                    for (int bi = 0; bi < 8; ++bi) {
+                        const u32x2_t qv = lds_at<u32x2_t>(
+                            smem, __builtin_amdgcn_perm(p[bi >> 2], sv, 0x0C020000u | ((4u + (bi & 3)) << 8)) +
+                                      (b & 1) * 128);
+                        bw[bi >> 1][2 * (bi & 1)] = qv[0];
+                        bw[bi >> 1][2 * (bi & 1) + 1] = qv[1];
+                    }
+                } else if constexpr (!I4) {
+                    // the pair bytes of the four B operands (any3: the fourth from the top bits)
+                    const u32x4_t pd = A3 ? u32x4_t{p[0], p[1], p[2], any3_top_pairs(p)} : p;
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                        for (int jb = 0; jb < 4; ++jb)
+                            bw[s4][jb] = lds_at<uint32_t>(
+                                smem, __builtin_amdgcn_perm(pd[s4], sv, 0x0C020000u | ((4u + jb) << 8)) +
+                                          (b & 1) * 128);
+                }
+                const uint32_t pr = lds_at<uint32_t>(smem, L.ab + b * G * 64 + (grp * 16 + j) * 4) &
+                                    (live ? 0xFFFFFFFFu : 0u);
+                const float a = __builtin_ldexpf(bf16_to_f32(pr & 0xFFFFu), rsc[b]);
+                const float bt = bf16_to_f32(pr >> 16);
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const u32x4_t w = I4 ? deq_int4(p[s4], a, bt) : deq_quad(bw[s4], a, bt);
+                    const u32x4_t& xa = XL ? xv[s4] : xq[XL ? 0 : s][s4];
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, xa), __builtin_bit_cast(bf16x8_t, w), acc[b], 0,
+                        0, 0);
+                }
+                issue_next(k, u);
+            }
+        }
+        if (k == 0)
+            stamp(5);
+        if (kb == bpg - 1) {
+            // end of a group: partial sums through LDS, y, then the next group's
+            // tables.  Only the outputs of rows m < M are passed on: lane l holds
+            // y[4*(l/16) + v][l % 16], so the first 16*LQ lanes and VC values.
+            stamp(6);
+            constexpr int VC = MT < 4 ? MT : 4;
+            constexpr int LQ = (MT + 3) / 4;
+            constexpr int OUT = 16 * LQ * VC;   // outputs of a block
+            float* redf = reinterpret_cast<float*>(smem);
+            __syncthreads();
+            if (lane < 16 * LQ) {
+#pragma unroll
+                for (int b = 0; b < NBG; ++b)
+#pragma unroll
+                    for (int v = 0; v < VC; ++v)
+                        redf[(b * NW + wave) * OUT + lane * VC + v] = acc[b][v];
+            }
+            if constexpr (MG) {
+                if (gi + 1 < ngroups)
+                    stage_store(lqn, aqn, bqn);
+            }
+            __syncthreads();
+            for (int t = tid; t < NBG * OUT; t += NT) {   // every thread sums outputs
+                const int b = t / OUT;
+                const int o = t - b * OUT;
+                const int blk = gi * NBG + b;
+                float tot = redf[b * NW * OUT + o];
+                for (int w = 1; w < NW; ++w)
+                    tot += redf[(b * NW + w) * OUT + o];
+                const int l = o / VC;
+                const int m = (l >> 4) * 4 + (o - l * VC);
+                const int n = (r + blk * Gs) * TILE_ROWS + (l & 15);
+                if (blk < nblk && m < M && n < N)
+                    args.y[static_cast<size_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16(tot));
+            }
+            stamp(7);
+            if constexpr (MG) {
+                if (gi + 1 < ngroups) {
+                    __syncthreads();
+                    build();
+                    __syncthreads();
+                    load_scales();
+#pragma unroll
+                    for (int b = 0; b < NBG; ++b)
+                        acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // host helpers
 // ---------------------------------------------------------------------------
@@ -1846,8 +2308,30 @@ any4_status launched()
 constexpr int KM_GRID = 256;   // one workgroup per CU of an MI355X
 
 template <int MT, int FMT>
+bool launch_st(const GemmArgs& a, hipStream_t stream, unsigned long long* ts);
+#ifdef ANY4_PROBE_TS
+bool st_disable = false;   // probe builds: time the older kernels
+#endif
+
+// k_gemm_st where it measured faster than k_gemm_km / k_gemm_kb:
+// up to four row blocks per workgroup (one group), with more than one block
+// or K past 4096.
+bool use_st(const GemmArgs& a)
+{
+    const int64_t NB = row_blocks(a.N);
+    const int64_t grid = NB < KM_GRID ? NB : KM_GRID;
+    const int64_t nb = grid > 0 ? (NB + grid - 1) / grid : 0;
+    return nb >= 1 && nb <= 4 && (nb >= 2 || a.K > KM_MAX_K);
+}
+
+template <int MT, int FMT>
 void launch_gemm(const GemmArgs& a, hipStream_t stream)
 {
+#ifdef ANY4_PROBE_TS
+    if (!st_disable)
+#endif
+    if (use_st(a) && launch_st<MT, FMT>(a, stream, nullptr))
+        return;
     const int64_t NB = row_blocks(a.N);
     int64_t grid = NB < KM_GRID ? NB : KM_GRID;
     if (grid * KM_MAX_BLK < NB)
@@ -1890,6 +2374,145 @@ void launch_gemm(const GemmArgs& a, hipStream_t stream)
         hipLaunchKernelGGL((k_gemm_kb<MT, 3, false, FMT>), gd, dim3(GT), 0, stream, a);
     else
         hipLaunchKernelGGL((k_gemm_kb<MT, 4, false, FMT>), gd, dim3(GT), 0, stream, a);
+}
+
+// ---- k_gemm_st launch: the shape decides waves, blocks per group and ring --
+struct StPlan {
+    int grid, nw, nbg, r, cw;
+    bool mg, xl;
+    StLayout L;
+};
+
+// Ring depths that fit 128 VGPRs (16 waves per CU) without spilling: x in
+// the ring costs 16 registers per chunk, the next group's staging 20.
+constexpr bool st_ring_ok(int nbg, int r, bool xl, bool mg)
+{
+    const int tpw = nbg * r;
+    if (xl)
+        return tpw <= (mg ? 4 : 8);
+    if (mg)
+        return r == 1 && tpw <= 2;
+    return nbg == 1 ? r <= 4 : tpw <= 8 && r <= 2;
+}
+
+// Blocks per group, waves, body length and chunks per wave: the fewest dead
+// chunks, then the most waves, then the fewest bodies; x in LDS for M <= 2
+// where it fits.
+#ifdef ANY4_PROBE_TS
+int st_force_nw = 0, st_force_r = 0;
+#endif
+inline bool st_plan(int M, int N, int K, int g, StPlan& P)
+{
+    const int NB = static_cast<int>(row_blocks(N));
+    const int Kc = K / TILE_K;
+    const int G = K / g;
+    P.grid = NB < KM_GRID ? NB : KM_GRID;
+    const int nb = (NB + P.grid - 1) / P.grid;
+    for (int nbg = nb <= 1 ? 1 : nb <= 2 ? 2 : 4; nbg >= 1; nbg /= 2) {
+        const bool mg = nb > nbg;
+        for (int xi = M <= 2 ? 0 : 1; xi < 2; ++xi) {
+            const bool xl = xi == 0;
+            const StLayout L = st_layout(nbg, G, M, K, xl);
+            if (L.total > ST_LDS)
+                continue;
+            int best = -1;
+            for (int r = 1; r * nbg <= 8; r *= 2) {
+                if (!st_ring_ok(nbg, r, xl, mg))
+                    continue;
+                for (int nw = ST_MAX_WAVES; nw >= 1; --nw) {
+#ifdef ANY4_PROBE_TS
+                    if ((st_force_nw && nw != st_force_nw) || (st_force_r && r != st_force_r))
+                        continue;
+#endif
+                    const int nt = 64 * nw;
+                    if (nbg * 2 * G > 2 * nt)
+                        continue;
+                    if (xl && static_cast<int64_t>(M) * K * 2 > static_cast<int64_t>(ST_XP) * nt * 16)
+                        continue;
+                    const int cw = r * ((Kc + nw * r - 1) / (nw * r));
+                    const int waste = nw * cw - Kc;
+                    const int score = waste * 4096 + (ST_MAX_WAVES - nw) * 64 + cw / r;
+                    if (best < 0 || score < best) {
+                        best = score;
+                        P.nw = nw;
+                        P.r = r;
+                        P.cw = cw;
+                    }
+                }
+            }
+            if (best >= 0) {
+                P.nbg = nbg;
+                P.mg = mg;
+                P.xl = xl;
+                P.L = L;
+                return true;
+            }
+        }
+    }
+    return false;
+}
+
+// Ring tiles issued before the staging data is waited for, and ring depth
+// (tiles in flight per wave).  Measured on the 14336x4096 and 4096x14336
+// layers: a wave that issues more loads than the CU accepts stalls at issue
+// (8 at once: ~6K cycles), while 2 per wave of 16 (32 KB per CU) never
+// stall and already keep HBM near its streaming rate; tiles requested ahead
+// of the staging loads delay the table build more than they save.
+#ifndef ANY4_ST_PRE
+#define ANY4_ST_PRE 0
+#endif
+#ifndef ANY4_ST_D
+#define ANY4_ST_D 2
+#endif
+template <int MT, int NBG, int R, bool XL, bool MG, int FMT>
+void st_go(const StArgs& sa, const StPlan& P, hipStream_t stream)
+{
+    constexpr int LB = 1024;
+    constexpr int TB = NBG * R;
+    constexpr int DD = ANY4_ST_D < TB ? ANY4_ST_D : TB;
+    constexpr int D = (XL || TB - DD >= NBG - 1) ? DD : 1;
+    hipLaunchKernelGGL((k_gemm_st<MT, NBG, R, XL, MG, LB, ANY4_ST_PRE, D, FMT>), dim3(P.grid), dim3(64 * P.nw),
+                       0, stream, sa);
+}
+
+template <int MT, int NBG, int R, int FMT>
+void st_go_r(const StArgs& sa, const StPlan& P, hipStream_t stream)
+{
+    if constexpr (MT <= 2) {
+        if (P.xl) {
+            if (P.mg)
+                st_go<MT, NBG, R, true, true, FMT>(sa, P, stream);
+            else
+                st_go<MT, NBG, R, true, false, FMT>(sa, P, stream);
+            return;
+        }
+    }
+    if (P.mg)
+        st_go<MT, NBG, R, false, true, FMT>(sa, P, stream);
+    else
+        st_go<MT, NBG, R, false, false, FMT>(sa, P, stream);
+}
+
+template <int MT, int FMT>
+bool launch_st(const GemmArgs& a, hipStream_t stream, unsigned long long* ts)
+{
+    StPlan P;
+    if (!st_plan(a.M, a.N, a.K, a.g, P))
+        return false;
+    StArgs sa{a, P.cw, P.L, ts};
+    switch (P.nbg * 16 + P.r) {
+    case 16 + 1: st_go_r<MT, 1, 1, FMT>(sa, P, stream); break;
+    case 16 + 2: st_go_r<MT, 1, 2, FMT>(sa, P, stream); break;
+    case 16 + 4: st_go_r<MT, 1, 4, FMT>(sa, P, stream); break;
+    case 16 + 8: st_go_r<MT, 1, 8, FMT>(sa, P, stream); break;
+    case 32 + 1: st_go_r<MT, 2, 1, FMT>(sa, P, stream); break;
+    case 32 + 2: st_go_r<MT, 2, 2, FMT>(sa, P, stream); break;
+    case 32 + 4: st_go_r<MT, 2, 4, FMT>(sa, P, stream); break;
+    case 64 + 1: st_go_r<MT, 4, 1, FMT>(sa, P, stream); break;
+    case 64 + 2: st_go_r<MT, 4, 2, FMT>(sa, P, stream); break;
+    default: return false;
+    }
+    return true;
 }
 
 }  // namespace
