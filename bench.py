@@ -71,6 +71,12 @@ def weight_bytes(N: int, K: int, g: int) -> int:
     return N * K // 2 + 4 * N * (K // g) + 32 * N
 
 
+def rotating_sets(wbytes: int) -> int:
+    """Weight sets to rotate over: R - 1 consecutive launches read more than
+    twice the 256 MB last-level cache, so each launch's weights come from HBM."""
+    return max(2, math.ceil(2 * CACHE_BYTES / wbytes) + 2)
+
+
 def kernel_source_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -90,35 +96,51 @@ def _traffic(M: int):
     return None if v is None else float(v["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(seconds: float) -> dict:
-    """The CPU oracle (dequant + fp64 GEMM) on the same workload, repeated for
-    about `seconds` of wall time on this host's cores."""
+def cpu_baseline() -> dict:
+    """The CPU oracle on the two MLP layers the targets are stated for (the
+    14336x4096 g128 and 4096x14336 g1024 layers), at M = 1 and M = 16, each
+    timed single-threaded and split over rows on every host core: one oracle
+    dequant of the layer (single-threaded, as the oracle has it) plus one fp64
+    GEMM.  µs and effective GB/s use the GPU's algorithmic bytes.  `value`
+    is the all-core rate of the benchmark's step (config 2, M = 1 then 16)."""
     import oracle
     import workloads
 
-    inp = workloads.generate(2)
     threads = oracle.default_threads()
-    packed = oracle.pack(inp.idx)
-    steps = 0
+    cases = []
     t0 = time.perf_counter()
-    while True:
-        w = oracle.dequant(packed, inp.lut, inp.alpha, inp.beta, G_)
+    for cfg in (2, 3):
+        inp = workloads.generate(cfg)
+        packed = oracle.pack(inp.idx)
+        c = workloads.CONFIGS[cfg]
+        td = time.perf_counter()
+        w = oracle.dequant(packed, inp.lut, inp.alpha, inp.beta, c.g)
+        t_dq = time.perf_counter() - td
         for M in MS:
-            oracle.gemm(inp.x[:M], w, nthreads=threads)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+            for nt in (1, threads):
+                tg = time.perf_counter()
+                oracle.gemm(inp.x[:M], w, nthreads=nt)
+                t_g = time.perf_counter() - tg
+                t = t_dq + t_g
+                bts = algorithmic_bytes(M, c.N, c.K, c.g)
+                cases.append({"config": cfg, "N": c.N, "K": c.K, "g": c.g, "M": M,
+                              "threads": nt, "us": t * 1e6, "dequant_us": t_dq * 1e6,
+                              "gemm_us": t_g * 1e6, "gbps": bts / t / 1e9})
+        del w, packed, inp
+    el = time.perf_counter() - t0
+    step = [x for x in cases if x["config"] == 2 and x["threads"] == threads]
+    step_us = sum(x["us"] for x in step)
     step_bytes = sum(algorithmic_bytes(M, N_, K_, G_) for M in MS)
     return {
-        "value": step_bytes * steps / el / 1e12,
+        "value": step_bytes / (step_us * 1e-6) / 1e12,
         "unit": "TB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"{steps} full steps of the same workload (oracle dequant of the "
-                   f"{N_}x{K_} layer, then fp64 GEMM at M=1 and M=16), {el:.1f} s; "
-                   "dequant single-threaded, GEMM split over rows"),
-        "ms_per_step": 1e3 * el / steps,
+        "sample": (f"one oracle dequant + fp64 GEMM per case: the {N_}x{K_} g{G_} and "
+                   "4096x14336 g1024 layers at M=1 and M=16, single-threaded and on "
+                   f"{threads} threads (GEMM split over rows); value = config-2 step "
+                   f"(M=1 then M=16) on {threads} threads; {el:.1f} s in total"),
+        "cases": cases,
     }
 
 
@@ -130,7 +152,7 @@ def _setup(torch, any4, workloads, sets_arg: int, cfg: int = 2):
     inp = workloads.generate(cfg)
     N_, K_, G_ = inp.N, inp.K, inp.g
     wb = weight_bytes(N_, K_, G_)
-    R = sets_arg or max(2, math.ceil(2 * CACHE_BYTES / wb) + 1)
+    R = sets_arg or rotating_sets(wb)
 
     def b16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
@@ -189,7 +211,7 @@ def lowbit_layer(torch, any4, workloads, cfg: int, steps: int, bits: int = 2) ->
     dev = torch.device("cuda:0")
     inp = workloads.generate(cfg)
     wb = c.N * c.K * bits // 8 + 4 * c.N * (c.K // c.g) + 32 * c.N
-    R = max(2, math.ceil(2 * CACHE_BYTES / wb) + 1)
+    R = rotating_sets(wb)
 
     def b16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
@@ -241,14 +263,16 @@ def decoder_layer(torch, any4, workloads, steps: int) -> dict:
     for name, spec in workloads.CONFIG4_LAYERS.items():
         N, K = spec["N"], spec["K"]
         wb = weight_bytes(N, K, g)
-        R = max(2, math.ceil(2 * CACHE_BYTES / wb) + 1)
+        R = rotating_sets(wb)
         idx = torch.randint(0, 16, (N, K), generator=gen, dtype=torch.uint8).to(dev)
         p0 = any4.pack(idx)
         del idx
         lut = torch.randn(N, 16, generator=gen).to(torch.bfloat16).to(dev)
         al = (torch.rand(N, K // g, generator=gen) * 0.015 + 0.005).to(torch.bfloat16).to(dev)
         be = (torch.randn(N, K // g, generator=gen) * 0.002).to(torch.bfloat16).to(dev)
-        sets = [(p0.clone(), lut, al, be) for _ in range(R)]
+        # every set has its own copy of all four weight tensors
+        sets = [(p0.clone(), lut.clone(), al.clone(), be.clone()) for _ in range(R)]
+        del lut, al, be
         del p0
         x = torch.randn(max(Ms), K, generator=gen).to(torch.bfloat16).to(dev)
         ys = {M: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for M in Ms}
@@ -331,16 +355,24 @@ def quantize_timing(torch, any4, N: int, K: int, g: int, iters: int = 10) -> dic
     return out
 
 
+def launch_numbers(steps: int, Ms) -> list:
+    """(launch number, M) of every launch a graph of `steps` steps records, in
+    order: the number counts launches, so with weight set number % R no set
+    is read twice within R consecutive launches (every launch of a step, every
+    M included, reads weights the previous R - 1 launches did not touch)."""
+    return [(i * len(Ms) + j, M) for i in range(steps) for j, M in enumerate(Ms)]
+
+
 def _graph(torch, launch, steps: int, Ms):
-    """Record `steps` steps of launches (one per M in Ms) in a HIP graph."""
+    """Record `steps` steps of launches (one per M in Ms) in a HIP graph;
+    launch(n, M) gets the running launch number n."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            for i in range(steps):
-                for M in Ms:
-                    launch(i, M)
+            for n, M in launch_numbers(steps, Ms):
+                launch(n, M)
     torch.cuda.synchronize()
     return g
 
@@ -364,10 +396,9 @@ def traffic_probe(torch, any4, workloads, sets_arg: int) -> int:
     """A few launches of each M and one COPY_BYTES device copy (the scale for
     the FETCH_SIZE / WRITE_SIZE counters)."""
     dev, R, sets, x, ys = _setup(torch, any4, workloads, sets_arg)
-    for i in range(6):
-        for M in MS:
-            p, l, a, b = sets[i % R]
-            any4.gemm(x[:M], p, l, a, b, G_, out=ys[M])
+    for n, M in launch_numbers(6, MS):
+        p, l, a, b = sets[n % R]
+        any4.gemm(x[:M], p, l, a, b, G_, out=ys[M])
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
     src.fill_(1)
     dst = torch.empty_like(src)
@@ -405,7 +436,7 @@ def traffic_summary(fetch_csv: str, write_csv: str) -> int:
             raise SystemExit("the last dispatch of a traffic probe is the calibration copy")
     fscale = COPY_BYTES / (fetch[-1][1] * 1024)
     wscale = COPY_BYTES / (write[-1][1] * 1024)
-    pat = re.compile(r"(k_gemm_k[mb]<(\d+),[^>]*>)")
+    pat = re.compile(r"(k_gemm_(?:km|kb|st)<(\d+),[^>]*>)")
 
     def by_m(rows):
         out = {}
@@ -442,7 +473,6 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=0, help="rotating weight sets (0 = auto)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-layers", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true")
@@ -478,9 +508,8 @@ def main() -> int:
         any4.gemm(x[:M], p, l, a, b, G_, out=ys[M])
 
     # warmup (eager), then the graphs: the timed K steps, and K launches of each M
-    for s in range(args.warmup):
-        for M in MS:
-            launch(s, M)
+    for n, M in launch_numbers(args.warmup, MS):
+        launch(n, M)
     torch.cuda.synchronize()
     K = args.steps
     g_all = _graph(torch, launch, K, MS)
@@ -548,7 +577,7 @@ def main() -> int:
     achieved = dm["bytes"] / (dm["us_per_launch"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": _traffic(dom),
-                "kernel": f"k_gemm_km (any4_gemm, M={dom})",
+                "kernel": f"k_gemm_st (any4_gemm, M={dom})",
                 "bytes_per_launch": dm["bytes"], "launch_us": dm["us_per_launch"]}
 
     out = {
@@ -584,7 +613,7 @@ def main() -> int:
         out["decoder_layer_70b"] = decoder_layer(torch, any4, workloads, min(K, 50))
         out["quantize"] = quantize_timing(torch, any4, 4096, 4096, 128)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
     return 0
 

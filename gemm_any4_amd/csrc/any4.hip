@@ -1030,9 +1030,12 @@ __global__ __launch_bounds__(GT) void k_gemm_km(const GemmArgs args)
 #pragma unroll
                 for (int h = 0; h < NX; ++h) {
                     const int c = cbase + (u0 + h) / NBG;
+                    // a chunk past K reads the zeroed bytes behind x, never the
+                    // next x row (its weights are zero, and 0 * inf is not)
                     const uint32_t xo =
-                        Cfg::XS +
-                        (static_cast<uint32_t>(j < M ? j : M - 1) * K + c * TILE_K + kq * 32) * 2;
+                        c < Kc ? Cfg::XS + (static_cast<uint32_t>(j < M ? j : M - 1) * K +
+                                            c * TILE_K + kq * 32) * 2
+                               : Cfg::XS + ((xbytes + 15u) & ~15u) + kq * 64;
 #pragma unroll
                     for (int s4 = 0; s4 < 4; ++s4)
                         xv[h][s4] = lds_at<u32x4_t>(smem, xo + s4 * 16);

@@ -122,16 +122,28 @@ size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
  * as 16-row slices, beyond that a tiled matrix-core product over weight
  * tiles dequantised in on-chip memory.
  *     y[m][n] = bf16_rne( sum_k x[m][k] * w[n][k] )
- * with w[n][k] exactly the any4_dequant value (every weight is dequantised to
- * that bf16 inside the kernel; the weights are never written to memory).  The
- * products are exact and the sum is fp32 (matrix-core accumulation), so y
- * differs from the fp64 product y_ref with those bf16 weights by the fp32
- * summation error and y's own rounding to bf16 (at most 2^-8 * |y|); that is
- * within
+ * Every weight is dequantised inside the kernel (the weights are never
+ * written to memory) as bf16_rne(fp32(alpha * v + beta)), v the table value
+ * as the kernel holds it: each table row is kept as f16 scaled by 2^-s, s
+ * chosen so that the row's largest finite magnitude lies in [2^14, 2^15)
+ * (and s >= -60).  A table value is therefore held exactly -- and w[n][k] is
+ * exactly the any4_dequant value -- when it is 0, inf, NaN, or its binary
+ * exponent is at least both (that of the row's largest finite magnitude) - 31
+ * and -77.  Any other value v of the row (more than 2^31 below the row's
+ * largest, or a bf16 subnormal) is rounded to the f16 grid of the scaled row,
+ * an error of at most 2^(s-25) (values below that become 0).
+ * The products are exact and the sum is fp32 (matrix-core accumulation), so,
+ * for tables whose values are all held exactly, y differs from the fp64
+ * product y_ref over the any4_dequant weights by the fp32 summation error and
+ * y's own rounding to bf16 (at most 2^-8 * |y|); that is within
  *     |y - y_ref| <= 2e-3 * sum_k |x[m][k] * w[n][k]| + 1e-3
  * whenever |y| <= sum_k |x[m][k] * w[n][k]| / 2 (sums with cancellation, as
- * for activations and weights of both signs).  Runs are deterministic (same
- * inputs, same bits): the summation order depends only on the shape.
+ * for activations and weights of both signs).  With values not held exactly,
+ * each such weight adds at most |alpha| * 2^(s-25) to that error: negligible
+ * where a row's small values are small in absolute terms (1.0 beside 2^-40 or
+ * subnormals), not where a row's other values are needed beside a value
+ * 2^39 times larger.  Runs are deterministic (same inputs, same bits): the
+ * summation order depends only on the shape.
  *   x                         device, [M][K] bf16, read-only.
  *   packed, lut, alpha, beta  device, read-only.
  *   y                         device, [M][N] bf16, written.

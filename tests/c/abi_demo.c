@@ -1,6 +1,6 @@
 /*
  * A caller of libany4.so through its C ABI alone: no Python, no torch.
- * Test infrastructure (tests/test_gpu_c_abi.py runs it and checks its output
+ * Test infrastructure (tests/test_gpu_zz_c_caller.py runs it and checks its output
  * against the CPU oracle).
  *
  * Usage: abi_demo IN OUT

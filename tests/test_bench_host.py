@@ -30,11 +30,17 @@ def _write_csv(path, counter, rows):
                     "Counter_Value": f"{v:.6f}"})
 
 
-def _probe_rows(gemm_vals, copy_val, fill_val):
+# the decode kernels' names as rocprofv3 prints them
+KNAMES = {"km": "k_gemm_km<{M}, 4, 0>",
+          "st": "k_gemm_st<{M}, 4, 2, true, false, 1024, 0, 2, 0>"}
+
+
+def _probe_rows(gemm_vals, copy_val, fill_val, kname="km"):
     rows = [("__amd_rocclr_copyBuffer", [999.0])]          # a set-up copy
+    arg = "(GemmArgs)" if kname == "km" else "(StArgs)"
     for i in range(6):
         for M in bench.MS:
-            rows.append((f"void (anonymous namespace)::k_gemm_km<{M}, 4, 0>(GemmArgs)",
+            rows.append((f"void (anonymous namespace)::{KNAMES[kname].format(M=M)}{arg}",
                          gemm_vals[M]))
     rows.append(("void at::native::vectorized_elementwise_kernel<16>", [fill_val]))
     rows.append(("__amd_rocclr_copyBuffer", [copy_val]))
@@ -48,21 +54,23 @@ def traffic_file(tmp_path, monkeypatch):
     return path
 
 
-def test_traffic_summary_scales_by_the_copy(tmp_path, traffic_file):
+@pytest.mark.parametrize("kname", sorted(KNAMES))
+def test_traffic_summary_scales_by_the_copy(tmp_path, traffic_file, kname):
     copy_kib = bench.COPY_BYTES / 1024
     fetch = tmp_path / "fetch.csv"
     write = tmp_path / "write.csv"
     # FETCH_SIZE reads the copy at half its size (scale 2); per-dimension rows are summed
     _write_csv(fetch, "FETCH_SIZE", _probe_rows({1: [6000.0, 4000.0], 16: [12000.0]},
-                                                copy_kib / 2, 5.0))
-    _write_csv(write, "WRITE_SIZE", _probe_rows({1: [28.0], 16: [448.0]}, copy_kib, copy_kib))
+                                                copy_kib / 2, 5.0, kname))
+    _write_csv(write, "WRITE_SIZE", _probe_rows({1: [28.0], 16: [448.0]}, copy_kib, copy_kib,
+                                                kname))
     assert bench.traffic_summary(str(fetch), str(write)) == 0
     t = json.loads(traffic_file.read_text())
     assert t["kernel_source_sha256_16"] == bench.kernel_source_hash()
     assert t["fetch_scale"] == pytest.approx(2.0)
     assert t["write_scale"] == pytest.approx(1.0)
     m1, m16 = t["per_m"]["1"], t["per_m"]["16"]
-    assert m1["kernel"] == "k_gemm_km<1, 4, 0>" and m1["dispatches"] == 6
+    assert m1["kernel"] == KNAMES[kname].format(M=1) and m1["dispatches"] == 6
     assert m1["hbm_bytes_per_launch"] == round(10000 * 1024 * 2 + 28 * 1024)
     assert m16["hbm_bytes_per_launch"] == round(12000 * 1024 * 2 + 448 * 1024)
     assert m1["algorithmic_bytes"] == bench.algorithmic_bytes(1, bench.N_, bench.K_, bench.G_)
@@ -89,3 +97,19 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("Ms", [bench.MS, (1,), (16,)])
+def test_no_weight_set_is_read_twice_within_the_rotation(Ms):
+    """Every launch of a recorded graph -- both launches of a step included --
+    reads a weight set that none of the previous R - 1 launches read, and
+    R - 1 sets of the benchmark layer exceed twice the last-level cache."""
+    R = bench.rotating_sets(bench.weight_bytes(bench.N_, bench.K_, bench.G_))
+    assert (R - 1) * bench.weight_bytes(bench.N_, bench.K_, bench.G_) > 2 * bench.CACHE_BYTES
+    seq = [n % R for n, _ in bench.launch_numbers(50, Ms)]
+    assert len(seq) == 50 * len(Ms)
+    for i in range(len(seq)):
+        window = seq[max(0, i - R + 1):i + 1]
+        assert len(set(window)) == len(window), (i, window)
+    # every M of a step is recorded, in order
+    assert [M for _, M in bench.launch_numbers(2, Ms)] == list(Ms) * 2
