@@ -219,8 +219,9 @@ def dequant(packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor, beta: 
     return out
 
 
-# One zeroed workspace per (device, stream): calls on one stream run one after
-# another, and each call leaves its workspace zeroed again.
+# One workspace per (device, stream), grown on demand: calls on one stream run
+# one after another, so they can share it.  The kernels write every partial
+# sum before they read it, so it needs no initialisation.
 _workspaces: dict = {}
 
 
@@ -228,7 +229,7 @@ def _workspace(need: int, device: torch.device, stream_handle: int) -> torch.Ten
     key = (device.index, stream_handle)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(max(need, 1 << 16), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(need, 1 << 16), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -239,8 +240,10 @@ def gemm(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: torch.
     """y [M, N] = x [M, K] * W^T with W the any4 weights (N from lut).
 
     workspace: optional uint8 device tensor of at least workspace_size(M, N, K, g)
-    bytes, all zero before its first use (each call leaves it zeroed).  By
-    default a workspace kept per device and stream is used."""
+    bytes (contents need not be initialised); with it, K may be split over
+    workgroups, their fp32 partial sums kept there.  An empty tensor runs the
+    kernels that need no workspace.  By default a workspace kept per device
+    and stream is used."""
     _b16(x, "x"), _b16(lut, "lut"), _b16(alpha, "alpha"), _b16(beta, "beta")
     M, K = x.shape
     if lut.dim() != 2 or lut.shape[1] != 16:
@@ -260,7 +263,9 @@ def gemm(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: torch.
     if need:
         if workspace is None:
             workspace = _workspace(need, x.device, sh)
-        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        if workspace.numel():
+            _dev(workspace, "workspace")
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     check(gemm_raw(_ptr(x), _ptr(packed), _ptr(lut), _ptr(alpha), _ptr(beta), _ptr(out), M, N, K,
                    g, ws_ptr, ws_bytes, sh))
     return out

@@ -455,6 +455,8 @@ struct GemmArgs {
     const uint16_t* beta;
     uint16_t* y;
     int M, N, K, g;
+    float* ws;          // split-K partial sums (k_gemm_st), or null: no split
+    size_t ws_bytes;
 };
 
 // Byte address of table entry `byte j of d` in the lane's slot: (d.byte[j] << 8) | slot4.
@@ -562,6 +564,29 @@ __device__ __forceinline__ void store_pairs(uint8_t* smem, uint32_t base, int q,
         const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
         lds_at<uint32_t>(smem, base + (grp * 16 + row) * 4) =
             __builtin_amdgcn_perm(qb[i >> 1], qa[i >> 1], sel);
+        if (++grp == G) {
+            grp = 0;
+            ++row;
+        }
+    }
+}
+
+// store_pairs for a staged range of groups: of the 8 values of piece q
+// (elements 8q..8q+7 of the block's [16][G] arrays), those of groups
+// gbase..gbase+GS-1, stored as [group - gbase][row].
+__device__ __forceinline__ void store_pairs_range(uint8_t* smem, uint32_t base, int q, int G,
+                                                  int gbase, int GS, const u32x4_t& qa,
+                                                  const u32x4_t& qb)
+{
+    int row = (8 * q) / G;
+    int grp = 8 * q - row * G;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        const int gi = grp - gbase;
+        if (gi >= 0 && gi < GS && row < 16)
+            lds_at<uint32_t>(smem, base + (gi * 16 + row) * 4) =
+                __builtin_amdgcn_perm(qb[i >> 1], qa[i >> 1], sel);
         if (++grp == G) {
             grp = 0;
             ++row;
@@ -1852,7 +1877,8 @@ __global__ __launch_bounds__(64 * PROBE_WAVES) void k_read_probe(const uint8_t* 
 //   [0, ZERO)  pair tables: table b in 64 KB region b/2, half b%2, entry e at
 //              e*256 + (b%2)*128 + slot*4; the partial sums reuse it
 //   ZERO       256 zero bytes (64 KB aligned: the table reads of dead tiles)
-//   AB         [NBG][G][16 rows] (alpha | beta << 16) dwords
+//   AB         [NBG][GS][16 rows] (alpha | beta << 16) dwords: the GS groups
+//              from gbase on that the workgroup's chunks touch
 //   LUTS       [NBG][4 row quads][16 entries][4 rows] f16, each row scaled by 2^-s
 //   SCL        [NBG][16 rows] int: the row scale exponents s
 //   XS, XZ     (XL) x as [M][K] bf16, then 256 zero bytes (x of dead chunks)
@@ -1860,12 +1886,14 @@ struct StLayout {
     uint32_t zero, ab, luts, scl, xs, xz, total;
 };
 
-__host__ __device__ inline StLayout st_layout(int nbg, int G, int M, int K, bool xl)
+// GS: the groups of alpha/beta staged per block (all K/g without a split of
+// K, else those of one split's chunks)
+__host__ __device__ inline StLayout st_layout(int nbg, int GS, int M, int K, bool xl)
 {
     StLayout L;
     L.zero = static_cast<uint32_t>((nbg + 1) / 2) * 65536u;
     L.ab = L.zero + 256;
-    L.luts = L.ab + static_cast<uint32_t>(nbg) * G * 64;
+    L.luts = L.ab + static_cast<uint32_t>(nbg) * GS * 64;
     L.scl = L.luts + nbg * 512;
     L.xs = L.scl + nbg * 64;
     L.xz = L.xs + (xl ? ((static_cast<uint32_t>(M) * K * 2 + 15u) & ~15u) : 0u);
@@ -1879,6 +1907,8 @@ constexpr int ST_XP = 4;   // 16-byte pieces of x per thread (XL)
 
 struct StArgs {
     GemmArgs a;
+    int splits;    // K is split over this many workgroups (partial sums in a.ws)
+    int gstage;    // alpha/beta groups staged per block (GS)
     int cw;        // chunks per wave (a multiple of R)
     StLayout L;
     unsigned long long* ts;   // per-wave timestamps (probe builds only), or null
@@ -1913,13 +1943,21 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
     const int NB = (N + TILE_ROWS - 1) / TILE_ROWS;
     const int G = K / g;
     const int gc = g / TILE_K;   // chunks per group
-    const int Gs = gridDim.x;
-    const int r = blockIdx.x;
+    // with splits S, workgroup r' = split * Gs + r takes chunks
+    // [split*KcS, (split+1)*KcS) of the same row blocks as workgroup r
+    const int S = sa.splits;
+    const int Gs = gridDim.x / S;
+    const int split = blockIdx.x / Gs;
+    const int r = blockIdx.x - split * Gs;
+    const int KcS = (Kc + S - 1) / S;
+    const int kend = min((split + 1) * KcS, Kc);   // chunks from kend on are dead
     const int nblk = r < NB ? (NB - 1 - r) / Gs + 1 : 0;
     const int ngroups = MG ? (nblk + NBG - 1) / NBG : 1;
     const int cw = sa.cw;
     const int bpg = cw / R;        // bodies per group
-    const int c0 = wave * cw;
+    const int c0 = split * KcS + wave * cw;
+    const int GS = sa.gstage;
+    const int gbase = (split * KcS) / gc;   // first staged group
 #ifdef ANY4_PROBE_TS
     unsigned long long* ts = sa.ts ? sa.ts + (static_cast<size_t>(r) * NW + wave) * 8 : nullptr;
     auto stamp = [&](int i) {
@@ -1964,7 +2002,12 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int blk = gi * NBG + ab_blk[h];
-            const bool live = ab_blk[h] < NBG && blk < nblk;
+            // the piece's 8 values are groups g0..g0+7 (mod G) of its rows:
+            // loaded only if one of them is staged
+            const int g0 = (8 * ab_pc[h]) % G;
+            const bool need = G <= GS || (g0 + 7 >= gbase && g0 < gbase + GS) ||
+                              (g0 + 7 >= G && (g0 + 7 - G) >= gbase);
+            const bool live = ab_blk[h] < NBG && blk < nblk && need;
             const uint32_t o = (static_cast<uint32_t>(r + blk * Gs) * (G * 32) + ab_pc[h] * 16) |
                                (static_cast<uint32_t>(!live) << 31);
             aq[h] = load16(ra, o);
@@ -1990,7 +2033,8 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
             if (ab_blk[h] < NBG)
-                store_pairs(smem, L.ab + ab_blk[h] * G * 64, ab_pc[h], G, aq[h], bq[h]);
+                store_pairs_range(smem, L.ab + ab_blk[h] * GS * 64, ab_pc[h], G, gbase, GS, aq[h],
+                                  bq[h]);
     };
     // Pair tables of the group with 16-byte writes.  Item it = (block b, half
     // h, hi, slot quad q) writes slots 4q..4q+3 (rows 4(q%4)..+3) of the
@@ -2069,7 +2113,7 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
         const int s = (k - gi * bpg) * R + u / NBG;
         const int blk = gi * NBG + u % NBG;
         const int c = c0 + s;
-        const bool live = gi < ngroups && blk < nblk && c < Kc;
+        const bool live = gi < ngroups && blk < nblk && c < kend;
         const uint32_t uo = (static_cast<uint32_t>(r + blk * Gs) * static_cast<uint32_t>(Kc) + c) * TB |
                             (static_cast<uint32_t>(!live) << 31);
         pb[u % D] = A2   ? load8_nt(rp, off2(tile_lane, uo))
@@ -2077,7 +2121,7 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
                          : load16_nt(rp, off2(tile_lane, uo));
         if constexpr (XSTREAM) {
             if (u % NBG == 0) {
-                const bool xl = gi < ngroups && c < Kc;
+                const bool xl = gi < ngroups && c < kend;
                 const uint32_t xc = static_cast<uint32_t>(c) * TILE_K * 2 | (static_cast<uint32_t>(!xl) << 31);
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4)
@@ -2182,8 +2226,8 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
             const int grp = min(c / gc, G - 1);
             u32x4_t xv[4];
             if constexpr (XL) {
-                const uint32_t xo = c < Kc ? L.xs + (static_cast<uint32_t>(jr) * K + c * TILE_K + kq * 32) * 2
-                                           : L.xz + kq * 64;
+                const uint32_t xo = c < kend ? L.xs + (static_cast<uint32_t>(jr) * K + c * TILE_K + kq * 32) * 2
+                                             : L.xz + kq * 64;
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4)
                     xv[s4] = lds_at<u32x4_t>(smem, xo + s4 * 16);
@@ -2191,7 +2235,7 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
 #pragma unroll
             for (int b = 0; b < NBG; ++b) {
                 const int u = s * NBG + b;
-                const bool live = gi * NBG + b < nblk && c < Kc;
+                const bool live = gi * NBG + b < nblk && c < kend;
                 const u32x4_t p = pb[u % D];
                 const uint32_t sv = slot4 | (live ? static_cast<uint32_t>(b >> 1) << 16 : L.zero);
                 u32x4_t bw[4];
@@ -2217,8 +2261,9 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
                                 smem, __builtin_amdgcn_perm(pd[s4], sv, 0x0C020000u | ((4u + jb) << 8)) +
                                           (b & 1) * 128);
                 }
-                const uint32_t pr = lds_at<uint32_t>(smem, L.ab + b * G * 64 + (grp * 16 + j) * 4) &
-                                    (live ? 0xFFFFFFFFu : 0u);
+                const uint32_t pr =
+                    lds_at<uint32_t>(smem, L.ab + b * GS * 64 + (min(grp - gbase, GS - 1) * 16 + j) * 4) &
+                    (live ? 0xFFFFFFFFu : 0u);
                 const float a = __builtin_ldexpf(bf16_to_f32(pr & 0xFFFFu), rsc[b]);
                 const float bt = bf16_to_f32(pr >> 16);
 #pragma unroll
@@ -2266,8 +2311,12 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
                 const int l = o / VC;
                 const int m = (l >> 4) * 4 + (o - l * VC);
                 const int n = (r + blk * Gs) * TILE_ROWS + (l & 15);
-                if (blk < nblk && m < M && n < N)
-                    args.y[static_cast<size_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16(tot));
+                if (blk < nblk && m < M && n < N) {
+                    if (S > 1)   // this split's partial sum, added up by k_split_sum
+                        args.ws[(static_cast<size_t>(split) * M + m) * N + n] = tot;
+                    else
+                        args.y[static_cast<size_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16(tot));
+                }
             }
             stamp(7);
             if constexpr (MG) {
@@ -2379,12 +2428,50 @@ void launch_gemm(const GemmArgs& a, hipStream_t stream)
         hipLaunchKernelGGL((k_gemm_kb<MT, 4, false, FMT>), gd, dim3(GT), 0, stream, a);
 }
 
+// ---- k_split_sum: y = bf16(sum over splits of the partial sums) ------------
+// The partial sums of the S workgroups that split K, added in split order
+// (so the result does not depend on which workgroup finished first), then
+// rounded once to bf16.  ws is [S][M][N] fp32.
+__global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ ws,
+                                                   uint16_t* __restrict__ y, int S, size_t mn)
+{
+    const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= mn)
+        return;
+    float t = ws[i];
+    for (int s = 1; s < S; ++s)
+        t += ws[static_cast<size_t>(s) * mn + i];
+    y[i] = static_cast<uint16_t>(f32_to_bf16(t));
+}
+
 // ---- k_gemm_st launch: the shape decides waves, blocks per group and ring --
 struct StPlan {
-    int grid, nw, nbg, r, cw;
+    int grid, nw, nbg, r, cw, splits, gstage;
     bool mg, xl;
     StLayout L;
 };
+
+// Split K over S workgroups when x, read once per workgroup for all of the
+// workgroup's K, would cost more than the weights: M > 2 (the x loads are
+// full-width whatever M) with one or two row blocks per CU and K of 12288 or
+// more; then each workgroup takes four row blocks over K/S.  Needs a
+// workspace of S*M*N fp32 partial sums.  (Measured at M = 16: 4096x14336
+// 20.4 -> 16.8 us, 8192x28672 45.7 -> 37.4 us; 8192x8192 gained nothing.)
+inline int st_splits(int M, int N, int K)
+{
+    const int NB = static_cast<int>(row_blocks(N));
+    const int grid = NB < KM_GRID ? NB : KM_GRID;
+    const int nb = grid > 0 ? (NB + grid - 1) / grid : 0;
+    if (M <= 2 || nb < 1 || nb > 2 || K / TILE_K < 96 || NB < KM_GRID)
+        return 1;
+    return 4 / nb;
+}
+
+size_t st_workspace_bytes(int M, int N, int K)
+{
+    const int S = st_splits(M, N, K);
+    return S > 1 ? static_cast<size_t>(S) * M * N * sizeof(float) : 0;
+}
 
 // Ring depths that fit 128 VGPRs (16 waves per CU) without spilling: x in
 // the ring costs 16 registers per chunk, the next group's staging 20.
@@ -2404,18 +2491,24 @@ constexpr bool st_ring_ok(int nbg, int r, bool xl, bool mg)
 #ifdef ANY4_PROBE_TS
 int st_force_nw = 0, st_force_r = 0;
 #endif
-inline bool st_plan(int M, int N, int K, int g, StPlan& P)
+inline bool st_plan(int M, int N, int K, int g, bool split_ok, StPlan& P)
 {
     const int NB = static_cast<int>(row_blocks(N));
-    const int Kc = K / TILE_K;
     const int G = K / g;
-    P.grid = NB < KM_GRID ? NB : KM_GRID;
-    const int nb = (NB + P.grid - 1) / P.grid;
+    P.splits = split_ok ? st_splits(M, N, K) : 1;
+    const int Kc = (K / TILE_K + P.splits - 1) / P.splits;   // chunks of one split
+    const int gcn = g / TILE_K;
+    // alpha/beta groups a split's chunks touch (its first chunk need not start a group)
+    const int gtouch = (Kc + gcn - 1) / gcn + 1;
+    P.gstage = P.splits > 1 && gtouch < G ? gtouch : G;
+    const int gs = NB * P.splits < KM_GRID ? NB : KM_GRID / P.splits;   // workgroups per split
+    P.grid = gs * P.splits;
+    const int nb = (NB + gs - 1) / gs;
     for (int nbg = nb <= 1 ? 1 : nb <= 2 ? 2 : 4; nbg >= 1; nbg /= 2) {
         const bool mg = nb > nbg;
         for (int xi = M <= 2 ? 0 : 1; xi < 2; ++xi) {
             const bool xl = xi == 0;
-            const StLayout L = st_layout(nbg, G, M, K, xl);
+            const StLayout L = st_layout(nbg, P.gstage, M, K, xl);
             if (L.total > ST_LDS)
                 continue;
             int best = -1;
@@ -2500,9 +2593,9 @@ template <int MT, int FMT>
 bool launch_st(const GemmArgs& a, hipStream_t stream, unsigned long long* ts)
 {
     StPlan P;
-    if (!st_plan(a.M, a.N, a.K, a.g, P))
+    if (!st_plan(a.M, a.N, a.K, a.g, a.ws != nullptr, P))
         return false;
-    StArgs sa{a, P.cw, P.L, ts};
+    StArgs sa{a, P.splits, P.gstage, P.cw, P.L, ts};
     switch (P.nbg * 16 + P.r) {
     case 16 + 1: st_go_r<MT, 1, 1, FMT>(sa, P, stream); break;
     case 16 + 2: st_go_r<MT, 1, 2, FMT>(sa, P, stream); break;
@@ -2514,6 +2607,11 @@ bool launch_st(const GemmArgs& a, hipStream_t stream, unsigned long long* ts)
     case 64 + 1: st_go_r<MT, 4, 1, FMT>(sa, P, stream); break;
     case 64 + 2: st_go_r<MT, 4, 2, FMT>(sa, P, stream); break;
     default: return false;
+    }
+    if (P.splits > 1) {
+        const size_t mn = static_cast<size_t>(a.M) * a.N;
+        hipLaunchKernelGGL(k_split_sum, dim3(static_cast<unsigned>((mn + 255) / 256)), dim3(256), 0,
+                           stream, a.ws, a.y, P.splits, mn);
     }
     return true;
 }
@@ -2566,7 +2664,8 @@ static void launch_big(const GemmArgs& a, int fmt, hipStream_t stream)
 // and any3_gemm.
 static any4_status gemm_call(int fmt, const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
                       const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
-                      int64_t N, int64_t K, int64_t g, hipStream_t stream)
+                      int64_t N, int64_t K, int64_t g, hipStream_t stream,
+                      void* workspace = nullptr, size_t workspace_bytes = 0)
 {
     const bool i4 = fmt == FMT_INT4;
     if (M < 0 || N < 0 || !group_ok(K, g) || K / (g > 0 ? g : 1) > MAX_G ||
@@ -2583,6 +2682,14 @@ static any4_status gemm_call(int fmt, const uint16_t* x, const uint8_t* packed, 
     if (!aligned(y, 2) || (K > 0 && (!aligned(x, 16) || !aligned(packed, 16) ||
                                      (!i4 && !aligned(lut, 16)) || !aligned(alpha, 16) ||
                                      !aligned(beta, 16))))
+        return ANY4_E_ALIGN;
+    // the workspace is optional: with one, K may be split over workgroups
+    const size_t need = M <= 16 && K > 0 ? st_workspace_bytes(static_cast<int>(M),
+                                                              static_cast<int>(N),
+                                                              static_cast<int>(K)) : 0;
+    if (workspace && workspace_bytes < need)
+        return ANY4_E_WORKSPACE;
+    if (workspace && !aligned(workspace, 16))
         return ANY4_E_ALIGN;
     (void)hipGetLastError();
     if (K == 0) {
@@ -2602,6 +2709,8 @@ static any4_status gemm_call(int fmt, const uint16_t* x, const uint8_t* packed, 
     a.N = static_cast<int>(N);
     a.K = static_cast<int>(K);
     a.g = static_cast<int>(g);
+    a.ws = need > 0 && workspace ? static_cast<float*>(workspace) : nullptr;
+    a.ws_bytes = a.ws ? workspace_bytes : 0;
     if (M > 16 && M <= 48) {
         // a few decode batches: the streaming kernels on 16-row slices of x and
         // y (each slice re-reads the weights, still cheaper than the tiled
@@ -2610,6 +2719,7 @@ static any4_status gemm_call(int fmt, const uint16_t* x, const uint8_t* packed, 
             GemmArgs s16 = a;
             s16.x = x + m0 * K;
             s16.y = y + m0 * N;
+            s16.ws = nullptr;   // the slices do not split K
             s16.M = static_cast<int>(M - m0 < 16 ? M - m0 : 16);
             launch_decode(s16, fmt, stream);
         }
@@ -2761,11 +2871,10 @@ any4_status any4_dequant(const uint8_t* packed, const uint16_t* lut, const uint1
 
 size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g)
 {
-    (void)M;
-    (void)N;
-    (void)K;
-    (void)g;
-    return 0;   // neither kernel needs device scratch
+    if (M <= 0 || M > 16 || N <= 0 || K <= 0 || !group_ok(K, g) ||
+        N >= (static_cast<int64_t>(1) << 31) || K >= (static_cast<int64_t>(1) << 31))
+        return 0;
+    return st_workspace_bytes(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
 }
 
 any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
@@ -2773,9 +2882,8 @@ any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* 
                       int64_t N, int64_t K, int64_t g, void* workspace, size_t workspace_bytes,
                       hipStream_t stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;
-    return gemm_call(FMT_ANY4, x, packed, lut, alpha, beta, y, M, N, K, g, stream);
+    return gemm_call(FMT_ANY4, x, packed, lut, alpha, beta, y, M, N, K, g, stream, workspace,
+                     workspace_bytes);
 }
 
 any4_status any4_gemm_int4(const uint16_t* x, const uint8_t* packed, const uint16_t* alpha,

@@ -108,10 +108,14 @@ any4_status any4_dequant(const uint8_t* packed, const uint16_t* lut, const uint1
                          hipStream_t stream);
 
 /*
- * any4_gemm_workspace_size -- bytes of device workspace any4_gemm needs for
- * this shape.  The current kernels need none: it returns 0 for every shape.
- * (The workspace arguments stay in the ABI so that a kernel that needs
- * scratch can be added without changing it.)
+ * any4_gemm_workspace_size -- bytes of device workspace with which any4_gemm
+ * may split K over several workgroups for this shape, or 0 when it does not
+ * split.  It splits for M = 3..16 when the weights give each CU one or two
+ * 16-row blocks (N/16 between 256 and 512 on the 256 CUs of an MI355X) and K
+ * is at least 12288: then x, which every workgroup reads for its whole K,
+ * would cost more than the weights.  The workspace then holds S*M*N fp32
+ * partial sums (S = 4 / blocks per CU), added up in a fixed order.  Invalid
+ * shapes give 0.
  */
 size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
 
@@ -150,10 +154,16 @@ size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
  *   M >= 0 (at most 65535*64), N >= 0, K >= 0 with K % g == 0 and K/g <= 512.
  *   M*N == 0 is a no-op; K == 0 writes y = 0 (x, packed, lut, alpha and beta
  *   may then be NULL).
- *   workspace, workspace_bytes  device scratch of at least
- *       any4_gemm_workspace_size(M, N, K, g) bytes; NULL and 0 when that is 0,
- *       which it is for every shape today.
- * Errors: ANY4_E_SHAPE, ANY4_E_NULL, ANY4_E_ALIGN, ANY4_E_WORKSPACE, ANY4_E_HIP.
+ *   workspace, workspace_bytes  optional device scratch, 16-byte aligned,
+ *       owned by the caller, contents need not be initialised.  With at least
+ *       any4_gemm_workspace_size(M, N, K, g) bytes the call may split K over
+ *       workgroups (a second kernel then adds the partial sums in split order,
+ *       so results stay deterministic); with NULL it uses kernels that need no
+ *       scratch (same result bound, another summation order).  Calls that
+ *       share one workspace must be ordered (e.g. one stream).
+ * Errors: ANY4_E_SHAPE, ANY4_E_NULL, ANY4_E_ALIGN (also a misaligned
+ * workspace), ANY4_E_WORKSPACE (a non-NULL workspace smaller than
+ * any4_gemm_workspace_size), ANY4_E_HIP.
  */
 any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
                       const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
@@ -167,9 +177,10 @@ any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* 
  *     w[n][k] = bf16_rne( fp32( alpha[n][k/g] * q[n][k] + beta[n][k/g] ) )
  *     y[m][n] = bf16_rne( sum_k x[m][k] * w[n][k] )
  * q[n][k] is the 4-bit code in `packed` (same tile layout), read as 0..15.
- * The result is bit-identical to any4_gemm with every table row 0, 1, .., 15,
- * and carries the same error bound.  Arguments, sizes, alignment and errors as
- * any4_gemm, without lut and without the (always empty) workspace.
+ * The result is bit-identical to any4_gemm with every table row 0, 1, .., 15
+ * and a NULL workspace (K is never split here), and carries the same error
+ * bound.  Arguments, sizes, alignment and errors as any4_gemm, without lut
+ * and without a workspace.
  */
 any4_status any4_gemm_int4(const uint16_t* x, const uint8_t* packed, const uint16_t* alpha,
                            const uint16_t* beta, uint16_t* y, int64_t M, int64_t N, int64_t K,

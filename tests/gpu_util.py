@@ -17,6 +17,13 @@ def require_gpu():
         raise RuntimeError("GPU test run without a visible GPU")
 
 
+def no_workspace() -> torch.Tensor:
+    """An empty workspace: any4_gemm then uses the kernels that need none (K
+    is not split), the same summation order as the entry points without a
+    workspace argument."""
+    return torch.empty(0, dtype=torch.uint8, device=DEV)
+
+
 def dev_u8(a) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(DEV)
 

@@ -64,7 +64,7 @@ def test_any3_dequant_bitexact(N, K, g):
 def test_any3_gemm(M, N, K, g):
     L = Layer3(M * 17 + N + K, M, N, K, g)
     y = any4.any3_gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g)
-    y4 = any4.gemm(L.x, L.packed4, L.lut, L.alpha, L.beta, g)
+    y4 = any4.gemm(L.x, L.packed4, L.lut, L.alpha, L.beta, g, workspace=gu.no_workspace())
     torch.cuda.synchronize()
     assert np.array_equal(gu.host_b16(y), gu.host_b16(y4))
     rows = np.arange(N)

@@ -268,7 +268,8 @@ def test_gemm_int4(M, N, K, g, cfg):
     L = gu.Layer(workloads.Any4Inputs(inp.N, inp.K, inp.g, inp.idx, lut, inp.alpha, inp.beta,
                                       x_host))
     y4 = any4.gemm_int4(x, L.packed, L.alpha, L.beta, inp.g)
-    y = any4.gemm(x, L.packed, L.lut, L.alpha, L.beta, inp.g)
+    y = any4.gemm(x, L.packed, L.lut, L.alpha, L.beta, inp.g, workspace=gu.no_workspace())
+    ys = any4.gemm(x, L.packed, L.lut, L.alpha, L.beta, inp.g)   # K may be split
     torch.cuda.synchronize()
     assert np.array_equal(gu.host_b16(y4), gu.host_b16(y))
     w_int4 = L.w_ref()     # the oracle's dequant with the identity table is int4
@@ -277,8 +278,9 @@ def test_gemm_int4(M, N, K, g, cfg):
         rng = np.random.default_rng(M)
         rows = np.unique(np.concatenate([[0, inp.N - 1], rng.choice(inp.N, 300, replace=False)]))
     y_ref, ad = oracle.gemm(x_host, w_int4[rows], nthreads=oracle.default_threads())
-    gu.assert_within_bound(y4[:, torch.from_numpy(rows).to(gu.DEV)], y_ref, ad,
-                           f"int4 {M}x{inp.N}x{inp.K} g{inp.g}")
+    sel = torch.from_numpy(rows).to(gu.DEV)
+    gu.assert_within_bound(y4[:, sel], y_ref, ad, f"int4 {M}x{inp.N}x{inp.K} g{inp.g}")
+    gu.assert_within_bound(ys[:, sel], y_ref, ad, f"table 0..15 {M}x{inp.N}x{inp.K} g{inp.g}")
 
 
 def test_gemm_int4_empty_and_k0():
@@ -536,3 +538,53 @@ def test_inf_in_one_x_row_stays_in_that_row(N, K):
     assert torch.isfinite(y[0].float()).all()
     y_ref, ad = oracle.gemm(x[:1], L.w_ref())
     gu.assert_within_bound(y[:1], y_ref, ad, f"row 0 beside an inf row, {N}x{K}")
+
+
+# --------------------------------------------------------------------------
+# K split over workgroups (with a workspace): long K, one or two row blocks
+# per CU, M > 2; partial sums added in split order by a second kernel
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg,M", [(3, 4), (3, 8), (3, 16)])
+def test_split_k_config3(cfg, M):
+    L = gu.config_layer(cfg)
+    need = any4.workspace_size(M, L.N, L.K, L.g)
+    assert need == 4 * M * L.N * 4          # four splits of fp32 partial sums
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=gu.DEV)   # never zeroed
+    y1 = any4.gemm(L.x[:M], L.packed, L.lut, L.alpha, L.beta, L.g, workspace=ws)
+    y2 = any4.gemm(L.x[:M], L.packed, L.lut, L.alpha, L.beta, L.g, workspace=ws)
+    y0 = any4.gemm(L.x[:M], L.packed, L.lut, L.alpha, L.beta, L.g, workspace=gu.no_workspace())
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))   # deterministic
+    y_ref, ad = gu.config_ref(cfg, M)
+    r1 = gu.assert_within_bound(y1, y_ref, ad, f"split K, config {cfg} M={M}")
+    r0 = gu.assert_within_bound(y0, y_ref, ad, f"unsplit, config {cfg} M={M}")
+    print(f"config {cfg} M={M}: split max err/tol {r1:.3e}, unsplit {r0:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("M,N,K,g", [(3, 16 * 256, 12288, 128), (16, 16 * 512, 28672, 128),
+                                     (5, 16 * 300, 16384 + 128, 128), (9, 16 * 256 + 3, 12800, 256)])
+def test_split_k_ragged(M, N, K, g):
+    inp = workloads.generic(M * 19 + N + K, M, N, K, g)
+    L = gu.Layer(inp)
+    assert any4.workspace_size(M, N, K, g) > 0
+    y = any4.gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g)
+    torch.cuda.synchronize()
+    y_ref, ad = oracle.gemm(inp.x, L.w_ref(), nthreads=oracle.default_threads())
+    gu.assert_within_bound(y, y_ref, ad, f"split K {M}x{N}x{K} g{g}")
+
+
+def test_split_k_workspace_errors():
+    L = gu.config_layer(3)
+    M = 16
+    need = any4.workspace_size(M, L.N, L.K, L.g)
+    small = torch.zeros(need - 16, dtype=torch.uint8, device=gu.DEV)
+    y = torch.zeros((M, L.N), dtype=torch.bfloat16, device=gu.DEV)
+    s = any4.gemm_raw(L.x.data_ptr(), L.packed.data_ptr(), L.lut.data_ptr(), L.alpha.data_ptr(),
+                      L.beta.data_ptr(), y.data_ptr(), M, L.N, L.K, L.g, small.data_ptr(),
+                      small.numel())
+    assert s == 4          # ANY4_E_WORKSPACE, nothing launched
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y.float()) == 0
+    assert any4.workspace_size(1, L.N, L.K, L.g) == 0       # M <= 2: never split
+    assert any4.workspace_size(16, 14336, 4096, 128) == 0   # short K: never split
+    assert any4.workspace_size(16, 8192, 8192, 128) == 0
