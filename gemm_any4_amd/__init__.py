@@ -39,7 +39,7 @@ _STATUS_NAMES = {0: "ANY4_OK", 1: "ANY4_E_NULL", 2: "ANY4_E_SHAPE", 3: "ANY4_E_A
 
 # every symbol include/any4.h declares
 EXPORTS = ("any4_packed_bytes", "any4_pack", "any4_dequant", "any4_gemm_workspace_size",
-           "any4_gemm", "any4_gemm_int4", "any4_quantize", "any4_status_string",
+           "any4_gemm", "any4_gemm_noalloc", "any4_gemm_int4", "any4_quantize", "any4_status_string",
            "any2_packed_bytes", "any2_pack", "any2_dequant", "any2_gemm",
            "any3_packed_bytes", "any3_pack", "any3_dequant", "any3_gemm", "any4_read_probe")
 
@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.any4_gemm_workspace_size.argtypes = [I64, I64, I64, I64]
         L.any4_gemm.restype = ctypes.c_int
         L.any4_gemm.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P, SZ, P]
+        L.any4_gemm_noalloc.restype = ctypes.c_int
+        L.any4_gemm_noalloc.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
         L.any4_gemm_int4.restype = ctypes.c_int
         L.any4_gemm_int4.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
         L.any4_quantize.restype = ctypes.c_int
@@ -159,6 +161,12 @@ def gemm_raw(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
              ws_ptr=None, ws_bytes=0, stream=None) -> int:
     return lib().any4_gemm(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
                            ws_ptr, ws_bytes, _stream(stream))
+
+
+def gemm_noalloc_raw(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
+                     stream=None) -> int:
+    return lib().any4_gemm_noalloc(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M,
+                                   N, K, g, _stream(stream))
 
 
 def gemm_int4_raw(x_ptr, packed_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,

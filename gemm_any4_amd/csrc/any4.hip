@@ -33,6 +33,8 @@
 //   k_zero                 y = 0 when K = 0.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "any4.h"
 
 namespace {
@@ -2799,6 +2801,40 @@ static any4_status lowbit_dequant(int bits, const uint8_t* packed, const uint16_
 // ---------------------------------------------------------------------------
 // C ABI
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// allocation-free GEMM: the split-K partial sums in a static device array
+// ---------------------------------------------------------------------------
+// Each GPU the library runs on holds its own copy of `scratch` until the
+// process ends.  Host code never passes the array's name to a kernel: in
+// host code that name is only a stand-in for the device symbol, so its
+// device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and kept in scratch_ptr.
+constexpr size_t SCRATCH_BYTES = static_cast<size_t>(4) << 20;   // 4 MiB per GPU
+static __device__ __attribute__((aligned(256))) uint8_t scratch[SCRATCH_BYTES];
+
+namespace {
+constexpr int SCRATCH_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[SCRATCH_DEVICES];
+
+// The current device's copy of `scratch` (looked up on its first use there).
+any4_status scratch_of_current_device(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_DEVICES)
+        return ANY4_E_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return ANY4_E_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return ANY4_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char* any4_status_string(any4_status s)
@@ -2884,6 +2920,24 @@ any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* 
 {
     return gemm_call(FMT_ANY4, x, packed, lut, alpha, beta, y, M, N, K, g, stream, workspace,
                      workspace_bytes);
+}
+
+any4_status any4_gemm_noalloc(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
+                              const uint16_t* alpha, const uint16_t* beta, uint16_t* y,
+                              int64_t M, int64_t N, int64_t K, int64_t g, hipStream_t stream)
+{
+    // the same kernels as any4_gemm with a workspace of
+    // any4_gemm_workspace_size bytes, that workspace being this GPU's scratch
+    const size_t need = any4_gemm_workspace_size(M, N, K, g);
+    if (need > SCRATCH_BYTES)
+        return ANY4_E_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0) {
+        const any4_status st = scratch_of_current_device(&ws);
+        if (st != ANY4_OK)
+            return st;
+    }
+    return gemm_call(FMT_ANY4, x, packed, lut, alpha, beta, y, M, N, K, g, stream, ws, need);
 }
 
 any4_status any4_gemm_int4(const uint16_t* x, const uint8_t* packed, const uint16_t* alpha,

@@ -171,6 +171,28 @@ any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* 
                       hipStream_t stream);
 
 /*
+ * any4_gemm_noalloc -- any4_gemm for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops that must not call the
+ * allocator, harnesses that forbid it): the same arguments without the
+ * workspace, the same kernels and the same result, bit for bit, as any4_gemm
+ * given a workspace of any4_gemm_workspace_size(M, N, K, g) bytes.  Where
+ * that size is not 0 (K split over workgroups), the partial sums go to a
+ * 4 MiB array of device memory inside the library, one per GPU, held until
+ * the process ends; its device address is looked up on the first such call
+ * on each GPU (with that GPU current: `stream` must belong to the current
+ * device).  Nothing is allocated per call and nothing needs clearing (every
+ * partial sum is written before it is read).  Calls on one GPU that use the
+ * array and can overlap in time (other streams, other threads) race on it:
+ * order them, e.g. on one stream.
+ * Errors: as any4_gemm; ANY4_E_WORKSPACE if the shape would need more than
+ * the array's 4 MiB (the splitting shapes need at most 1 MiB); ANY4_E_HIP if
+ * the array's address cannot be looked up.
+ */
+any4_status any4_gemm_noalloc(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
+                              const uint16_t* alpha, const uint16_t* beta, uint16_t* y,
+                              int64_t M, int64_t N, int64_t K, int64_t g, hipStream_t stream);
+
+/*
  * any4_gemm_int4 -- the same product for plain asymmetric int4 weights, the
  * baseline the explainer compares any4 against (section 二: int4 is the fixed
  * table 0..15, with the group scale and offset of step 1):
