@@ -246,6 +246,31 @@ def lowbit_layer(torch, any4, workloads, cfg: int, steps: int, bits: int = 2) ->
     return out
 
 
+def gemv_dot_layer(torch, any4, workloads, cfg: int, steps: int) -> dict:
+    """Per-launch µs at M = 1 of the vector-ALU product (any4_gemv_dot: the
+    same decode, v_dot2_f32_bf16 instead of the matrix cores) beside any4_gemm
+    on config `cfg`'s layer, graph replays over rotating weight sets."""
+    import numpy as np
+
+    c = workloads.CONFIGS[cfg]
+    dev, R, sets, x, ys = _setup(torch, any4, workloads, 0, cfg)
+    out = {"N": c.N, "K": c.K, "g": c.g, "M": 1, "rotating_weight_sets": R}
+    for name, fn in (("mfma_us", any4.gemm), ("vdot2_us", any4.gemv_dot)):
+        def launch(i: int, M: int, fn=fn):
+            p, l, a, b = sets[i % R]
+            fn(x[:1], p, l, a, b, c.g, out=ys[1])
+
+        for i in range(5):
+            launch(i, 1)
+        g = _graph(torch, launch, steps, (1,))
+        _time_graph(torch, g)
+        out[name] = float(np.median([_time_graph(torch, g) * 1e3 / steps for _ in range(3)]))
+        del g
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
 def decoder_layer(torch, any4, workloads, steps: int) -> dict:
     """The 70B decoder-layer shapes (q/k/v/o 8192x8192, up/gate 28672x8192,
     down 8192x28672, g = 128) at M = 1, 4, 16, graph-timed over rotating
@@ -609,6 +634,8 @@ def main() -> int:
                        for c in (2, 3)}
         out["any3"] = {f"config{c}": lowbit_layer(torch, any4, workloads, c, min(K, 100), 3)
                        for c in (2, 3)}
+        out["gemv_vdot2_vs_mfma"] = {f"config{c}": gemv_dot_layer(torch, any4, workloads, c,
+                                                                 min(K, 100)) for c in (2, 3)}
         out["prefill"] = prefill(torch, any4, workloads, (64, 256, 1024))
         out["decoder_layer_70b"] = decoder_layer(torch, any4, workloads, min(K, 50))
         out["quantize"] = quantize_timing(torch, any4, 4096, 4096, 128)

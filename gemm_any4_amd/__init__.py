@@ -39,7 +39,7 @@ _STATUS_NAMES = {0: "ANY4_OK", 1: "ANY4_E_NULL", 2: "ANY4_E_SHAPE", 3: "ANY4_E_A
 
 # every symbol include/any4.h declares
 EXPORTS = ("any4_packed_bytes", "any4_pack", "any4_dequant", "any4_gemm_workspace_size",
-           "any4_gemm", "any4_gemm_noalloc", "any4_gemm_int4", "any4_quantize", "any4_status_string",
+           "any4_gemm", "any4_gemm_noalloc", "any4_gemv_dot", "any4_gemm_int4", "any4_quantize", "any4_status_string",
            "any2_packed_bytes", "any2_pack", "any2_dequant", "any2_gemm",
            "any3_packed_bytes", "any3_pack", "any3_dequant", "any3_gemm", "any4_read_probe")
 
@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.any4_gemm.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P, SZ, P]
         L.any4_gemm_noalloc.restype = ctypes.c_int
         L.any4_gemm_noalloc.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
+        L.any4_gemv_dot.restype = ctypes.c_int
+        L.any4_gemv_dot.argtypes = [P, P, P, P, P, P, I64, I64, I64, P]
         L.any4_gemm_int4.restype = ctypes.c_int
         L.any4_gemm_int4.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
         L.any4_quantize.restype = ctypes.c_int
@@ -167,6 +169,33 @@ def gemm_noalloc_raw(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, 
                      stream=None) -> int:
     return lib().any4_gemm_noalloc(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M,
                                    N, K, g, _stream(stream))
+
+
+def gemv_dot_raw(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, N, K, g,
+                 stream=None) -> int:
+    return lib().any4_gemv_dot(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, N, K, g,
+                               _stream(stream))
+
+
+def gemv_dot(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor,
+             beta: torch.Tensor, g: int, out: torch.Tensor | None = None,
+             stream=None) -> torch.Tensor:
+    """y [1, N] = x [1, K] * W^T on the vector ALUs (v_dot2) instead of the
+    matrix cores: the same product as gemm at M = 1, for comparison."""
+    _b16(x, "x"), _b16(lut, "lut"), _b16(alpha, "alpha"), _b16(beta, "beta")
+    if x.dim() != 2 or x.shape[0] != 1:
+        raise ValueError("x must be [1, K]")
+    K = x.shape[1]
+    N = lut.shape[0]
+    if g <= 0 or K % g or alpha.shape != (N, K // g) or beta.shape != (N, K // g):
+        raise ValueError("alpha/beta must be [N, K/g]")
+    _check_packed(packed, N, K)
+    if out is None:
+        out = torch.empty((1, N), dtype=torch.bfloat16, device=x.device)
+    _b16(out, "y")
+    check(gemv_dot_raw(_ptr(x), _ptr(packed), _ptr(lut), _ptr(alpha), _ptr(beta), _ptr(out),
+                       N, K, g, stream))
+    return out
 
 
 def gemm_int4_raw(x_ptr, packed_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,

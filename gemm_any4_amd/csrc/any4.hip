@@ -1916,9 +1916,10 @@ struct StArgs {
     unsigned long long* ts;   // per-wave timestamps (probe builds only), or null
 };
 
-template <int MT, int NBG, int R, bool XL, bool MG, int LB, int PRE, int D, int FMT>
+template <int MT, int NBG, int R, bool XL, bool MG, int LB, int PRE, int D, int FMT, bool VD = false>
 __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
 {
+    static_assert(!VD || (MT == 1 && XL), "the VALU dot path is the M = 1 product with x in LDS");
     constexpr bool I4 = FMT == FMT_INT4;
     constexpr bool A2 = FMT == FMT_ANY2;
     constexpr bool A3 = FMT == FMT_ANY3;
@@ -2204,6 +2205,10 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
 #pragma unroll
     for (int b = 0; b < NBG; ++b)
         acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float dacc[VD ? NBG : 1];   // VD: the lane's partial dot product per block
+#pragma unroll
+    for (int b = 0; b < (VD ? NBG : 1); ++b)
+        dacc[b] = 0.f;
     int rsc[NBG];
     auto load_scales = [&]() {
 #pragma unroll
@@ -2272,9 +2277,21 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
                 for (int s4 = 0; s4 < 4; ++s4) {
                     const u32x4_t w = I4 ? deq_int4(p[s4], a, bt) : deq_quad(bw[s4], a, bt);
                     const u32x4_t& xa = XL ? xv[s4] : xq[XL ? 0 : s][s4];
-                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, xa), __builtin_bit_cast(bf16x8_t, w), acc[b], 0,
-                        0, 0);
+                    if constexpr (VD) {
+                        // v_dot2_f32_bf16: the lane's own two weights times its two x values
+                        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const uint32_t wt = w[t], xt = xa[t];
+                            dacc[b] = __builtin_amdgcn_fdot2_f32_bf16(
+                                __builtin_bit_cast(bf16x2_t, wt), __builtin_bit_cast(bf16x2_t, xt),
+                                dacc[b], false);
+                        }
+                    } else {
+                        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, xa), __builtin_bit_cast(bf16x8_t, w), acc[b],
+                            0, 0, 0);
+                    }
                 }
                 issue_next(k, u);
             }
@@ -2290,6 +2307,17 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
             constexpr int LQ = (MT + 3) / 4;
             constexpr int OUT = 16 * LQ * VC;   // outputs of a block
             float* redf = reinterpret_cast<float*>(smem);
+            if constexpr (VD) {
+                // the four lanes of a row (l, l+16, l+32, l+48) hold its four
+                // k quarters: add them, as the matrix core's output would be
+#pragma unroll
+                for (int b = 0; b < NBG; ++b) {
+                    float t = dacc[b] + __shfl_xor(dacc[b], 16);
+                    t += __shfl_xor(t, 32);
+                    acc[b] = f32x4_t{t, 0.f, 0.f, 0.f};
+                    dacc[b] = 0.f;
+                }
+            }
             __syncthreads();
             if (lane < 16 * LQ) {
 #pragma unroll
@@ -2589,6 +2617,35 @@ void st_go_r(const StArgs& sa, const StPlan& P, hipStream_t stream)
         st_go<MT, NBG, R, false, true, FMT>(sa, P, stream);
     else
         st_go<MT, NBG, R, false, false, FMT>(sa, P, stream);
+}
+
+// The M = 1 product with v_dot2_f32_bf16 instead of the matrix cores (same
+// decode, ring and staging); kept to compare the two.
+bool launch_st_dot(const GemmArgs& a, hipStream_t stream)
+{
+    StPlan P;
+    if (a.M != 1 || !st_plan(1, a.N, a.K, a.g, false, P) || !P.xl || P.mg)
+        return false;
+    StArgs sa{a, P.splits, P.gstage, P.cw, P.L, nullptr};
+    const dim3 gd(P.grid), bd(64 * P.nw);
+#define ST_DOT(NBG_, R_)                                                                          \
+    hipLaunchKernelGGL((k_gemm_st<1, NBG_, R_, true, false, 1024, ANY4_ST_PRE,                    \
+                                  (ANY4_ST_D < NBG_ * R_ ? ANY4_ST_D : NBG_ * R_), FMT_ANY4, true>), \
+                       gd, bd, 0, stream, sa)
+    switch (P.nbg * 16 + P.r) {
+    case 16 + 1: ST_DOT(1, 1); break;
+    case 16 + 2: ST_DOT(1, 2); break;
+    case 16 + 4: ST_DOT(1, 4); break;
+    case 16 + 8: ST_DOT(1, 8); break;
+    case 32 + 1: ST_DOT(2, 1); break;
+    case 32 + 2: ST_DOT(2, 2); break;
+    case 32 + 4: ST_DOT(2, 4); break;
+    case 64 + 1: ST_DOT(4, 1); break;
+    case 64 + 2: ST_DOT(4, 2); break;
+    default: return false;
+    }
+#undef ST_DOT
+    return true;
 }
 
 template <int MT, int FMT>
@@ -2938,6 +2995,39 @@ any4_status any4_gemm_noalloc(const uint16_t* x, const uint8_t* packed, const ui
             return st;
     }
     return gemm_call(FMT_ANY4, x, packed, lut, alpha, beta, y, M, N, K, g, stream, ws, need);
+}
+
+any4_status any4_gemv_dot(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
+                          const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t N,
+                          int64_t K, int64_t g, hipStream_t stream)
+{
+    if (N < 0 || !group_ok(K, g) || K == 0 || K / g > MAX_G)
+        return ANY4_E_SHAPE;
+    if (any4_packed_bytes(N, K) >= (static_cast<size_t>(1) << 31) ||
+        static_cast<size_t>(N) * 32 >= (static_cast<size_t>(1) << 31))
+        return ANY4_E_SHAPE;
+    if (N == 0)
+        return ANY4_OK;
+    if (!x || !packed || !lut || !alpha || !beta || !y)
+        return ANY4_E_NULL;
+    if (!aligned(y, 2) || !aligned(x, 16) || !aligned(packed, 16) || !aligned(lut, 16) ||
+        !aligned(alpha, 16) || !aligned(beta, 16))
+        return ANY4_E_ALIGN;
+    GemmArgs a{};
+    a.x = x;
+    a.packed = packed;
+    a.lut = lut;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.y = y;
+    a.M = 1;
+    a.N = static_cast<int>(N);
+    a.K = static_cast<int>(K);
+    a.g = static_cast<int>(g);
+    (void)hipGetLastError();
+    if (!launch_st_dot(a, stream))
+        return ANY4_E_SHAPE;   // x does not fit the kernel's LDS staging
+    return launched();
 }
 
 any4_status any4_gemm_int4(const uint16_t* x, const uint8_t* packed, const uint16_t* alpha,

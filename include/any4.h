@@ -193,6 +193,21 @@ any4_status any4_gemm_noalloc(const uint16_t* x, const uint8_t* packed, const ui
                               int64_t M, int64_t N, int64_t K, int64_t g, hipStream_t stream);
 
 /*
+ * any4_gemv_dot -- the M = 1 product (y = x * W^T with one row of x) computed
+ * on the vector ALUs with v_dot2_f32_bf16 instead of the matrix cores: the
+ * GEMV form of the decode-batch product (the explainer's section 三, batch
+ * 1), kept beside any4_gemm to compare the two; any4_gemm is the faster and
+ * is what any4_gemm uses at M = 1.  Same decode and dequantisation as
+ * any4_gemm (so the same exactness condition and bound), x [1][K], y [1][N].
+ * Shapes whose x does not fit the kernel's on-chip staging (2*K bytes above
+ * 64 KiB with the weights' tables) return ANY4_E_SHAPE.
+ * Errors: ANY4_E_SHAPE, ANY4_E_NULL, ANY4_E_ALIGN, ANY4_E_HIP.
+ */
+any4_status any4_gemv_dot(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
+                          const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t N,
+                          int64_t K, int64_t g, hipStream_t stream);
+
+/*
  * any4_gemm_int4 -- the same product for plain asymmetric int4 weights, the
  * baseline the explainer compares any4 against (section 二: int4 is the fixed
  * table 0..15, with the group scale and offset of step 1):

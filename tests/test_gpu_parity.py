@@ -588,3 +588,40 @@ def test_split_k_workspace_errors():
     assert any4.workspace_size(1, L.N, L.K, L.g) == 0       # M <= 2: never split
     assert any4.workspace_size(16, 14336, 4096, 128) == 0   # short K: never split
     assert any4.workspace_size(16, 8192, 8192, 128) == 0
+
+
+# --------------------------------------------------------------------------
+# the M = 1 product on the vector ALUs (v_dot2), kept for comparison
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_gemv_dot_configs(cfg):
+    L = gu.config_layer(cfg)
+    y = any4.gemv_dot(L.x[:1], L.packed, L.lut, L.alpha, L.beta, L.g)
+    torch.cuda.synchronize()
+    y_ref, ad = gu.config_ref(cfg, 1)
+    r = gu.assert_within_bound(y, y_ref, ad, f"gemv_dot config {cfg}")
+    print(f"gemv_dot config {cfg}: max err/tol = {r:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("N,K,g", [(17, 128, 128), (16 * 700 + 5, 256, 128), (100, 14336, 1024),
+                                   (16 * 300 + 9, 4096, 128), (40, 8192 + 128, 128)])
+def test_gemv_dot_ragged(N, K, g):
+    inp = workloads.generic(N * 7 + K, 1, N, K, g)
+    L = gu.Layer(inp)
+    y = any4.gemv_dot(L.x, L.packed, L.lut, L.alpha, L.beta, g)
+    torch.cuda.synchronize()
+    y_ref, ad = oracle.gemm(inp.x, L.w_ref())
+    gu.assert_within_bound(y, y_ref, ad, f"gemv_dot {N}x{K} g{g}")
+
+
+def test_gemv_dot_one_hot_returns_dequantised_columns():
+    inp = workloads.generic(35, 1, 16 * 300, 1024, 256)
+    L = gu.Layer(inp)
+    w_ref = L.w_ref()
+    one = workloads.to_bf16_bits(np.array([1.0]))[0]
+    for k in (0, 33, 511, 1023):
+        x = np.zeros((1, 1024), np.uint16)
+        x[0, k] = one
+        y = any4.gemv_dot(gu.dev_b16(x), L.packed, L.lut, L.alpha, L.beta, 256)
+        torch.cuda.synchronize()
+        assert np.array_equal(gu.host_b16(y)[0], w_ref[:, k]), k
