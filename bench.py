@@ -58,7 +58,7 @@ CACHE_BYTES = 256 * 1024 ** 2   # MI355X last-level cache (MALL)
 N_, K_, G_ = 14336, 4096, 128
 MS = (1, 16)
 KERNEL_SRC = os.path.join(ROOT, "gemm_any4_amd", "csrc", "any4.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_any4_gemm_14336x4096.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_any4_gemm_14336x4096.json")   # config 2
 COPY_BYTES = 256 * 1024 ** 2    # the calibration copy of --traffic-probe
 
 
@@ -417,20 +417,28 @@ def _time_graph(torch, g, reps: int = 1) -> float:
     return e0.elapsed_time(e1)
 
 
-def traffic_probe(torch, any4, workloads, sets_arg: int) -> int:
-    """A few launches of each M and one COPY_BYTES device copy (the scale for
-    the FETCH_SIZE / WRITE_SIZE counters)."""
-    dev, R, sets, x, ys = _setup(torch, any4, workloads, sets_arg)
+def traffic_file(cfg: int) -> str:
+    if cfg == 2:
+        return TRAFFIC_FILE
+    return os.path.join(ROOT, "profiles", "traffic_any4_gemm_4096x14336.json")
+
+
+def traffic_probe(torch, any4, workloads, sets_arg: int, cfg: int = 2) -> int:
+    """A few launches of each M on config `cfg`'s layer (each on its own
+    weight set) and one COPY_BYTES device copy (the scale for the FETCH_SIZE
+    / WRITE_SIZE counters)."""
+    c = workloads.CONFIGS[cfg]
+    dev, R, sets, x, ys = _setup(torch, any4, workloads, sets_arg, cfg)
     for n, M in launch_numbers(6, MS):
         p, l, a, b = sets[n % R]
-        any4.gemm(x[:M], p, l, a, b, G_, out=ys[M])
+        any4.gemm(x[:M], p, l, a, b, c.g, out=ys[M])
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
     src.fill_(1)
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"traffic_probe": True, "copy_bytes": COPY_BYTES,
-                      "launches_per_m": 6}), flush=True)
+    print(json.dumps({"traffic_probe": True, "layer": f"N={c.N} K={c.K} g={c.g}",
+                      "copy_bytes": COPY_BYTES, "launches_per_m": 6}), flush=True)
     return 0
 
 
@@ -448,12 +456,16 @@ def _counter_per_dispatch(path: str, counter: str) -> list:
     return [per[d] for d in sorted(per)]
 
 
-def traffic_summary(fetch_csv: str, write_csv: str) -> int:
-    """Write the committed traffic summary from the counter files of two
-    `--traffic-probe` runs (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE):
-    HBM bytes per launch of each M, each counter scaled by what it reads for
-    the COPY_BYTES device copy that ends the probe."""
+def traffic_summary(fetch_csv: str, write_csv: str, cfg: int = 2) -> int:
+    """Write the committed traffic summary of config `cfg`'s layer from the
+    counter files of two `--traffic-probe` runs (rocprofv3 --pmc FETCH_SIZE,
+    then WRITE_SIZE): HBM bytes per launch of each M, each counter scaled by
+    what it reads for the COPY_BYTES device copy that ends the probe.  A
+    launch that splits K is its GEMM kernel plus the k_split_sum after it;
+    the partial sums' bytes are given apart (they are not algorithmic)."""
     import re
+    import workloads
+    c = workloads.CONFIGS[cfg]
     fetch = _counter_per_dispatch(fetch_csv, "FETCH_SIZE")
     write = _counter_per_dispatch(write_csv, "WRITE_SIZE")
     for rows in (fetch, write):
@@ -465,27 +477,36 @@ def traffic_summary(fetch_csv: str, write_csv: str) -> int:
 
     def by_m(rows):
         out = {}
+        last = None
         for name, v in rows:
             m = pat.search(name)
             if m:
-                out.setdefault(int(m.group(2)), (m.group(1), []))[1].append(v)
+                last = int(m.group(2))
+                out.setdefault(last, {"kernel": m.group(1), "gemm": [], "split": []})["gemm"].append(v)
+            elif "k_split_sum" in name and last is not None:
+                out[last]["split"].append(v)
         return out
 
     f_m, w_m = by_m(fetch), by_m(write)
     per_m = {}
     for M in MS:
-        name, fv = f_m[M]
-        wv = w_m[M][1]
-        fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
+        fe, wr = f_m[M], w_m[M]
+        n = len(fe["gemm"])
+        fk, wk = sum(fe["gemm"]) / n, sum(wr["gemm"]) / n
         hbm = fk * 1024 * fscale + wk * 1024 * wscale
-        alg = algorithmic_bytes(M, N_, K_, G_)
-        per_m[str(M)] = {"kernel": name, "dispatches": len(fv), "fetch_kib_raw": round(fk, 2),
-                         "write_kib": round(wk, 2), "hbm_bytes_per_launch": round(hbm),
-                         "algorithmic_bytes": alg, "ratio": hbm / alg}
+        alg = algorithmic_bytes(M, c.N, c.K, c.g)
+        e = {"kernel": fe["kernel"], "dispatches": n, "fetch_kib_raw": round(fk, 2),
+             "write_kib": round(wk, 2), "hbm_bytes_per_launch": round(hbm),
+             "algorithmic_bytes": alg, "ratio": hbm / alg}
+        if fe["split"]:
+            sf = sum(fe["split"]) / len(fe["split"]) * 1024 * fscale
+            sw = sum(wr["split"]) / len(wr["split"]) * 1024 * wscale
+            e["k_split_sum_hbm_bytes"] = round(sf + sw)
+        per_m[str(M)] = e
     t = {"kernel_source_sha256_16": kernel_source_hash(),
-         "workload": f"N={N_} K={K_} g={G_}", "copy_bytes": COPY_BYTES,
+         "workload": f"N={c.N} K={c.K} g={c.g}", "copy_bytes": COPY_BYTES,
          "fetch_scale": fscale, "write_scale": wscale, "per_m": per_m}
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file(cfg), "w") as f:
         json.dump(t, f, indent=1)
         f.write("\n")
     print(json.dumps(t))
@@ -503,9 +524,12 @@ def main() -> int:
     ap.add_argument("--traffic-probe", action="store_true")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two --traffic-probe counter files")
+    ap.add_argument("--layer", type=int, default=2, choices=(2, 3),
+                    help="layer of --traffic-probe / --traffic-summary: config 2 (14336x4096) "
+                         "or 3 (4096x14336 g1024)")
     args = ap.parse_args()
     if args.traffic_summary:
-        return traffic_summary(*args.traffic_summary)
+        return traffic_summary(*args.traffic_summary, cfg=args.layer)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the any4 GEMM runs on a single MI355X; "
@@ -523,7 +547,7 @@ def main() -> int:
         return 2
     any4.lib()
     if args.traffic_probe:
-        return traffic_probe(torch, any4, workloads, args.sets)
+        return traffic_probe(torch, any4, workloads, args.sets, args.layer)
 
     dev, R, sets, x, ys = _setup(torch, any4, workloads, args.sets)
     wb = weight_bytes(N_, K_, G_)
@@ -621,24 +645,36 @@ def main() -> int:
                                "rotating sets: the streaming-read ceiling of one launch"},
         "host_wall_s": wall,
     }
+    def progress(what):
+        print(f"[bench] {what} done", file=sys.stderr, flush=True)
+
+    progress("headline layer")
     if not args.no_other_layers:
         del g_all, g_m, sets
         torch.cuda.empty_cache()
         out["other_layers"] = {"config3": other_layer(torch, any4, workloads, 3, min(K, 100))}
+        progress("other layer")
         # the same layers as plain int4 (no table lookup): the cost of the table
         out["int4_no_table"] = {f"config{c}": other_layer(torch, any4, workloads, c,
                                                           min(K, 100), int4=True)
                                 for c in (2, 3)}
+        progress("int4")
     if not args.no_other_layers:
         out["any2"] = {f"config{c}": lowbit_layer(torch, any4, workloads, c, min(K, 100), 2)
                        for c in (2, 3)}
+        progress("any2")
         out["any3"] = {f"config{c}": lowbit_layer(torch, any4, workloads, c, min(K, 100), 3)
                        for c in (2, 3)}
+        progress("any3")
         out["gemv_vdot2_vs_mfma"] = {f"config{c}": gemv_dot_layer(torch, any4, workloads, c,
                                                                  min(K, 100)) for c in (2, 3)}
+        progress("gemv")
         out["prefill"] = prefill(torch, any4, workloads, (64, 256, 1024))
+        progress("prefill")
         out["decoder_layer_70b"] = decoder_layer(torch, any4, workloads, min(K, 50))
+        progress("70B decoder layer")
         out["quantize"] = quantize_timing(torch, any4, 4096, 4096, 128)
+        progress("quantiser")
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -2597,8 +2597,8 @@ void st_go(const StArgs& sa, const StPlan& P, hipStream_t stream)
     constexpr int TB = NBG * R;
     constexpr int DD = ANY4_ST_D < TB ? ANY4_ST_D : TB;
     constexpr int D = (XL || TB - DD >= NBG - 1) ? DD : 1;
-    hipLaunchKernelGGL((k_gemm_st<MT, NBG, R, XL, MG, LB, ANY4_ST_PRE, D, FMT>), dim3(P.grid), dim3(64 * P.nw),
-                       0, stream, sa);
+    hipLaunchKernelGGL((k_gemm_st<MT, NBG, R, XL, MG, LB, ANY4_ST_PRE, D, FMT>), dim3(P.grid),
+                       dim3(64 * P.nw), 0, stream, sa);
 }
 
 template <int MT, int NBG, int R, int FMT>

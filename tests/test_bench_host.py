@@ -113,3 +113,30 @@ def test_no_weight_set_is_read_twice_within_the_rotation(Ms):
         assert len(set(window)) == len(window), (i, window)
     # every M of a step is recorded, in order
     assert [M for _, M in bench.launch_numbers(2, Ms)] == list(Ms) * 2
+
+
+def test_traffic_summary_counts_the_split_sum_apart(tmp_path, monkeypatch):
+    """A launch that splits K is its GEMM kernel and the k_split_sum after it:
+    the GEMM's bytes are the launch's HBM traffic, the partial sums' apart."""
+    out = tmp_path / "t3.json"
+    monkeypatch.setattr(bench, "traffic_file", lambda cfg: str(out))
+    copy_kib = bench.COPY_BYTES / 1024
+    rows_f, rows_w = [], []
+    for i in range(6):
+        for M in bench.MS:
+            name = f"void (anonymous namespace)::k_gemm_st<{M}, 4, 2, false, false, 1024, 0, 2, 0>(StArgs)"
+            rows_f.append((name, [100.0 * M]))
+            rows_w.append((name, [2.0]))
+            if M > 2:
+                rows_f.append(("void (anonymous namespace)::k_split_sum(float const*, unsigned short*, int, unsigned long)", [8.0]))
+                rows_w.append(("void (anonymous namespace)::k_split_sum(float const*, unsigned short*, int, unsigned long)", [4.0]))
+    rows_f.append(("__amd_rocclr_copyBuffer", [copy_kib / 2]))
+    rows_w.append(("__amd_rocclr_copyBuffer", [copy_kib]))
+    _write_csv(tmp_path / "f.csv", "FETCH_SIZE", rows_f)
+    _write_csv(tmp_path / "w.csv", "WRITE_SIZE", rows_w)
+    assert bench.traffic_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), cfg=3) == 0
+    t = json.loads(out.read_text())
+    assert t["workload"] == "N=4096 K=14336 g=1024"
+    assert t["per_m"]["16"]["hbm_bytes_per_launch"] == round(1600 * 1024 * 2 + 2 * 1024)
+    assert t["per_m"]["16"]["k_split_sum_hbm_bytes"] == round(8 * 1024 * 2 + 4 * 1024)
+    assert "k_split_sum_hbm_bytes" not in t["per_m"]["1"]
