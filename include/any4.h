@@ -331,10 +331,11 @@ any4_status any4_quantize(const float* W, const float* ex, uint8_t* idx, uint16_
 /*
  * any4_read_probe -- a measurement aid, not part of the method: reads `bytes`
  * of device memory at `buf` once, with the GEMM kernels' loads (16 bytes per
- * lane, 1 KB per wave, non-temporal, 16 loads in flight per wave, one
- * workgroup of 8 waves per CU), and writes at most one word to `out`.  Its
- * duration is the streaming-read ceiling that the GEMM's bandwidth is
- * compared with.  bytes: a multiple of 1024, below 2 GiB (0: no-op).
+ * lane, 1 KB per wave, non-temporal), one workgroup of 16 waves per CU, each
+ * wave issuing its ceil(bytes / 4 MiB) loads (at most 16 at a time) at once,
+ * and writes at most one word to `out`.  Its duration is the streaming-read
+ * ceiling that the GEMM's bandwidth is compared with.  bytes: a multiple of
+ * 1024, below 2 GiB (0: no-op).
  * Errors: ANY4_E_SHAPE, ANY4_E_NULL, ANY4_E_ALIGN (buf not 16-byte or out
  * not 4-byte aligned), ANY4_E_HIP.
  */
