@@ -24,12 +24,18 @@
 //   k_pack, k_pack2, k_pack3        idx[N][K] u8 -> tiles, one tile slot per thread.
 //   k_dequant, k_dequant2, k_dequant3  w = bf16(fma(alpha, LUT[idx], beta)), one slot
 //                          per thread.
-//   k_gemm_km, k_gemm_kb   y = x * W^T for M <= 16 (K <= 4096 / any K): the
-//                          weights stream once, decoded through table lookups
-//                          in LDS into v_mfma_f32_16x16x32_bf16 operands; see
-//                          the comments above the kernels.
+//   k_gemm_st              y = x * W^T for M <= 16 with one to four row blocks
+//                          per CU: the weights stream once, decoded through
+//                          table lookups in LDS into v_mfma_f32_16x16x32_bf16
+//                          operands; K optionally split over workgroups.
+//   k_split_sum            y from the split partial sums, in split order.
+//   k_gemm_km, k_gemm_kb   the same decode for the other M <= 16 shapes (one
+//                          block per CU with K <= 4096, more than four).
 //   k_gemm_big             M > 48: tiles dequantised into LDS, then MFMAs.
-//   k_quantize             group scale + weighted k-means, one thread per row.
+//   k_quantize_w           group scale + weighted k-means, one wave per row
+//                          (k_quantize, one thread per row, for rows of more
+//                          than 1024 groups).
+//   k_read_probe           a streaming read (measurement only).
 //   k_zero                 y = 0 when K = 0.
 #include <hip/hip_runtime.h>
 
@@ -1820,6 +1826,139 @@ __global__ __launch_bounds__(QT) void k_quantize(const float* __restrict__ W,
     }
 }
 
+// ---- k_quantize_w: the same quantiser, one wave per row ---------------------
+// k_quantize's steps and roundings, spread over a wave's 64 lanes so that a
+// layer's rows fill the chip (one thread per row leaves most CUs idle):
+//   1. group scale: lane l folds groups l, l+64, ... exactly as k_quantize
+//      (min and max in increasing k) and keeps the row's alpha | beta << 16
+//      in LDS;
+//   2-3. each k-means round walks the row in chunks of 64 consecutive k, one
+//      per lane: every lane forms its weight's ws, wt = alpha * ex[k], its
+//      nearest table value q and wt * ws (the E-step, in parallel) and leaves
+//      (wt * ws, wt) in LDS; then lane q adds the chunk's members of cluster q
+//      (a ballot per cluster names them) to its two sums in increasing k, so
+//      each cluster's sums are rounded in k_quantize's order.  L[q] = sum /
+//      weight for the non-empty clusters, broadcast from lane q;
+//   4. the stored table, and the final assignment one weight per lane.
+// A wave touches only its own LDS, so there is no barrier; rows with more
+// than QW_MAX_G groups (not enough LDS for their alpha/beta) use k_quantize.
+constexpr int QW_WAVES = 4;
+constexpr int QW_MAX_G = 1024;
+
+__global__ __launch_bounds__(64 * QW_WAVES) void k_quantize_w(const float* __restrict__ W,
+                                                              const float* __restrict__ ex,
+                                                              uint8_t* __restrict__ idx,
+                                                              uint16_t* __restrict__ lut,
+                                                              uint16_t* __restrict__ alpha,
+                                                              uint16_t* __restrict__ beta, int N,
+                                                              int K, int g, int iters, int Q)
+{
+    __shared__ uint32_t ab_s[QW_WAVES][QW_MAX_G];   // alpha | beta << 16 per group
+    __shared__ double pw_s[QW_WAVES][2][64];        // a chunk's (wt * ws, wt) per lane
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int n = blockIdx.x * QW_WAVES + wv;
+    if (n >= N)
+        return;   // whole waves: nothing below waits for another wave
+    const int G = K / g;
+    const float* row = W + static_cast<size_t>(n) * K;
+    uint32_t* ab = ab_s[wv];
+    double* pw0 = pw_s[wv][0];
+    double* pw1 = pw_s[wv][1];
+
+    for (int j = lane; j < G; j += 64) {   // 1. group scale
+        double lo = row[j * g], hi = lo;
+        for (int k = j * g + 1; k < (j + 1) * g; ++k) {
+            const double v = row[k];
+            lo = v < lo ? v : lo;
+            hi = v > hi ? v : hi;
+        }
+        const uint32_t b = f64_to_bf16(lo);
+        const uint32_t a = f64_to_bf16((hi - lo) / static_cast<double>(Q - 1));
+        beta[static_cast<size_t>(n) * G + j] = static_cast<uint16_t>(b);
+        alpha[static_cast<size_t>(n) * G + j] = static_cast<uint16_t>(a);
+        ab[j] = a | (b << 16);
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // ws and wt of weight k (its group's alpha and beta from LDS)
+    auto weight = [&](int k, double& ws, double& al) {
+        const uint32_t p = ab[k / g];
+        al = bf16_to_f64(p & 0xFFFFu);
+        const double be = bf16_to_f64(p >> 16);
+        ws = al != 0.0 ? (static_cast<double>(row[k]) - be) / al : 0.0;
+    };
+
+    double L[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        L[q] = q < Q ? q : 0;
+    const int nch = (K + 63) / 64;
+    for (int it = 0; it < iters; ++it) {   // 3. weighted k-means
+        double S = 0.0, T = 0.0;           // lane q: the sums of cluster q
+        for (int c = 0; c < nch; ++c) {
+            const int k = c * 64 + lane;
+            int q = 16;   // no cluster: a lane past K
+            double pr = 0.0, wt = 0.0;
+            if (k < K) {
+                double ws, al;
+                weight(k, ws, al);
+                wt = __dmul_rn(al, static_cast<double>(ex[k]));
+                q = nearest_q(ws, L, Q);
+                pr = __dmul_rn(wt, ws);
+            }
+            pw0[lane] = pr;
+            pw1[lane] = wt;
+            uint64_t mine = 0;   // lane q: the lanes of the chunk in cluster q
+#pragma unroll
+            for (int qq = 0; qq < 16; ++qq) {
+                if (qq < Q) {
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(q == qq);
+                    mine = lane == qq ? m : mine;
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            while (mine) {   // in increasing k
+                const int i = __builtin_ctzll(mine);
+                mine &= mine - 1;
+                S = __dadd_rn(S, pw0[i]);
+                T = __dadd_rn(T, pw1[i]);
+            }
+            __builtin_amdgcn_wave_barrier();   // reads done before the next chunk's writes
+        }
+        const bool upd = lane < Q && T > 0.0;
+        const double cand = upd ? S / T : 0.0;
+        const uint64_t um = __builtin_amdgcn_ballot_w64(upd);
+        const uint64_t cb = __builtin_bit_cast(uint64_t, cand);
+        const uint32_t clo = static_cast<uint32_t>(cb), chi = static_cast<uint32_t>(cb >> 32);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            if ((um >> q) & 1u) {
+                // readlane returns int: widen through uint32_t, not with sign
+                const uint32_t vlo = static_cast<uint32_t>(__builtin_amdgcn_readlane(clo, q));
+                const uint32_t vhi = static_cast<uint32_t>(__builtin_amdgcn_readlane(chi, q));
+                const uint64_t v = static_cast<uint64_t>(vlo) | (static_cast<uint64_t>(vhi) << 32);
+                L[q] = __builtin_bit_cast(double, v);
+            }
+        }
+    }
+
+    double Lq[16];   // 4. the stored table and the final assignment
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const uint32_t h = q < Q ? f64_to_bf16(L[q]) : 0u;
+        if (lane == q)
+            lut[static_cast<size_t>(n) * 16 + q] = static_cast<uint16_t>(h);
+        Lq[q] = bf16_to_f64(h);
+    }
+    uint8_t* in = idx + static_cast<size_t>(n) * K;
+    for (int k = lane; k < K; k += 64) {
+        double ws, al;
+        weight(k, ws, al);
+        in[k] = static_cast<uint8_t>(nearest_q(ws, Lq, Q));
+    }
+}
+
 // ---- k_read_probe: the streaming-read ceiling --------------------------------
 // Reads a buffer once with the GEMM's loads (16 bytes per lane, non-temporal,
 // a wave's 64 lanes on 1 KB contiguous) and writes one word (so the loads are
@@ -3146,9 +3285,15 @@ any4_status any4_quantize(const float* W, const float* ex, uint8_t* idx, uint16_
         !aligned(beta, 2))
         return ANY4_E_ALIGN;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(k_quantize, dim3(static_cast<unsigned>((N + QT - 1) / QT)), dim3(QT), 0,
-                       stream, W, ex, idx, lut, alpha, beta, static_cast<int>(N),
-                       static_cast<int>(K), static_cast<int>(g), iters, 1 << bits);
+    if (K / g <= QW_MAX_G)
+        hipLaunchKernelGGL(k_quantize_w, dim3(static_cast<unsigned>((N + QW_WAVES - 1) / QW_WAVES)),
+                           dim3(64 * QW_WAVES), 0, stream, W, ex, idx, lut, alpha, beta,
+                           static_cast<int>(N), static_cast<int>(K), static_cast<int>(g), iters,
+                           1 << bits);
+    else
+        hipLaunchKernelGGL(k_quantize, dim3(static_cast<unsigned>((N + QT - 1) / QT)), dim3(QT), 0,
+                           stream, W, ex, idx, lut, alpha, beta, static_cast<int>(N),
+                           static_cast<int>(K), static_cast<int>(g), iters, 1 << bits);
     return launched();
 }
 

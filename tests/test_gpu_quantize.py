@@ -52,6 +52,19 @@ def test_quantize_matches_oracle(N, K, g, iters):
     _check(got, ref, f"{N}x{K} g{g} iters{iters}")
 
 
+@pytest.mark.parametrize("N,K,g,iters", [(9, 96, 32, 4), (6, 200, 8, 3), (4, 330, 11, 3),
+                                         (5, 2048, 1, 2)])
+def test_quantize_odd_shapes(N, K, g, iters):
+    """K not a multiple of 64 (a ragged last chunk of the wave-per-row
+    kernel), groups shorter than a chunk or not dividing 64, and K/g above the
+    wave kernel's LDS share (2048 groups: the thread-per-row kernel)."""
+    rng = np.random.default_rng(N * 31 + K + g)
+    W = rng.normal(0.0, 0.02, size=(N, K))
+    ex = rng.lognormal(0.0, 1.0, size=K)
+    got, ref = _quantize_both(W.astype(np.float32), ex.astype(np.float32), g, iters)
+    _check(got, ref, f"{N}x{K} g{g} iters{iters}")
+
+
 def test_quantize_degenerate_groups():
     """Constant groups (alpha = 0: every normalised weight is 0), a zero row,
     and zero importance on some channels."""
