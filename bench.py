@@ -26,8 +26,9 @@ layer shape, the MLP down projection N=4096, K=14336, g=1024, at M=1 and
 M=16, under "other_layers"; and for both layers with plain int4 weights
 (any4_gemm_int4 on the same codes, scales and offsets, no table), under
 "int4_no_table", which puts a number on what the table lookup costs; and
-at prefill batches M = 64, 256, 1024 on the up/gate layer (TFLOP/s against
-the bf16 matrix peak), under "prefill"; both layers with the codes taken to
+at M = 24, 32, 48 on the up/gate layer (one launch against 16-row slices),
+under "wide_batch"; at prefill batches M = 64, 256, 1024 on the up/gate layer
+(TFLOP/s against the bf16 matrix peak), under "prefill"; both layers with the codes taken to
 2 bits through any2_gemm and to 3 bits through any3_gemm, under "any2" and
 "any3"; the 70B decoder-layer shapes and their
 layer total, under "decoder_layer_70b"; and the GPU quantiser on a 4096x4096
@@ -358,9 +359,54 @@ def prefill(torch, any4, workloads, Ms) -> dict:
     return out
 
 
+def wide_batch(torch, any4, workloads, Ms) -> dict:
+    """µs and TB/s of any4_gemm at M = 17..48 on the up/gate layer, where one
+    launch runs the streaming kernel with two or three 16-row slices of x
+    against each decoded weight tile, beside the same product as 16-row slices
+    (one launch per slice, each re-reading the weights); graph-timed over
+    rotating weight sets."""
+    import numpy as np
+
+    c = workloads.CONFIGS[2]
+    dev, R, sets, x, ys = _setup(torch, any4, workloads, 0, 2)
+    out = {"N": c.N, "K": c.K, "g": c.g}
+    gen = torch.Generator(device="cpu").manual_seed(8)
+    for M in Ms:
+        xb = torch.randn(M, c.K, generator=gen).to(torch.bfloat16).to(dev)
+        yb = torch.empty(M, c.N, device=dev, dtype=torch.bfloat16)
+
+        def one_pass(i: int, M: int):
+            p, l, a, b = sets[i % R]
+            any4.gemm(xb, p, l, a, b, c.g, out=yb)
+
+        def slices(i: int, M: int):
+            p, l, a, b = sets[i % R]
+            for m0 in range(0, M, 16):
+                any4.gemm(xb[m0:m0 + 16], p, l, a, b, c.g, out=yb[m0:m0 + 16])
+
+        res = {}
+        for name, fn in (("one_pass", one_pass), ("slices", slices)):
+            for i in range(3):
+                fn(i, M)
+            steps = 20
+            g = _graph(torch, fn, steps, (M,))
+            _time_graph(torch, g)
+            us = float(np.median([_time_graph(torch, g) * 1e3 / steps for _ in range(3)]))
+            res[name + "_us"] = us
+            del g
+        byt = algorithmic_bytes(M, c.N, c.K, c.g)
+        res["bytes"] = byt
+        res["tbps"] = byt / (res["one_pass_us"] * 1e-6) / 1e12
+        res["pct_hbm_peak"] = 100.0 * res["tbps"] * 1e3 / HBM_PEAK_GBS
+        out[str(M)] = res
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
 def quantize_timing(torch, any4, N: int, K: int, g: int, iters: int = 10) -> dict:
     """ms of any4_quantize (group scale + 10 rounds of weighted k-means, one
-    GPU thread per row) on an N x K layer, for 4, 3 and 2 bits."""
+    GPU wave per row) on an N x K layer, for 4, 3 and 2 bits."""
     gen = torch.Generator(device="cpu").manual_seed(11)
     dev = torch.device("cuda:0")
     W = (torch.randn(N, K, generator=gen) * 0.02).to(dev)
@@ -669,6 +715,8 @@ def main() -> int:
         out["gemv_vdot2_vs_mfma"] = {f"config{c}": gemv_dot_layer(torch, any4, workloads, c,
                                                                  min(K, 100)) for c in (2, 3)}
         progress("gemv")
+        out["wide_batch"] = wide_batch(torch, any4, workloads, (24, 32, 48))
+        progress("wide batch")
         out["prefill"] = prefill(torch, any4, workloads, (64, 256, 1024))
         progress("prefill")
         out["decoder_layer_70b"] = decoder_layer(torch, any4, workloads, min(K, 50))

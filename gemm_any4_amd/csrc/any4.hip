@@ -1512,16 +1512,18 @@ constexpr int BIG_BN = 64;
 constexpr int BIG_LD = TILE_K + 8;   // padded row length in bf16
 constexpr int BIG_PF = 2;            // chunks of global data in flight per thread
 
-template <int BM, int FMT>
+template <int BM, int FMT, int BN = BIG_BN>
 __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
 {
     constexpr bool A2 = FMT == FMT_ANY2;
     constexpr bool A3 = FMT == FMT_ANY3;
     constexpr uint32_t TB = tile_bytes(FMT);
     constexpr int MTW = BM / 32;   // 16-row m tiles per wave (the wave's BM/2 rows)
+    constexpr int NTW = BN / 32;   // 16-row n tiles per wave (the wave's BN/2 rows)
+    constexpr int SL = BN / 64;    // dequantisation slots per thread per chunk
     __shared__ __attribute__((aligned(16))) uint16_t xs[BM * BIG_LD];
-    __shared__ __attribute__((aligned(16))) uint16_t ws[BIG_BN * BIG_LD];
-    __shared__ float lt[BIG_BN * 16];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[BN * BIG_LD];
+    __shared__ float lt[BN * 16];
 
     const int M = args.M, N = args.N, K = args.K, g = args.g;
     const int tid = threadIdx.x;
@@ -1529,32 +1531,40 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
     const int wave = tid >> 6;
     const int Kc = K / TILE_K;
     const int G = K / g;
-    const int n0 = blockIdx.x * BIG_BN;
+    const int n0 = blockIdx.x * BN;
     const int m0 = blockIdx.y * BM;
 
     // table rows of the 64 weight rows (rows >= N: zeros); no table (plain
     // int4): the codes themselves, 0..15
-    for (int e = tid; e < BIG_BN * 16; e += 256) {
+    for (int e = tid; e < BN * 16; e += 256) {
         const int n = n0 + e / 16;
         lt[e] = n >= N      ? 0.f
                 : args.lut ? bf16_to_f32(args.lut[static_cast<size_t>(n) * 16 + (e & 15)])
                            : static_cast<float>(e & 15);
     }
 
-    // this thread's dequantisation slot
-    const int tb = tid >> 6;                 // row block within the workgroup
-    const int wrow = tb * 16 + (lane & 15);  // row within the 64
-    const int wn = n0 + wrow;
+    // this thread's dequantisation slots: row block wave + 4*sl of the
+    // workgroup's BN/16, the lane's slot of its tile
+    int wrow[SL], wn[SL], blk[SL];
+    bool wlive[SL];
+#pragma unroll
+    for (int sl = 0; sl < SL; ++sl) {
+        const int tb = (tid >> 6) + 4 * sl;  // row block within the workgroup
+        wrow[sl] = tb * 16 + (lane & 15);    // row within the BN
+        wn[sl] = n0 + wrow[sl];
+        blk[sl] = (n0 >> 4) + tb;            // global row block
+        wlive[sl] = wn[sl] < N;
+    }
     const int wk = (lane >> 4) * 32;         // k offset within the chunk
-    const int blk = (n0 >> 4) + tb;          // global row block
-    const bool wlive = wn < N;
 
-    f32x4_t acc[MTW][2];
+    f32x4_t acc[MTW][NTW];
 #pragma unroll
     for (int a = 0; a < MTW; ++a)
-        acc[a][0] = acc[a][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < NTW; ++b)
+            acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int wm = (wave >> 1) * (BM / 2);   // the wave's rows within BM
-    const int wc = (wave & 1) * 32;          // ... and columns within the 64
+    const int wc = (wave & 1) * (BN / 2);    // ... and columns within the BN
     const int j = lane & 15;
     const int kq = lane >> 4;
 
@@ -1570,29 +1580,33 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(args.alpha, static_cast<uint32_t>(N) * G * 2);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(args.beta, static_cast<uint32_t>(N) * G * 2);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(args.x, static_cast<uint32_t>(M) * K * 2);
-    u32x4_t pk[PF];
-    uint32_t ab[PF];
+    u32x4_t pk[PF][SL];
+    uint32_t ab[PF][SL];
     u32x4_t xv[PF][XP];
     auto fetch = [&](int c, int sl) {
-        const uint32_t dead = static_cast<uint32_t>(!wlive || c >= Kc) << 31;
-        const uint32_t po =
-            ((static_cast<uint32_t>(blk) * Kc + c) * TB + lane * (TB / 64)) | dead;
-        if constexpr (A2) {
-            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-            const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rp, po, 0, 0);
-            pk[sl] = u32x4_t{v[0], v[1], 0u, 0u};
-        } else if constexpr (A3) {
-            typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
-            const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(rp, po, 0, 0);
-            pk[sl] = u32x4_t{v[0], v[1], v[2], 0u};
-        } else {
-            pk[sl] = load16(rp, po);
+#pragma unroll
+        for (int q = 0; q < SL; ++q) {
+            const uint32_t dead = static_cast<uint32_t>(!wlive[q] || c >= Kc) << 31;
+            const uint32_t po =
+                ((static_cast<uint32_t>(blk[q]) * Kc + c) * TB + lane * (TB / 64)) | dead;
+            if constexpr (A2) {
+                typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+                const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rp, po, 0, 0);
+                pk[sl][q] = u32x4_t{v[0], v[1], 0u, 0u};
+            } else if constexpr (A3) {
+                typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+                const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(rp, po, 0, 0);
+                pk[sl][q] = u32x4_t{v[0], v[1], v[2], 0u};
+            } else {
+                pk[sl][q] = load16(rp, po);
+            }
+            const uint32_t ao = ((static_cast<uint32_t>(wn[q]) * G +
+                                  static_cast<uint32_t>(c * TILE_K + wk) / g) * 2) |
+                                dead;
+            ab[sl][q] =
+                static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(ra, ao, 0, 0)) |
+                (static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rb, ao, 0, 0)) << 16);
         }
-        const uint32_t ao =
-            ((static_cast<uint32_t>(wn) * G + static_cast<uint32_t>(c * TILE_K + wk) / g) * 2) |
-            dead;
-        ab[sl] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(ra, ao, 0, 0)) |
-                 (static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rb, ao, 0, 0)) << 16);
 #pragma unroll
         for (int i = 0; i < XP; ++i) {
             const int piece = tid + i * 256;
@@ -1611,14 +1625,15 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
         for (int sl = 0; sl < PF; ++sl) {
             const int c = c0 + sl;   // chunks past K (the last round) add zeros
             __syncthreads();   // the previous chunk's tiles are consumed (and lt is written)
-            // weights: 32 per thread, exactly the any4_dequant values
-            {
+            // weights: 32 per slot, exactly the any4_dequant values
+#pragma unroll
+            for (int q = 0; q < SL; ++q) {
                 u32x4_t out[4] = {};
-                if (wlive && c < Kc) {
-                    const float a = bf16_to_f32(ab[sl] & 0xFFFFu);
-                    const float bt = bf16_to_f32(ab[sl] >> 16);
-                    const float* L = lt + wrow * 16;
-                    const u32x4_t p = pk[sl];
+                if (wlive[q] && c < Kc) {
+                    const float a = bf16_to_f32(ab[sl][q] & 0xFFFFu);
+                    const float bt = bf16_to_f32(ab[sl][q] >> 16);
+                    const float* L = lt + wrow[q] * 16;
+                    const u32x4_t p = pk[sl][q];
                     if constexpr (A2) {   // 8 bytes of four 2-bit codes: dwords 2i, 2i+1
 #pragma unroll
                         for (int i = 0; i < 8; ++i) {
@@ -1651,7 +1666,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
                         }
                     }
                 }
-                u32x4_t* dst = reinterpret_cast<u32x4_t*>(ws + wrow * BIG_LD + wk);
+                u32x4_t* dst = reinterpret_cast<u32x4_t*>(ws + wrow[q] * BIG_LD + wk);
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     dst[q] = out[q];
@@ -1668,16 +1683,16 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
 #pragma unroll
             for (int ks = 0; ks < TILE_K / 32; ++ks) {
                 const int k = ks * 32 + kq * 8;
-                u32x4_t bf[2];
+                u32x4_t bf[NTW];
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
+                for (int nt = 0; nt < NTW; ++nt)
                     bf[nt] = *reinterpret_cast<const u32x4_t*>(ws + (wc + nt * 16 + j) * BIG_LD + k);
 #pragma unroll
                 for (int mt = 0; mt < MTW; ++mt) {
                     const u32x4_t af =
                         *reinterpret_cast<const u32x4_t*>(xs + (wm + mt * 16 + j) * BIG_LD + k);
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
+                    for (int nt = 0; nt < NTW; ++nt)
                         acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             __builtin_bit_cast(bf16x8_t, af), __builtin_bit_cast(bf16x8_t, bf[nt]),
                             acc[mt][nt], 0, 0, 0);
@@ -1689,7 +1704,7 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int m = m0 + wm + mt * 16 + kq * 4 + v;
@@ -2065,6 +2080,11 @@ template <int MT, int NBG, int R, bool XL, bool MG, int LB, int PRE, int D, int 
 __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
 {
     static_assert(!VD || (MT == 1 && XL), "the VALU dot path is the M = 1 product with x in LDS");
+    static_assert(MT <= 16 || (MT % 16 == 0 && !XL && !VD), "wide batches: 16-row slices of x in the ring");
+    // M > 16: MS slices of 16 x rows, each with its own MFMA chains against the
+    // same decoded weights, so the weights are read once for all of them
+    constexpr int MS = MT > 16 ? MT / 16 : 1;
+    constexpr int MTS = MT > 16 ? 16 : MT;   // rows per slice
     constexpr bool I4 = FMT == FMT_INT4;
     constexpr bool A2 = FMT == FMT_ANY2;
     constexpr bool A3 = FMT == FMT_ANY3;
@@ -2253,9 +2273,12 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
     // of block (k / bpg)*NBG + u % NBG; it sits in ring slot u % D (D divides
     // a body).  x (XSTREAM): a step's operands are loaded with its first tile.
     u32x4_t pb[D];
-    u32x4_t xq[XSTREAM ? R : 1][4];
+    u32x4_t xq[XSTREAM ? R : 1][MS][4];
     const uint32_t tile_lane = static_cast<uint32_t>(lane) * (TB / 64);
-    const uint32_t x_lane = j < M ? static_cast<uint32_t>(j * K + kq * 32) * 2 : OOR;
+    uint32_t x_lane[MS];   // x row j + 16*ms of the lane's k quarter, or out of range
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+        x_lane[ms] = j + 16 * ms < M ? static_cast<uint32_t>((j + 16 * ms) * K + kq * 32) * 2 : OOR;
     auto issue = [&](int k, int u) {
         const int gi = k / bpg;
         const int s = (k - gi * bpg) * R + u / NBG;
@@ -2272,8 +2295,10 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
                 const bool xl = gi < ngroups && c < kend;
                 const uint32_t xc = static_cast<uint32_t>(c) * TILE_K * 2 | (static_cast<uint32_t>(!xl) << 31);
 #pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4)
-                    xq[u / NBG][s4] = load16(rx, off2(x_lane, xc) + s4 * 16);
+                for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4)
+                        xq[u / NBG][ms][s4] = load16(rx, off2(x_lane[ms], xc) + s4 * 16);
             }
         }
     };
@@ -2346,10 +2371,12 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
 
     // the lane's slot in a table entry (any2: 16 slots of 8 bytes)
     const uint32_t slot4 = A2 ? static_cast<uint32_t>(lane & 15) * 8 : static_cast<uint32_t>(lane & 31) * 4;
-    f32x4_t acc[NBG];
+    f32x4_t acc[NBG][MS];
 #pragma unroll
     for (int b = 0; b < NBG; ++b)
-        acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+            acc[b][ms] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float dacc[VD ? NBG : 1];   // VD: the lane's partial dot product per block
 #pragma unroll
     for (int b = 0; b < (VD ? NBG : 1); ++b)
@@ -2421,7 +2448,7 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4) {
                     const u32x4_t w = I4 ? deq_int4(p[s4], a, bt) : deq_quad(bw[s4], a, bt);
-                    const u32x4_t& xa = XL ? xv[s4] : xq[XL ? 0 : s][s4];
+                    const u32x4_t& xa = XL ? xv[s4] : xq[XL ? 0 : s][0][s4];
                     if constexpr (VD) {
                         // v_dot2_f32_bf16: the lane's own two weights times its two x values
                         typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -2433,9 +2460,14 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
                                 dacc[b], false);
                         }
                     } else {
-                        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, xa), __builtin_bit_cast(bf16x8_t, w), acc[b],
-                            0, 0, 0);
+                        acc[b][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, xa), __builtin_bit_cast(bf16x8_t, w),
+                            acc[b][0], 0, 0, 0);
+#pragma unroll
+                        for (int ms = 1; ms < MS; ++ms)
+                            acc[b][ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, xq[XL ? 0 : s][ms][s4]),
+                                __builtin_bit_cast(bf16x8_t, w), acc[b][ms], 0, 0, 0);
                     }
                 }
                 issue_next(k, u);
@@ -2448,9 +2480,9 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
             // tables.  Only the outputs of rows m < M are passed on: lane l holds
             // y[4*(l/16) + v][l % 16], so the first 16*LQ lanes and VC values.
             stamp(6);
-            constexpr int VC = MT < 4 ? MT : 4;
-            constexpr int LQ = (MT + 3) / 4;
-            constexpr int OUT = 16 * LQ * VC;   // outputs of a block
+            constexpr int VC = MTS < 4 ? MTS : 4;
+            constexpr int LQ = (MTS + 3) / 4;
+            constexpr int OUT = 16 * LQ * VC;   // outputs of a block's slice
             float* redf = reinterpret_cast<float*>(smem);
             if constexpr (VD) {
                 // the four lanes of a row (l, l+16, l+32, l+48) hold its four
@@ -2459,38 +2491,44 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
                 for (int b = 0; b < NBG; ++b) {
                     float t = dacc[b] + __shfl_xor(dacc[b], 16);
                     t += __shfl_xor(t, 32);
-                    acc[b] = f32x4_t{t, 0.f, 0.f, 0.f};
+                    acc[b][0] = f32x4_t{t, 0.f, 0.f, 0.f};
                     dacc[b] = 0.f;
                 }
             }
-            __syncthreads();
-            if (lane < 16 * LQ) {
+            // one pass per slice of 16 x rows (the partial sums of one slice
+            // fill the table region)
 #pragma unroll
-                for (int b = 0; b < NBG; ++b)
+            for (int ms = 0; ms < MS; ++ms) {
+                __syncthreads();
+                if (lane < 16 * LQ) {
 #pragma unroll
-                    for (int v = 0; v < VC; ++v)
-                        redf[(b * NW + wave) * OUT + lane * VC + v] = acc[b][v];
-            }
-            if constexpr (MG) {
-                if (gi + 1 < ngroups)
-                    stage_store(lqn, aqn, bqn);
-            }
-            __syncthreads();
-            for (int t = tid; t < NBG * OUT; t += NT) {   // every thread sums outputs
-                const int b = t / OUT;
-                const int o = t - b * OUT;
-                const int blk = gi * NBG + b;
-                float tot = redf[b * NW * OUT + o];
-                for (int w = 1; w < NW; ++w)
-                    tot += redf[(b * NW + w) * OUT + o];
-                const int l = o / VC;
-                const int m = (l >> 4) * 4 + (o - l * VC);
-                const int n = (r + blk * Gs) * TILE_ROWS + (l & 15);
-                if (blk < nblk && m < M && n < N) {
-                    if (S > 1)   // this split's partial sum, added up by k_split_sum
-                        args.ws[(static_cast<size_t>(split) * M + m) * N + n] = tot;
-                    else
-                        args.y[static_cast<size_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16(tot));
+                    for (int b = 0; b < NBG; ++b)
+#pragma unroll
+                        for (int v = 0; v < VC; ++v)
+                            redf[(b * NW + wave) * OUT + lane * VC + v] = acc[b][ms][v];
+                }
+                if constexpr (MG) {
+                    if (ms == 0 && gi + 1 < ngroups)
+                        stage_store(lqn, aqn, bqn);
+                }
+                __syncthreads();
+                for (int t = tid; t < NBG * OUT; t += NT) {   // every thread sums outputs
+                    const int b = t / OUT;
+                    const int o = t - b * OUT;
+                    const int blk = gi * NBG + b;
+                    float tot = redf[b * NW * OUT + o];
+                    for (int w = 1; w < NW; ++w)
+                        tot += redf[(b * NW + w) * OUT + o];
+                    const int l = o / VC;
+                    const int m = 16 * ms + (l >> 4) * 4 + (o - l * VC);
+                    const int n = (r + blk * Gs) * TILE_ROWS + (l & 15);
+                    if (blk < nblk && m < M && n < N) {
+                        if (S > 1)   // this split's partial sum, added up by k_split_sum
+                            args.ws[(static_cast<size_t>(split) * M + m) * N + n] = tot;
+                        else
+                            args.y[static_cast<size_t>(m) * N + n] =
+                                static_cast<uint16_t>(f32_to_bf16(tot));
+                    }
                 }
             }
             stamp(7);
@@ -2502,7 +2540,9 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
                     load_scales();
 #pragma unroll
                     for (int b = 0; b < NBG; ++b)
-                        acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ms = 0; ms < MS; ++ms)
+                            acc[b][ms] = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 }
             }
         }
@@ -2649,10 +2689,25 @@ size_t st_workspace_bytes(int M, int N, int K)
 }
 
 // Ring depths that fit 128 VGPRs (16 waves per CU) without spilling: x in
-// the ring costs 16 registers per chunk, the next group's staging 20.
-constexpr bool st_ring_ok(int nbg, int r, bool xl, bool mg)
+// the ring costs 16 registers per chunk, the next group's staging 20.  Wide
+// batches (ms slices of 16 x rows, 8 waves per CU and 256 VGPRs) take 16*ms
+// registers of x per chunk and 4*ms of sums per block.
+#ifndef ANY4_ST_W16_MAX_M
+#define ANY4_ST_W16_MAX_M 32
+#endif
+constexpr int ST_W16_MAX_M = ANY4_ST_W16_MAX_M;   // 16 waves per CU up to this many x rows
+// The most waves per workgroup: 16 (128 VGPRs each) up to 32 x rows, 8 (256
+// VGPRs) beyond, and for two or three slices of x with one block per group
+// (its two-step bodies do not fit 128)
+constexpr int st_waves(int M, int nbg)
+{
+    return M > ST_W16_MAX_M || (M > 16 && nbg == 1) ? ST_MAX_WAVES / 2 : ST_MAX_WAVES;
+}
+constexpr bool st_ring_ok(int nbg, int r, bool xl, bool mg, int ms = 1)
 {
     const int tpw = nbg * r;
+    if (ms > 1)
+        return !xl && !mg && tpw <= 8 && r <= 2;
     if (xl)
         return tpw <= (mg ? 4 : 8);
     if (mg)
@@ -2687,10 +2742,12 @@ inline bool st_plan(int M, int N, int K, int g, bool split_ok, StPlan& P)
             if (L.total > ST_LDS)
                 continue;
             int best = -1;
+            const int ms = M > 16 ? (M + 15) / 16 : 1;
+            const int max_waves = st_waves(M, nbg);
             for (int r = 1; r * nbg <= 8; r *= 2) {
-                if (!st_ring_ok(nbg, r, xl, mg))
+                if (!st_ring_ok(nbg, r, xl, mg, ms))
                     continue;
-                for (int nw = ST_MAX_WAVES; nw >= 1; --nw) {
+                for (int nw = max_waves; nw >= 1; --nw) {
 #ifdef ANY4_PROBE_TS
                     if ((st_force_nw && nw != st_force_nw) || (st_force_r && r != st_force_r))
                         continue;
@@ -2702,7 +2759,7 @@ inline bool st_plan(int M, int N, int K, int g, bool split_ok, StPlan& P)
                         continue;
                     const int cw = r * ((Kc + nw * r - 1) / (nw * r));
                     const int waste = nw * cw - Kc;
-                    const int score = waste * 4096 + (ST_MAX_WAVES - nw) * 64 + cw / r;
+                    const int score = waste * 4096 + (max_waves - nw) * 64 + cw / r;
                     if (best < 0 || score < best) {
                         best = score;
                         P.nw = nw;
@@ -2735,13 +2792,23 @@ inline bool st_plan(int M, int N, int K, int g, bool split_ok, StPlan& P)
 #ifndef ANY4_ST_D
 #define ANY4_ST_D 2
 #endif
+// The deepest ring up to dw tiles that divides a body and, with x in the
+// ring, does not overwrite a step's x before the step's last tile.
+constexpr int st_depth(int tb, int nbg, bool xl, int dw)
+{
+    for (int d = dw < tb ? dw : tb; d > 1; --d)
+        if (tb % d == 0 && (xl || tb - d >= nbg - 1))
+            return d;
+    return 1;
+}
+
 template <int MT, int NBG, int R, bool XL, bool MG, int FMT>
 void st_go(const StArgs& sa, const StPlan& P, hipStream_t stream)
 {
-    constexpr int LB = 1024;
-    constexpr int TB = NBG * R;
-    constexpr int DD = ANY4_ST_D < TB ? ANY4_ST_D : TB;
-    constexpr int D = (XL || TB - DD >= NBG - 1) ? DD : 1;
+    // 8 waves of 256 VGPRs, 4 tiles in flight each: see st_waves
+    constexpr bool W8 = st_waves(MT, NBG) < ST_MAX_WAVES;
+    constexpr int LB = W8 ? 512 : 1024;
+    constexpr int D = st_depth(NBG * R, NBG, XL, W8 ? 4 : ANY4_ST_D);
     hipLaunchKernelGGL((k_gemm_st<MT, NBG, R, XL, MG, LB, ANY4_ST_PRE, D, FMT>), dim3(P.grid),
                        dim3(64 * P.nw), 0, stream, sa);
 }
@@ -2800,17 +2867,33 @@ bool launch_st(const GemmArgs& a, hipStream_t stream, unsigned long long* ts)
     if (!st_plan(a.M, a.N, a.K, a.g, a.ws != nullptr, P))
         return false;
     StArgs sa{a, P.splits, P.gstage, P.cw, P.L, ts};
-    switch (P.nbg * 16 + P.r) {
-    case 16 + 1: st_go_r<MT, 1, 1, FMT>(sa, P, stream); break;
-    case 16 + 2: st_go_r<MT, 1, 2, FMT>(sa, P, stream); break;
-    case 16 + 4: st_go_r<MT, 1, 4, FMT>(sa, P, stream); break;
-    case 16 + 8: st_go_r<MT, 1, 8, FMT>(sa, P, stream); break;
-    case 32 + 1: st_go_r<MT, 2, 1, FMT>(sa, P, stream); break;
-    case 32 + 2: st_go_r<MT, 2, 2, FMT>(sa, P, stream); break;
-    case 32 + 4: st_go_r<MT, 2, 4, FMT>(sa, P, stream); break;
-    case 64 + 1: st_go_r<MT, 4, 1, FMT>(sa, P, stream); break;
-    case 64 + 2: st_go_r<MT, 4, 2, FMT>(sa, P, stream); break;
-    default: return false;
+    if constexpr (MT > 16) {
+        // wide batches: one group, x in the ring, bodies of one or two steps
+        if (P.mg || P.xl || P.splits > 1)
+            return false;
+        switch (P.nbg * 16 + P.r) {
+        case 16 + 1: st_go<MT, 1, 1, false, false, FMT>(sa, P, stream); break;
+        case 16 + 2: st_go<MT, 1, 2, false, false, FMT>(sa, P, stream); break;
+        case 32 + 1: st_go<MT, 2, 1, false, false, FMT>(sa, P, stream); break;
+        case 32 + 2: st_go<MT, 2, 2, false, false, FMT>(sa, P, stream); break;
+        case 64 + 1: st_go<MT, 4, 1, false, false, FMT>(sa, P, stream); break;
+        case 64 + 2: st_go<MT, 4, 2, false, false, FMT>(sa, P, stream); break;
+        default: return false;
+        }
+        return true;
+    } else {
+        switch (P.nbg * 16 + P.r) {
+        case 16 + 1: st_go_r<MT, 1, 1, FMT>(sa, P, stream); break;
+        case 16 + 2: st_go_r<MT, 1, 2, FMT>(sa, P, stream); break;
+        case 16 + 4: st_go_r<MT, 1, 4, FMT>(sa, P, stream); break;
+        case 16 + 8: st_go_r<MT, 1, 8, FMT>(sa, P, stream); break;
+        case 32 + 1: st_go_r<MT, 2, 1, FMT>(sa, P, stream); break;
+        case 32 + 2: st_go_r<MT, 2, 2, FMT>(sa, P, stream); break;
+        case 32 + 4: st_go_r<MT, 2, 4, FMT>(sa, P, stream); break;
+        case 64 + 1: st_go_r<MT, 4, 1, FMT>(sa, P, stream); break;
+        case 64 + 2: st_go_r<MT, 4, 2, FMT>(sa, P, stream); break;
+        default: return false;
+        }
     }
     if (P.splits > 1) {
         const size_t mn = static_cast<size_t>(a.M) * a.N;
@@ -2838,6 +2921,27 @@ static void launch_decode_fmt(const GemmArgs& a, hipStream_t stream)
         launch_gemm<16, FMT>(a, stream);
 }
 
+// M = 17..48 in one pass of the streaming kernel (32 or 48 rows), where it
+// runs for the shape; false: the caller takes 16-row slices instead
+template <int FMT>
+static bool launch_wide_fmt(const GemmArgs& a, hipStream_t stream)
+{
+    if (!use_st(a))
+        return false;
+    return a.M <= 32 ? launch_st<32, FMT>(a, stream, nullptr) : launch_st<48, FMT>(a, stream, nullptr);
+}
+
+static bool launch_wide(const GemmArgs& a, int fmt, hipStream_t stream)
+{
+    if (fmt == FMT_INT4)
+        return launch_wide_fmt<FMT_INT4>(a, stream);
+    if (fmt == FMT_ANY2)
+        return launch_wide_fmt<FMT_ANY2>(a, stream);
+    if (fmt == FMT_ANY3)
+        return launch_wide_fmt<FMT_ANY3>(a, stream);
+    return launch_wide_fmt<FMT_ANY4>(a, stream);
+}
+
 static void launch_decode(const GemmArgs& a, int fmt, hipStream_t stream)
 {
     if (fmt == FMT_INT4)
@@ -2850,17 +2954,20 @@ static void launch_decode(const GemmArgs& a, int fmt, hipStream_t stream)
         launch_decode_fmt<FMT_ANY4>(a, stream);
 }
 
+// 64 weight rows per workgroup: 128 (waves of 64 x 64 outputs) measured
+// slower, 370 against 294 us at M = 1024 on 14336x4096
 template <int BM>
 static void launch_big(const GemmArgs& a, int fmt, hipStream_t stream)
 {
-    const dim3 gd(static_cast<unsigned>((a.N + BIG_BN - 1) / BIG_BN),
+    constexpr int BN = BIG_BN;
+    const dim3 gd(static_cast<unsigned>((a.N + BN - 1) / BN),
                   static_cast<unsigned>((a.M + BM - 1) / BM));
     if (fmt == FMT_ANY2)
-        hipLaunchKernelGGL((k_gemm_big<BM, FMT_ANY2>), gd, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_gemm_big<BM, FMT_ANY2, BN>), gd, dim3(256), 0, stream, a);
     else if (fmt == FMT_ANY3)
-        hipLaunchKernelGGL((k_gemm_big<BM, FMT_ANY3>), gd, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_gemm_big<BM, FMT_ANY3, BN>), gd, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL((k_gemm_big<BM, FMT_ANY4>), gd, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((k_gemm_big<BM, FMT_ANY4, BN>), gd, dim3(256), 0, stream, a);
 }
 
 // Argument checks and dispatch shared by any4_gemm (table lookup),
@@ -2916,9 +3023,15 @@ static any4_status gemm_call(int fmt, const uint16_t* x, const uint8_t* packed, 
     a.ws = need > 0 && workspace ? static_cast<float*>(workspace) : nullptr;
     a.ws_bytes = a.ws ? workspace_bytes : 0;
     if (M > 16 && M <= 48) {
-        // a few decode batches: the streaming kernels on 16-row slices of x and
-        // y (each slice re-reads the weights, still cheaper than the tiled
-        // kernel while it cannot fill the chip)
+        // a few decode batches: one pass of the streaming kernel with two or
+        // three 16-row slices of x against each decoded weight tile; for the
+        // shapes it does not run, 16-row slices of x and y through the decode
+        // kernels (each slice re-reads the weights, still cheaper than the
+        // tiled kernel while it cannot fill the chip)
+        GemmArgs w = a;
+        w.ws = nullptr;   // no split of K
+        if (launch_wide(w, fmt, stream))
+            return launched();
         for (int64_t m0 = 0; m0 < M; m0 += 16) {
             GemmArgs s16 = a;
             s16.x = x + m0 * K;

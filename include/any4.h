@@ -123,8 +123,10 @@ size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
  * any4_gemm -- y = x * W^T with W the any4 weights above.  Built for the
  * decode batches M = 1..16 of the explainer's section 三 (weights streamed
  * once, decoded in registers); larger M (prefill) also works: up to 48 rows
- * as 16-row slices, beyond that a tiled matrix-core product over weight
- * tiles dequantised in on-chip memory.
+ * with the weights still streamed once (two or three 16-row slices of x per
+ * decoded tile; for a few shapes, 16-row slices of x and y that each stream
+ * the weights), beyond that a tiled matrix-core product over weight tiles
+ * dequantised in on-chip memory.
  *     y[m][n] = bf16_rne( sum_k x[m][k] * w[n][k] )
  * Every weight is dequantised inside the kernel (the weights are never
  * written to memory) as bf16_rne(fp32(alpha * v + beta)), v the table value

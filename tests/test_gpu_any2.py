@@ -59,7 +59,9 @@ def test_any2_dequant_bitexact(N, K, g):
                                      (8, 33, 384, 128), (1, 4096 // 4, 14336, 1024),
                                      (16, 300, 14336, 1024), (3, 17, 8192 + 128, 128),
                                      (32, 70, 512, 128), (100, 65, 1024, 128),
-                                     (1, 17, 128, 128), (16, 300, 128, 128)])
+                                     (1, 17, 128, 128), (16, 300, 128, 128),
+                                     # one pass of the streaming kernel for 17..48 rows
+                                     (24, 16 * 600, 512, 128), (40, 16 * 300 + 5, 1024, 256)])
 def test_any2_gemm(M, N, K, g):
     L = Layer2(M * 13 + N + K, M, N, K, g)
     y = any4.any2_gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g)

@@ -189,10 +189,46 @@ def test_gemm_large_k(M, N, K, g):
 
 
 # --------------------------------------------------------------------------
-# M > 16: 16-row slices (M <= 48), then the LDS-tiled MFMA kernel (64 or 128
-# x rows per workgroup)
+# M > 16: M <= 48 in one pass of the streaming kernel where it runs (two or
+# three 16-row slices of x against each decoded weight tile), else 16-row
+# slices through the decode kernels; above 48 the LDS-tiled MFMA kernel (64
+# or 128 x rows per workgroup)
 # --------------------------------------------------------------------------
-# 17..48: 16-row slices through the streaming kernels; above: the tiled kernel
+# one pass: two to four row blocks per CU, or one with K > 4096 (including
+# a workgroup with one block beside others with two, and ragged N and M)
+@pytest.mark.parametrize("M,N,K,g", [(20, 16 * 600, 512, 128), (32, 16 * 600 + 5, 1024, 128),
+                                     (33, 16 * 300, 256, 128), (48, 16 * 600, 640, 128),
+                                     (24, 100, 8192, 1024), (47, 16 * 257, 384, 128),
+                                     (17, 16 * 900, 4096, 128)])
+def test_gemm_wide_batch_one_pass(M, N, K, g):
+    inp = workloads.generic(M * 9 + N + K, M, N, K, g)
+    L = gu.Layer(inp)
+    y = any4.gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g)
+    torch.cuda.synchronize()
+    y_ref, ad = oracle.gemm(inp.x, L.w_ref(), nthreads=oracle.default_threads())
+    r = gu.assert_within_bound(y, y_ref, ad, f"wide batch {M}x{N}x{K} g{g}")
+    print(f"wide batch {M}x{N}x{K} g{g}: max err/tol = {r:.3e}", flush=True)
+
+
+def test_gemm_wide_batch_one_hot_x_returns_dequantised_columns():
+    """One-hot x rows, M = 48 on three row blocks per CU: every x row of each
+    16-row slice lands in its own output row, bit-exactly the dequantised
+    column (the slices share the decoded weights)."""
+    inp = workloads.generic(93, 48, 16 * 600, 512, 128)
+    L = gu.Layer(inp)
+    w_ref = L.w_ref()
+    one = workloads.to_bf16_bits(np.array([1.0]))[0]
+    x = np.zeros((48, 512), np.uint16)
+    ks = np.arange(48) * 10 + 7
+    x[np.arange(48), ks] = one
+    y = any4.gemm(gu.dev_b16(x), L.packed, L.lut, L.alpha, L.beta, 128)
+    torch.cuda.synchronize()
+    yb = gu.host_b16(y)
+    for m, k in enumerate(ks):
+        assert np.array_equal(yb[m], w_ref[:, k]), (m, k)
+
+
+# 17..48 elsewhere: 16-row slices through the decode kernels; above: the tiled kernel
 @pytest.mark.parametrize("M,N,K,g", [(17, 40, 256, 128), (48, 70, 256, 128), (49, 33, 256, 128),
                                      (64, 64, 128, 128), (65, 100, 512, 128),
                                      (100, 300, 1024, 256), (128, 17, 384, 128),
@@ -253,7 +289,8 @@ def _identity_table(N):
                                          (1, 16 * 2000 + 3, 128, 128, None),
                                          (2, 16 * 300 + 7, 8192, 128, None),
                                          (5, 100, 14336, 1024, None), (16, 33, 65536, 128, None),
-                                         (40, 70, 512, 128, None), (200, 33, 1024, 256, None)])
+                                         (40, 70, 512, 128, None), (200, 33, 1024, 256, None),
+                                         (32, 16 * 600, 512, 128, None)])
 def test_gemm_int4(M, N, K, g, cfg):
     """any4_gemm_int4 is bitwise any4_gemm with every table row 0..15, and both
     are within the bound of the oracle's product with the int4 weights."""
