@@ -1506,8 +1506,10 @@ __global__ __launch_bounds__(GT) void k_gemm_kb(const GemmArgs args)
 // wave per SIMD to hide the LDS latency.
 //
 // LDS: XS [BM][128 + 8] bf16, WS [64][128 + 8] bf16 (rows padded by 16 B so
-// that the 16 rows of an operand read fall in different banks), LT [64][16]
-// fp32 (the table rows of the workgroup's 64 weight rows).
+// that the 16 rows of an operand read fall in different banks), LT [16][64][2]
+// fp32 (the table rows of the workgroup's 64 weight rows, entry-major, each
+// value twice so that a half wave's 32 lookups hit 32 banks; row-major, they
+// cost about 7.7K cycles of bank conflicts per wave at M = 256).
 constexpr int BIG_BN = 64;
 constexpr int BIG_LD = TILE_K + 8;   // padded row length in bf16
 constexpr int BIG_PF = 2;            // chunks of global data in flight per thread
@@ -1523,7 +1525,9 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
     constexpr int SL = BN / 64;    // dequantisation slots per thread per chunk
     __shared__ __attribute__((aligned(16))) uint16_t xs[BM * BIG_LD];
     __shared__ __attribute__((aligned(16))) uint16_t ws[BN * BIG_LD];
-    __shared__ float lt[BN * 16];
+    // table values as fp32, [entry][row][2 copies]: the 32 lanes of a half
+    // wave (16 rows x two k quarters) read 32 different banks
+    __shared__ float lt[16 * BN * 2];
 
     const int M = args.M, N = args.N, K = args.K, g = args.g;
     const int tid = threadIdx.x;
@@ -1538,9 +1542,11 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
     // int4): the codes themselves, 0..15
     for (int e = tid; e < BN * 16; e += 256) {
         const int n = n0 + e / 16;
-        lt[e] = n >= N      ? 0.f
-                : args.lut ? bf16_to_f32(args.lut[static_cast<size_t>(n) * 16 + (e & 15)])
-                           : static_cast<float>(e & 15);
+        const float v = n >= N      ? 0.f
+                        : args.lut ? bf16_to_f32(args.lut[static_cast<size_t>(n) * 16 + (e & 15)])
+                                   : static_cast<float>(e & 15);
+        lt[(e & 15) * BN * 2 + (e / 16) * 2] = v;
+        lt[(e & 15) * BN * 2 + (e / 16) * 2 + 1] = v;
     }
 
     // this thread's dequantisation slots: row block wave + 4*sl of the
@@ -1632,7 +1638,16 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
                 if (wlive[q] && c < Kc) {
                     const float a = bf16_to_f32(ab[sl][q] & 0xFFFFu);
                     const float bt = bf16_to_f32(ab[sl][q] >> 16);
-                    const float* L = lt + wrow[q] * 16;
+                    // entry i of this lane's row (its copy for the lane's half wave)
+                    const float* Lr = lt + wrow[q] * 2 + ((lane >> 4) & 1);
+                    auto L = [&](uint32_t i) { return Lr[i * (BN * 2)]; };
+                    // bf16(a*l0 + b) | bf16(a*l1 + b) << 16 with one conversion
+                    auto deq2 = [&](float l0, float l1) {
+                        typedef float f2_t __attribute__((ext_vector_type(2)));
+                        typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+                        const f2_t w = {fmaf(a, l0, bt), fmaf(a, l1, bt)};
+                        return __builtin_bit_cast(uint32_t, __builtin_convertvector(w, bf2_t));
+                    };
                     const u32x4_t p = pk[sl][q];
                     if constexpr (A2) {   // 8 bytes of four 2-bit codes: dwords 2i, 2i+1
 #pragma unroll
@@ -1640,10 +1655,9 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
                             const uint32_t byte = (p[i >> 2] >> (8 * (i & 3))) & 0xFFu;
 #pragma unroll
                             for (int t = 0; t < 2; ++t) {
-                                const float lo = fmaf(a, L[(byte >> (4 * t)) & 3u], bt);
-                                const float hi = fmaf(a, L[(byte >> (4 * t + 2)) & 3u], bt);
                                 const int d = 2 * i + t;
-                                out[d >> 2][d & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+                                out[d >> 2][d & 3] =
+                                    deq2(L((byte >> (4 * t)) & 3u), L((byte >> (4 * t + 2)) & 3u));
                             }
                         }
                     } else if constexpr (A3) {   // 16 pair indices: dwords 0-2, then the top bits
@@ -1652,17 +1666,13 @@ __global__ __launch_bounds__(256) void k_gemm_big(const GemmArgs args)
                         for (int q = 0; q < 16; ++q) {
                             const uint32_t P =
                                 ((q < 12 ? p[q >> 2] : top) >> (8 * (q & 3))) & 0x3Fu;
-                            const float lo = fmaf(a, L[P & 7u], bt);
-                            const float hi = fmaf(a, L[P >> 3], bt);
-                            out[q >> 2][q & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+                            out[q >> 2][q & 3] = deq2(L(P & 7u), L(P >> 3));
                         }
                     } else {
 #pragma unroll
                         for (int q = 0; q < 16; ++q) {
                             const uint32_t byte = (p[q >> 2] >> (8 * (q & 3))) & 0xFFu;
-                            const float lo = fmaf(a, L[byte & 15u], bt);
-                            const float hi = fmaf(a, L[byte >> 4], bt);
-                            out[q >> 2][q & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+                            out[q >> 2][q & 3] = deq2(L(byte & 15u), L(byte >> 4));
                         }
                     }
                 }
