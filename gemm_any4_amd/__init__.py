@@ -76,7 +76,7 @@ def lib() -> ctypes.CDLL:
         L.any4_gemv_dot.restype = ctypes.c_int
         L.any4_gemv_dot.argtypes = [P, P, P, P, P, P, I64, I64, I64, P]
         L.any4_gemm_int4.restype = ctypes.c_int
-        L.any4_gemm_int4.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P]
+        L.any4_gemm_int4.argtypes = [P, P, P, P, P, I64, I64, I64, I64, P, SZ, P]
         L.any4_quantize.restype = ctypes.c_int
         L.any4_quantize.argtypes = [P, P, P, P, P, P, I64, I64, I64, ctypes.c_int, ctypes.c_int, P]
         for v in ("any2", "any3"):
@@ -87,7 +87,7 @@ def lib() -> ctypes.CDLL:
             getattr(L, v + "_dequant").restype = ctypes.c_int
             getattr(L, v + "_dequant").argtypes = [P, P, P, P, P, I64, I64, I64, P]
             getattr(L, v + "_gemm").restype = ctypes.c_int
-            getattr(L, v + "_gemm").argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P]
+            getattr(L, v + "_gemm").argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, P, SZ, P]
         L.any4_read_probe.restype = ctypes.c_int
         L.any4_read_probe.argtypes = [P, SZ, P, P]
         L.any4_status_string.restype = ctypes.c_char_p
@@ -199,9 +199,9 @@ def gemv_dot(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: to
 
 
 def gemm_int4_raw(x_ptr, packed_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
-                  stream=None) -> int:
+                  ws_ptr=None, ws_bytes=0, stream=None) -> int:
     return lib().any4_gemm_int4(x_ptr, packed_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
-                                _stream(stream))
+                                ws_ptr, ws_bytes, _stream(stream))
 
 
 def quantize_raw(w_ptr, ex_ptr, idx_ptr, lut_ptr, alpha_ptr, beta_ptr, N, K, g, iters,
@@ -295,23 +295,32 @@ def gemm(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: torch.
     if out.shape != (M, N):
         raise ValueError("y must be [M, N]")
     sh = _stream(stream)
-    need = workspace_size(M, N, K, g)
-    ws_ptr, ws_bytes = None, 0
-    if need:
-        if workspace is None:
-            workspace = _workspace(need, x.device, sh)
-        if workspace.numel():
-            _dev(workspace, "workspace")
-            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    ws_ptr, ws_bytes = _workspace_args(workspace, M, N, K, g, x.device, sh)
     check(gemm_raw(_ptr(x), _ptr(packed), _ptr(lut), _ptr(alpha), _ptr(beta), _ptr(out), M, N, K,
                    g, ws_ptr, ws_bytes, sh))
     return out
 
 
+def _workspace_args(workspace, M: int, N: int, K: int, g: int, device, sh):
+    """(pointer, bytes) of the split-K workspace for a GEMM call: the caller's
+    tensor (an empty one: none), else the cached one of this device and
+    stream, or (None, 0) where the shape needs none."""
+    need = workspace_size(M, N, K, g)
+    if not need:
+        return None, 0
+    if workspace is None:
+        workspace = _workspace(need, device, sh)
+    if not workspace.numel():
+        return None, 0
+    _dev(workspace, "workspace")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def gemm_int4(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
-              g: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+              g: int, out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+              stream=None) -> torch.Tensor:
     """y [M, N] = x [M, K] * W^T with plain int4 weights w = alpha * q + beta
-    (q the 4-bit code, 0..15; N from alpha)."""
+    (q the 4-bit code, 0..15; N from alpha).  workspace as for gemm()."""
     _b16(x, "x"), _b16(alpha, "alpha"), _b16(beta, "beta")
     M, K = x.shape
     if g <= 0 or K % g or alpha.dim() != 2 or alpha.shape[1] != K // g or beta.shape != alpha.shape:
@@ -323,8 +332,10 @@ def gemm_int4(x: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor, beta: 
     _b16(out, "y")
     if out.shape != (M, N):
         raise ValueError("y must be [M, N]")
+    sh = _stream(stream)
+    ws_ptr, ws_bytes = _workspace_args(workspace, M, N, K, g, x.device, sh)
     check(gemm_int4_raw(_ptr(x), _ptr(packed), _ptr(alpha), _ptr(beta), _ptr(out), M, N, K, g,
-                        stream))
+                        ws_ptr, ws_bytes, sh))
     return out
 
 
@@ -387,15 +398,15 @@ def any3_dequant_raw(packed_ptr, lut_ptr, alpha_ptr, beta_ptr, w_ptr, N, K, g,
 
 
 def any2_gemm_raw(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
-                  stream=None) -> int:
+                  ws_ptr=None, ws_bytes=0, stream=None) -> int:
     return lib().any2_gemm(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
-                           _stream(stream))
+                           ws_ptr, ws_bytes, _stream(stream))
 
 
 def any3_gemm_raw(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
-                  stream=None) -> int:
+                  ws_ptr=None, ws_bytes=0, stream=None) -> int:
     return lib().any3_gemm(x_ptr, packed_ptr, lut_ptr, alpha_ptr, beta_ptr, y_ptr, M, N, K, g,
-                           _stream(stream))
+                           ws_ptr, ws_bytes, _stream(stream))
 
 
 _LOWBIT = {2: (any2_packed_bytes, any2_pack_raw, any2_dequant_raw, any2_gemm_raw),
@@ -443,7 +454,8 @@ def _lowbit_dequant(bits: int, packed, lut, alpha, beta, g: int, out, stream) ->
     return out
 
 
-def _lowbit_gemm(bits: int, x, packed, lut, alpha, beta, g: int, out, stream) -> torch.Tensor:
+def _lowbit_gemm(bits: int, x, packed, lut, alpha, beta, g: int, out, workspace,
+                 stream) -> torch.Tensor:
     _b16(x, "x"), _b16(lut, "lut"), _b16(alpha, "alpha"), _b16(beta, "beta")
     M, K = x.shape
     if lut.dim() != 2 or lut.shape[1] != 16:
@@ -457,8 +469,10 @@ def _lowbit_gemm(bits: int, x, packed, lut, alpha, beta, g: int, out, stream) ->
     _b16(out, "y")
     if out.shape != (M, N):
         raise ValueError("y must be [M, N]")
+    sh = _stream(stream)
+    ws_ptr, ws_bytes = _workspace_args(workspace, M, N, K, g, x.device, sh)
     check(_LOWBIT[bits][3](_ptr(x), _ptr(packed), _ptr(lut), _ptr(alpha), _ptr(beta), _ptr(out),
-                           M, N, K, g, stream))
+                           M, N, K, g, ws_ptr, ws_bytes, sh))
     return out
 
 
@@ -488,16 +502,18 @@ def any3_dequant(packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor,
 
 def any2_gemm(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor,
               beta: torch.Tensor, g: int, out: torch.Tensor | None = None,
-              stream=None) -> torch.Tensor:
-    """y [M, N] = x [M, K] * W^T with W an any2 layer (N from lut)."""
-    return _lowbit_gemm(2, x, packed, lut, alpha, beta, g, out, stream)
+              workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y [M, N] = x [M, K] * W^T with W an any2 layer (N from lut); workspace
+    as for gemm()."""
+    return _lowbit_gemm(2, x, packed, lut, alpha, beta, g, out, workspace, stream)
 
 
 def any3_gemm(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: torch.Tensor,
               beta: torch.Tensor, g: int, out: torch.Tensor | None = None,
-              stream=None) -> torch.Tensor:
-    """y [M, N] = x [M, K] * W^T with W an any3 layer (N from lut)."""
-    return _lowbit_gemm(3, x, packed, lut, alpha, beta, g, out, stream)
+              workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y [M, N] = x [M, K] * W^T with W an any3 layer (N from lut); workspace
+    as for gemm()."""
+    return _lowbit_gemm(3, x, packed, lut, alpha, beta, g, out, workspace, stream)
 
 
 def read_probe_raw(buf_ptr, nbytes: int, out_ptr, stream=None) -> int:

@@ -3327,9 +3327,11 @@ any4_status any4_gemv_dot(const uint16_t* x, const uint8_t* packed, const uint16
 
 any4_status any4_gemm_int4(const uint16_t* x, const uint8_t* packed, const uint16_t* alpha,
                            const uint16_t* beta, uint16_t* y, int64_t M, int64_t N, int64_t K,
-                           int64_t g, hipStream_t stream)
+                           int64_t g, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream)
 {
-    return gemm_call(FMT_INT4, x, packed, nullptr, alpha, beta, y, M, N, K, g, stream);
+    return gemm_call(FMT_INT4, x, packed, nullptr, alpha, beta, y, M, N, K, g, stream, workspace,
+                     workspace_bytes);
 }
 
 any4_status any4_read_probe(const void* buf, size_t bytes, uint32_t* out, hipStream_t stream)
@@ -3408,16 +3410,20 @@ any4_status any3_dequant(const uint8_t* packed, const uint16_t* lut, const uint1
 
 any4_status any2_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
                       const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
-                      int64_t N, int64_t K, int64_t g, hipStream_t stream)
+                      int64_t N, int64_t K, int64_t g, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream)
 {
-    return gemm_call(FMT_ANY2, x, packed, lut, alpha, beta, y, M, N, K, g, stream);
+    return gemm_call(FMT_ANY2, x, packed, lut, alpha, beta, y, M, N, K, g, stream, workspace,
+                     workspace_bytes);
 }
 
 any4_status any3_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
                       const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
-                      int64_t N, int64_t K, int64_t g, hipStream_t stream)
+                      int64_t N, int64_t K, int64_t g, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream)
 {
-    return gemm_call(FMT_ANY3, x, packed, lut, alpha, beta, y, M, N, K, g, stream);
+    return gemm_call(FMT_ANY3, x, packed, lut, alpha, beta, y, M, N, K, g, stream, workspace,
+                     workspace_bytes);
 }
 
 any4_status any4_quantize(const float* W, const float* ex, uint8_t* idx, uint16_t* lut,

@@ -217,13 +217,14 @@ any4_status any4_gemv_dot(const uint16_t* x, const uint8_t* packed, const uint16
  *     y[m][n] = bf16_rne( sum_k x[m][k] * w[n][k] )
  * q[n][k] is the 4-bit code in `packed` (same tile layout), read as 0..15.
  * The result is bit-identical to any4_gemm with every table row 0, 1, .., 15
- * and a NULL workspace (K is never split here), and carries the same error
- * bound.  Arguments, sizes, alignment and errors as any4_gemm, without lut
- * and without a workspace.
+ * and the same workspace (given or NULL), and carries the same error bound.
+ * Arguments, sizes, alignment, workspace and errors as any4_gemm, without
+ * lut.
  */
 any4_status any4_gemm_int4(const uint16_t* x, const uint8_t* packed, const uint16_t* alpha,
                            const uint16_t* beta, uint16_t* y, int64_t M, int64_t N, int64_t K,
-                           int64_t g, hipStream_t stream);
+                           int64_t g, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /*
  * any2 -- the 2-bit variant at 2 bits per stored weight (the paper's abstract
@@ -243,8 +244,9 @@ any4_status any4_gemm_int4(const uint16_t* x, const uint8_t* packed, const uint1
  * [N/16][K/128][4][16][8].
  * any2_pack, any2_dequant and any2_gemm take the same arguments and follow
  * the same conventions, checks and errors as any4_pack, any4_dequant and
- * any4_gemm (no workspace argument), with idx read as codes 0..3 (bits
- * above 1 ignored):
+ * any4_gemm (the same optional workspace, sized by
+ * any4_gemm_workspace_size), with idx read as codes 0..3 (bits above 1
+ * ignored):
  *     w[n][k] = bf16_rne( fp32( alpha[n][k/g] * lut[n][code[n][k]] + beta[n][k/g] ) )
  *     y[m][n] = bf16_rne( sum_k x[m][k] * w[n][k] )   (same bound as any4_gemm)
  * Returns of any2_packed_bytes: ceil(N/16) * 16 * K/4, or 0 as any4_packed_bytes.
@@ -257,7 +259,8 @@ any4_status any2_dequant(const uint8_t* packed, const uint16_t* lut, const uint1
                          hipStream_t stream);
 any4_status any2_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
                       const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
-                      int64_t N, int64_t K, int64_t g, hipStream_t stream);
+                      int64_t N, int64_t K, int64_t g, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
 
 /*
  * any3 -- the 3-bit variant at 3 bits per stored weight (the paper's abstract
@@ -291,7 +294,8 @@ any4_status any3_dequant(const uint8_t* packed, const uint16_t* lut, const uint1
                          hipStream_t stream);
 any4_status any3_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* lut,
                       const uint16_t* alpha, const uint16_t* beta, uint16_t* y, int64_t M,
-                      int64_t N, int64_t K, int64_t g, hipStream_t stream);
+                      int64_t N, int64_t K, int64_t g, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
 
 /*
  * any4_quantize -- the any4 quantiser: turns weights into the idx, lut, alpha

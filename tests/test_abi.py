@@ -116,6 +116,23 @@ def test_gemm_int4_errors():
     assert any4.gemm_int4_raw(None, None, None, None, None, 0, 16, 128, 128, stream=0) == 0
 
 
+def test_workspace_errors_of_every_format():
+    """A shape that splits K (M = 16, 256 row blocks, K = 12288) needs a
+    workspace of any4_gemm_workspace_size bytes; every GEMM entry point that
+    takes one rejects a smaller one (ANY4_E_WORKSPACE) or a misaligned one
+    (ANY4_E_ALIGN) before any launch."""
+    M, N, K, g = 16, 16 * 256, 12288, 128
+    need = any4.workspace_size(M, N, K, g)
+    assert need == 4 * M * N * 4
+    calls = [lambda w, b: any4.gemm_raw(A, A, A, A, A, A, M, N, K, g, w, b, stream=0),
+             lambda w, b: any4.gemm_int4_raw(A, A, A, A, A, M, N, K, g, w, b, stream=0),
+             lambda w, b: any4.any2_gemm_raw(A, A, A, A, A, A, M, N, K, g, w, b, stream=0),
+             lambda w, b: any4.any3_gemm_raw(A, A, A, A, A, A, M, N, K, g, w, b, stream=0)]
+    for call in calls:
+        assert call(A, need - 1) == 4
+        assert call(A + 8, need) == 3
+
+
 def test_quantize_errors():
     assert any4.quantize_raw(A, A, A, A, A, A, 4, 256, 96, 10, stream=0) == 2     # K % g
     assert any4.quantize_raw(A, A, A, A, A, A, 4, 256, 128, -1, stream=0) == 2    # iters

@@ -61,13 +61,18 @@ def test_any2_dequant_bitexact(N, K, g):
                                      (32, 70, 512, 128), (100, 65, 1024, 128),
                                      (1, 17, 128, 128), (16, 300, 128, 128),
                                      # one pass of the streaming kernel for 17..48 rows
-                                     (24, 16 * 600, 512, 128), (40, 16 * 300 + 5, 1024, 256)])
+                                     (24, 16 * 600, 512, 128), (40, 16 * 300 + 5, 1024, 256),
+                                     # K split over workgroups (with the default workspace)
+                                     (16, 16 * 256, 12288, 128)])
 def test_any2_gemm(M, N, K, g):
     L = Layer2(M * 13 + N + K, M, N, K, g)
-    y = any4.any2_gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g)
+    y = any4.any2_gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g, workspace=gu.no_workspace())
     y4 = any4.gemm(L.x, L.packed4, L.lut, L.alpha, L.beta, g, workspace=gu.no_workspace())
+    ys = any4.any2_gemm(L.x, L.packed, L.lut, L.alpha, L.beta, g)      # K may be split
+    y4s = any4.gemm(L.x, L.packed4, L.lut, L.alpha, L.beta, g)           # ... the same way
     torch.cuda.synchronize()
     assert np.array_equal(gu.host_b16(y), gu.host_b16(y4))
+    assert np.array_equal(gu.host_b16(ys), gu.host_b16(y4s))
     rows = np.arange(N)
     if N * K > 1 << 24:
         rng = np.random.default_rng(M)

@@ -292,8 +292,9 @@ def _identity_table(N):
                                          (40, 70, 512, 128, None), (200, 33, 1024, 256, None),
                                          (32, 16 * 600, 512, 128, None)])
 def test_gemm_int4(M, N, K, g, cfg):
-    """any4_gemm_int4 is bitwise any4_gemm with every table row 0..15, and both
-    are within the bound of the oracle's product with the int4 weights."""
+    """any4_gemm_int4 is bitwise any4_gemm with every table row 0..15 and the
+    same workspace (none, or one that lets K split), and both are within the
+    bound of the oracle's product with the int4 weights."""
     if cfg is not None:
         inp = gu.config_layer(cfg).inp
         x = gu.config_layer(cfg).x[:M]
@@ -304,11 +305,13 @@ def test_gemm_int4(M, N, K, g, cfg):
     lut = _identity_table(inp.N)
     L = gu.Layer(workloads.Any4Inputs(inp.N, inp.K, inp.g, inp.idx, lut, inp.alpha, inp.beta,
                                       x_host))
-    y4 = any4.gemm_int4(x, L.packed, L.alpha, L.beta, inp.g)
+    y4 = any4.gemm_int4(x, L.packed, L.alpha, L.beta, inp.g, workspace=gu.no_workspace())
     y = any4.gemm(x, L.packed, L.lut, L.alpha, L.beta, inp.g, workspace=gu.no_workspace())
-    ys = any4.gemm(x, L.packed, L.lut, L.alpha, L.beta, inp.g)   # K may be split
+    y4s = any4.gemm_int4(x, L.packed, L.alpha, L.beta, inp.g)             # K may be split
+    ys = any4.gemm(x, L.packed, L.lut, L.alpha, L.beta, inp.g)            # ... the same way
     torch.cuda.synchronize()
     assert np.array_equal(gu.host_b16(y4), gu.host_b16(y))
+    assert np.array_equal(gu.host_b16(y4s), gu.host_b16(ys))
     w_int4 = L.w_ref()     # the oracle's dequant with the identity table is int4
     rows = np.arange(inp.N)
     if inp.N * inp.K > 1 << 24:   # full-size layers: sampled rows
@@ -318,6 +321,7 @@ def test_gemm_int4(M, N, K, g, cfg):
     sel = torch.from_numpy(rows).to(gu.DEV)
     gu.assert_within_bound(y4[:, sel], y_ref, ad, f"int4 {M}x{inp.N}x{inp.K} g{inp.g}")
     gu.assert_within_bound(ys[:, sel], y_ref, ad, f"table 0..15 {M}x{inp.N}x{inp.K} g{inp.g}")
+    gu.assert_within_bound(y4s[:, sel], y_ref, ad, f"int4, split {M}x{inp.N}x{inp.K} g{inp.g}")
 
 
 def test_gemm_int4_empty_and_k0():
