@@ -579,14 +579,23 @@ __device__ __forceinline__ void store_pairs(uint8_t* smem, uint32_t base, int q,
     }
 }
 
+// floor(a / d) for 0 <= a < 2^22 from inv = 1/d rounded to fp32: (a + 1/2)/d
+// lies at least 1/(2d) from an integer and the product's error is below
+// (a + 1/2)/d * 2^-23, so the truncation is exact.
+__device__ __forceinline__ int small_div(int a, float inv)
+{
+    return static_cast<int>((static_cast<float>(a) + 0.5f) * inv);
+}
+
 // store_pairs for a staged range of groups: of the 8 values of piece q
 // (elements 8q..8q+7 of the block's [16][G] arrays), those of groups
-// gbase..gbase+GS-1, stored as [group - gbase][row].
+// gbase..gbase+GS-1, stored as [group - gbase][row].  inv_G = 1/G in fp32
+// (8q < 2^22).
 __device__ __forceinline__ void store_pairs_range(uint8_t* smem, uint32_t base, int q, int G,
-                                                  int gbase, int GS, const u32x4_t& qa,
-                                                  const u32x4_t& qb)
+                                                  float inv_G, int gbase, int GS,
+                                                  const u32x4_t& qa, const u32x4_t& qb)
 {
-    int row = (8 * q) / G;
+    int row = small_div(8 * q, inv_G);
     int grp = 8 * q - row * G;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -2097,11 +2106,18 @@ constexpr int ST_XP = 4;   // 16-byte pieces of x per thread (XL)
 
 struct StArgs {
     GemmArgs a;
-    int splits;    // K is split over this many workgroups (partial sums in a.ws)
+    int splits;    // K is split over this many workgroups (partial sums in a.ws), at most 4
     int gstage;    // alpha/beta groups staged per block (GS)
     int cw;        // chunks per wave (a multiple of R)
     StLayout L;
     unsigned long long* ts;   // per-wave timestamps (probe builds only), or null
+    // Launch constants the host works out, so that no integer division runs
+    // between a wave's start and its first loads: K/g, g/128, workgroups per
+    // split, chunks per split, the most row blocks a workgroup owns, the first
+    // staged group of each split, and 1/(2 K/g), 1/(K/g) for small quotients
+    int G, gc, Gs, KcS, nbmax;
+    int gbase[4];
+    float inv_abper, inv_G;
 };
 
 template <int MT, int NBG, int R, bool XL, bool MG, int LB, int PRE, int D, int FMT, bool VD = false>
@@ -2135,25 +2151,28 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
     const int NW = NT >> 6;
     const int j = lane & 15;
     const int kq = lane >> 4;
-    const int Kc = K / TILE_K;
+    const int Kc = K >> 7;   // K / TILE_K
     const int NB = (N + TILE_ROWS - 1) / TILE_ROWS;
-    const int G = K / g;
-    const int gc = g / TILE_K;   // chunks per group
-    // with splits S, workgroup r' = split * Gs + r takes chunks
+    const int G = sa.G;
+    const int gc = sa.gc;   // chunks per group
+    (void)g;
+    // with splits S (at most 4), workgroup r' = split * Gs + r takes chunks
     // [split*KcS, (split+1)*KcS) of the same row blocks as workgroup r
     const int S = sa.splits;
-    const int Gs = gridDim.x / S;
-    const int split = blockIdx.x / Gs;
-    const int r = blockIdx.x - split * Gs;
-    const int KcS = (Kc + S - 1) / S;
+    const int Gs = sa.Gs;
+    const int bx = blockIdx.x;
+    const int split = (bx >= Gs) + (bx >= 2 * Gs) + (bx >= 3 * Gs);
+    const int r = bx - split * Gs;
+    const int KcS = sa.KcS;
     const int kend = min((split + 1) * KcS, Kc);   // chunks from kend on are dead
-    const int nblk = r < NB ? (NB - 1 - r) / Gs + 1 : 0;
+    // row blocks r, r+Gs, ... below NB: nbmax of them, or one fewer (r < Gs <= NB)
+    const int nblk = sa.nbmax - 1 + (r + (sa.nbmax - 1) * Gs < NB ? 1 : 0);
     const int ngroups = MG ? (nblk + NBG - 1) / NBG : 1;
     const int cw = sa.cw;
     const int bpg = cw / R;        // bodies per group
     const int c0 = split * KcS + wave * cw;
     const int GS = sa.gstage;
-    const int gbase = (split * KcS) / gc;   // first staged group
+    const int gbase = sa.gbase[split];   // first staged group
 #ifdef ANY4_PROBE_TS
     unsigned long long* ts = sa.ts ? sa.ts + (static_cast<size_t>(r) * NW + wave) * 8 : nullptr;
     auto stamp = [&](int i) {
@@ -2181,13 +2200,27 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int q = tid + h * NT;
-        ab_blk[h] = q / ab_per;
+        ab_blk[h] = small_div(q, sa.inv_abper);   // q < 2048
         ab_pc[h] = q - ab_blk[h] * ab_per;
     }
+    // Early build (one group, pair tables, a build item per thread): the
+    // lanes of a wave build items of one 64 KB table region (blocks 2p and
+    // 2p+1, NBG even) or of one block (NBG odd), so each wave loads those
+    // blocks' table rows itself (lanes 0-31 block 2p, 32-63 block 2p+1, or
+    // lanes 0-31 the one block), stages them and builds its items without
+    // waiting for the other waves; the waves of a block store identical
+    // staging values.  Otherwise the first 32*NBG threads stage every
+    // block's rows and the workgroup meets at a barrier before the build.
+    constexpr bool EBC = !MG && !I4 && !A2;
+    constexpr bool RM = NBG % 2 == 0;   // region-major build items
+    const bool eb = EBC && NT >= NBG * 256;
+    const bool lut_lane = eb ? tid < NBG * 256 && (RM || lane < 32) : tid < 32 * NBG;
+    // block of the lane's staged rows
+    const int lut_blk = eb ? (RM ? 2 * (tid >> 9) + (lane >> 5) : tid >> 8) : tid >> 5;
     auto stage_load = [&](int gi, u32x4_t& lq, u32x4_t (&aq)[2], u32x4_t (&bq)[2]) {
         {
-            const int blk = gi * NBG + (tid >> 5);
-            const bool live = tid < 32 * NBG && blk < nblk;
+            const int blk = gi * NBG + lut_blk;
+            const bool live = lut_lane && blk < nblk;
             const uint32_t o = (static_cast<uint32_t>(r + blk * Gs) * 512 + (tid & 31) * 16) |
                                (static_cast<uint32_t>(!live) << 31);
             if constexpr (I4)
@@ -2200,7 +2233,7 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
             const int blk = gi * NBG + ab_blk[h];
             // the piece's 8 values are groups g0..g0+7 (mod G) of its rows:
             // loaded only if one of them is staged
-            const int g0 = (8 * ab_pc[h]) % G;
+            const int g0 = 8 * ab_pc[h] - G * small_div(8 * ab_pc[h], sa.inv_G);   // (8 pc) mod G
             const bool need = G <= GS || (g0 + 7 >= gbase && g0 < gbase + GS) ||
                               (g0 + 7 >= G && (g0 + 7 - G) >= gbase);
             const bool live = ab_blk[h] < NBG && blk < nblk && need;
@@ -2213,34 +2246,34 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
     auto stage_store = [&](const u32x4_t& lq, const u32x4_t (&aq)[2], const u32x4_t (&bq)[2]) {
         const int sc = I4 ? 0 : lut_scale(lq);   // all lanes: lanes 2i, 2i+1 hold one row
         const u32x4_t lh = I4 ? lq : lut_to_f16(lq, sc);
-        if (tid < 32 * NBG) {
+        if (lut_lane) {
             // by row quad, entry, row: a build thread reads one entry of four
             // rows with one 8-byte read, eight entries with two 16-byte reads
             const int row = (tid & 31) >> 1;
-            const uint32_t base = L.luts + (tid >> 5) * 512 + (row >> 2) * 128 + (row & 3) * 2;
+            const uint32_t base = L.luts + lut_blk * 512 + (row >> 2) * 128 + (row & 3) * 2;
             const int e0 = (tid & 1) * 8;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 lds_at<uint16_t>(smem, base + (e0 + i) * 8) =
                     static_cast<uint16_t>(lh[i >> 1] >> (16 * (i & 1)));
             if ((tid & 1) == 0)
-                lds_at<int>(smem, L.scl + (tid >> 1) * 4) = sc;
+                lds_at<int>(smem, L.scl + (lut_blk * 16 + row) * 4) = sc;
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h)
             if (ab_blk[h] < NBG)
-                store_pairs_range(smem, L.ab + ab_blk[h] * GS * 64, ab_pc[h], G, gbase, GS, aq[h],
+                store_pairs_range(smem, L.ab + ab_blk[h] * GS * 64, ab_pc[h], G, sa.inv_G, gbase, GS, aq[h],
                                   bq[h]);
     };
-    // Pair tables of the group with 16-byte writes.  Item it = (block b, half
-    // h, hi, slot quad q) writes slots 4q..4q+3 (rows 4(q%4)..+3) of the
-    // entries hi<<4 | lo, lo = 8h..8h+7; the 8 lanes of one entry write its
-    // 128 contiguous bytes, and the table values come from three LDS reads.
-    auto build_item = [&](int it, auto&& hook) {
-        const int q = it & 7;
-        const int hi = (it >> 3) & 15;
-        const int h = (it >> 7) & 1;
-        const int b = it >> 8;
+    // Pair tables of the group with 16-byte writes.  Item (block b, half h,
+    // hi, slot quad q) writes slots 4q..4q+3 (rows 4(q%4)..+3) of the entries
+    // hi<<4 | lo, lo = 8h..8h+7, and the table values come from three LDS
+    // reads.  Items are numbered it = b<<8 | h<<7 | hi<<3 | q (block-major:
+    // the 8 lanes of one entry write its 128 contiguous bytes) or, region-
+    // major, it = p<<9 | h<<8 | hi<<4 | (b&1)<<3 | q with p = b>>1 (the 16
+    // lanes of one entry write both tables of the region: 256 contiguous
+    // bytes, so one 16-byte write of a wave covers every LDS bank).
+    auto build_item = [&](int b, int h, int hi, int q, auto&& hook) {
         typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
         const uint32_t src = L.luts + b * 512 + (q & 3) * 128;
         // any4: entry hi<<4 | lo is (L[lo], L[hi]).  any3: the byte's low 6
@@ -2293,7 +2326,7 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
                 build_item2(it);
         } else if constexpr (!I4) {
             for (int it = tid; it < NBG * 256; it += NT)
-                build_item(it, [](int) {});
+                build_item(it >> 8, (it >> 7) & 1, (it >> 3) & 15, it & 7, [](int) {});
         }
     };
 
@@ -2370,16 +2403,22 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
     }
     stage_store(lq, aq, bq);
     stamp(2);
-    __syncthreads();
+    if (eb)
+        asm volatile("" ::: "memory");   // the wave reads back its own staging writes (in order)
+    else
+        __syncthreads();
     stamp(3);
     // the tables' 16-byte writes and the rest of the ring's loads, interleaved,
     // so that neither the LDS nor the texture unit waits for the other
     if (!I4 && !A2 && NT >= NBG * 256) {
         if (tid < NBG * 256) {   // uniform: NBG * 256 is a multiple of 64
-            build_item(tid, [&](int i) {
-                if (PRE + i < D)
-                    issue(0, PRE + i);
-            });
+            const bool rm = eb && RM;
+            build_item(rm ? 2 * (tid >> 9) + ((tid >> 3) & 1) : tid >> 8,
+                       rm ? (tid >> 8) & 1 : (tid >> 7) & 1, rm ? (tid >> 4) & 15 : (tid >> 3) & 15,
+                       tid & 7, [&](int i) {
+                           if (PRE + i < D)
+                               issue(0, PRE + i);
+                       });
 #pragma unroll
             for (int u = PRE + 8; u < D; ++u)
                 issue(0, u);
@@ -2868,6 +2907,30 @@ void st_go_r(const StArgs& sa, const StPlan& P, hipStream_t stream)
         st_go<MT, NBG, R, false, false, FMT>(sa, P, stream);
 }
 
+// The kernel arguments of a plan, with the launch constants worked out here
+StArgs st_args(const GemmArgs& a, const StPlan& P, unsigned long long* ts)
+{
+    StArgs sa;
+    sa.a = a;
+    sa.splits = P.splits;
+    sa.gstage = P.gstage;
+    sa.cw = P.cw;
+    sa.L = P.L;
+    sa.ts = ts;
+    const int NB = static_cast<int>(row_blocks(a.N));
+    const int Kc = a.K / TILE_K;
+    sa.G = a.K / a.g;
+    sa.gc = a.g / TILE_K;
+    sa.Gs = P.grid / P.splits;
+    sa.KcS = (Kc + P.splits - 1) / P.splits;
+    sa.nbmax = (NB + sa.Gs - 1) / sa.Gs;
+    for (int i = 0; i < 4; ++i)
+        sa.gbase[i] = i < P.splits ? i * sa.KcS / sa.gc : 0;
+    sa.inv_abper = 1.0f / static_cast<float>(2 * sa.G);
+    sa.inv_G = 1.0f / static_cast<float>(sa.G);
+    return sa;
+}
+
 // The M = 1 product with v_dot2_f32_bf16 instead of the matrix cores (same
 // decode, ring and staging); kept to compare the two.
 bool launch_st_dot(const GemmArgs& a, hipStream_t stream)
@@ -2875,7 +2938,7 @@ bool launch_st_dot(const GemmArgs& a, hipStream_t stream)
     StPlan P;
     if (a.M != 1 || !st_plan(1, a.N, a.K, a.g, false, P) || !P.xl || P.mg)
         return false;
-    StArgs sa{a, P.splits, P.gstage, P.cw, P.L, nullptr};
+    const StArgs sa = st_args(a, P, nullptr);
     const dim3 gd(P.grid), bd(64 * P.nw);
 #define ST_DOT(NBG_, R_)                                                                          \
     hipLaunchKernelGGL((k_gemm_st<1, NBG_, R_, true, false, 1024, ANY4_ST_PRE,                    \
@@ -2903,7 +2966,7 @@ bool launch_st(const GemmArgs& a, hipStream_t stream, unsigned long long* ts)
     StPlan P;
     if (!st_plan(a.M, a.N, a.K, a.g, a.ws != nullptr, P))
         return false;
-    StArgs sa{a, P.splits, P.gstage, P.cw, P.L, ts};
+    const StArgs sa = st_args(a, P, ts);
     if constexpr (MT > 16) {
         // wide batches: one group, x in the ring, bodies of one or two steps
         if (P.mg || P.xl || P.splits > 1)
