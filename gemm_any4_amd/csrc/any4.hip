@@ -2195,12 +2195,16 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
     // ---- staging of group gi.  Table rows: thread t < 32*NBG fetches 16 B
     // (8 entries of row (t%32)/2) of block t/32.  alpha/beta: item q = t + h*NT
     // (h < 2) is piece q % 2G of block q / 2G, 16 B of each tensor.
+    // The prologue's per-lane arithmetic runs four waves to a SIMD before the
+    // first loads go out, so waves with no live item skip it (uniform tests).
     const int ab_per = 2 * G;
     int ab_blk[2], ab_pc[2];
+    bool ab_wave[2];   // the wave holds live alpha/beta items in round h
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+        ab_wave[h] = wave * 64 + h * NT < NBG * ab_per;
         const int q = tid + h * NT;
-        ab_blk[h] = small_div(q, sa.inv_abper);   // q < 2048
+        ab_blk[h] = ab_wave[h] ? small_div(q, sa.inv_abper) : NBG;   // q < 2048
         ab_pc[h] = q - ab_blk[h] * ab_per;
     }
     // Early build (one group, pair tables, a build item per thread): the
@@ -2215,13 +2219,17 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
     constexpr bool RM = NBG % 2 == 0;   // region-major build items
     const bool eb = EBC && NT >= NBG * 256;
     const bool lut_lane = eb ? tid < NBG * 256 && (RM || lane < 32) : tid < 32 * NBG;
-    // block of the lane's staged rows
-    const int lut_blk = eb ? (RM ? 2 * (tid >> 9) + (lane >> 5) : tid >> 8) : tid >> 5;
+    // block of the lane's staged rows: the wave's first (uniform), plus one
+    // for lanes 32-63 where a wave stages two blocks
+    const int lut_wb = eb ? (RM ? 2 * (wave >> 3) : wave >> 2) : 2 * wave;
+    const int lut_hb = (!eb || RM) && lane >= 32 ? 1 : 0;
+    const int lut_blk = lut_wb + lut_hb;
     auto stage_load = [&](int gi, u32x4_t& lq, u32x4_t (&aq)[2], u32x4_t (&bq)[2]) {
         {
             const int blk = gi * NBG + lut_blk;
             const bool live = lut_lane && blk < nblk;
-            const uint32_t o = (static_cast<uint32_t>(r + blk * Gs) * 512 + (tid & 31) * 16) |
+            const uint32_t base = static_cast<uint32_t>(r + (gi * NBG + lut_wb) * Gs) * 512;   // uniform
+            const uint32_t o = (base + (lut_hb ? static_cast<uint32_t>(Gs) * 512 : 0u) + (tid & 31) * 16) |
                                (static_cast<uint32_t>(!live) << 31);
             if constexpr (I4)
                 lq = u32x4_t{0u, 0u, 0u, 0u};
@@ -2230,12 +2238,17 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+            aq[h] = bq[h] = u32x4_t{0u, 0u, 0u, 0u};
+            if (!ab_wave[h])
+                break;   // uniform; the later rounds hold no live item either
             const int blk = gi * NBG + ab_blk[h];
             // the piece's 8 values are groups g0..g0+7 (mod G) of its rows:
             // loaded only if one of them is staged
-            const int g0 = 8 * ab_pc[h] - G * small_div(8 * ab_pc[h], sa.inv_G);   // (8 pc) mod G
-            const bool need = G <= GS || (g0 + 7 >= gbase && g0 < gbase + GS) ||
-                              (g0 + 7 >= G && (g0 + 7 - G) >= gbase);
+            bool need = true;
+            if (G > GS) {
+                const int g0 = 8 * ab_pc[h] - G * small_div(8 * ab_pc[h], sa.inv_G);   // (8 pc) mod G
+                need = (g0 + 7 >= gbase && g0 < gbase + GS) || (g0 + 7 >= G && (g0 + 7 - G) >= gbase);
+            }
             const bool live = ab_blk[h] < NBG && blk < nblk && need;
             const uint32_t o = (static_cast<uint32_t>(r + blk * Gs) * (G * 32) + ab_pc[h] * 16) |
                                (static_cast<uint32_t>(!live) << 31);
@@ -2261,7 +2274,7 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-            if (ab_blk[h] < NBG)
+            if (ab_wave[h] && ab_blk[h] < NBG)
                 store_pairs_range(smem, L.ab + ab_blk[h] * GS * 64, ab_pc[h], G, sa.inv_G, gbase, GS, aq[h],
                                   bq[h]);
     };
@@ -2378,11 +2391,14 @@ __global__ __launch_bounds__(LB) void k_gemm_st(const StArgs sa)
     stage_load(0, lq, aq, bq);
     u32x4_t xc16[XL ? ST_XP : 1];
     const uint32_t xbytes = static_cast<uint32_t>(M) * K * 2;
+    // the waves past x load nothing (uniform test)
     if constexpr (XL) {
 #pragma unroll
         for (int i = 0; i < ST_XP; ++i) {
             const uint32_t o = static_cast<uint32_t>(tid + i * NT) * 16;
-            xc16[i] = load16(rx, o < xbytes ? o : OOR);
+            xc16[i] = u32x4_t{0u, 0u, 0u, 0u};
+            if (static_cast<uint32_t>(wave * 64 + i * NT) * 16 < xbytes)
+                xc16[i] = load16(rx, o < xbytes ? o : OOR);
         }
     }
 #pragma unroll
