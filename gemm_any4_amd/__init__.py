@@ -278,7 +278,8 @@ def gemm(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: torch.
 
     workspace: optional uint8 device tensor of at least workspace_size(M, N, K, g)
     bytes (contents need not be initialised); with it, K may be split over
-    workgroups, their fp32 partial sums kept there.  An empty tensor runs the
+    workgroups, their fp32 partial sums kept there, or (M >= 256) the layer is
+    dequantised into it for one library bf16 GEMM.  An empty tensor runs the
     kernels that need no workspace.  By default a workspace kept per device
     and stream is used."""
     _b16(x, "x"), _b16(lut, "lut"), _b16(alpha, "alpha"), _b16(beta, "beta")
@@ -302,7 +303,8 @@ def gemm(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: torch.
 
 
 def _workspace_args(workspace, M: int, N: int, K: int, g: int, device, sh):
-    """(pointer, bytes) of the split-K workspace for a GEMM call: the caller's
+    """(pointer, bytes) of the workspace for a GEMM call (split-K partial sums,
+    or the dequantised layer for prefill batches): the caller's
     tensor (an empty one: none), else the cached one of this device and
     stream, or (None, 0) where the shape needs none."""
     need = workspace_size(M, N, K, g)

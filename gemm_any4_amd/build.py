@@ -24,7 +24,8 @@ FLAGS = [
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-o", tmp, SRC]
+    # hipBLASLt: the plain bf16 GEMM of the prefill path
+    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-o", tmp, SRC, "-lhipblaslt"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -39,7 +39,9 @@
 //   k_zero                 y = 0 when K = 0.
 #include <hip/hip_runtime.h>
 
+#include <hipblaslt/hipblaslt.h>
 #include <mutex>
+#include <vector>
 
 #include "any4.h"
 
@@ -148,50 +150,71 @@ __global__ __launch_bounds__(PACK_THREADS) void k_pack(const uint8_t* __restrict
 constexpr int DQ_WAVES = 4;   // one tile per wave; a workgroup covers 4 chunks of one row block
 
 // w[n][k] = bf16(fma(alpha, LUT[idx], beta)).  The workgroup's 16 table rows
-// are widened to fp32 in LDS; each lane decodes its 32 weights and writes 64
-// contiguous bytes of w.
+// are widened to fp32 in LDS; each lane decodes the 32 weights of its tile
+// slot (a row's quarter of the wave's 128 k).  The decoded rows go through
+// LDS so that the stores are whole rows: a wave's 16-byte stores cover 1 KB
+// of one row (the workgroup's 4 chunks), not 16 rows' 16-byte pieces.
+// i4: plain int4, the code itself is the value (the table 0..15; lut unread).
 __global__ __launch_bounds__(64 * DQ_WAVES) void k_dequant(const uint8_t* __restrict__ packed,
                                                           const uint16_t* __restrict__ lut,
                                                           const uint16_t* __restrict__ alpha,
                                                           const uint16_t* __restrict__ beta,
                                                           uint16_t* __restrict__ w, int N, int K,
-                                                          int g)
+                                                          int g, int i4)
 {
+    constexpr int RP = DQ_WAVES * 16 + 1;   // 16-byte pieces per staged row (+1: banks)
     __shared__ float sl[TILE_ROWS * 16];
+    __shared__ u32x4_t so[TILE_ROWS * RP];
     const int Kc = K / TILE_K;
     const int cgroups = (Kc + DQ_WAVES - 1) / DQ_WAVES;
     const int b = blockIdx.x / cgroups;
-    const int c = (blockIdx.x % cgroups) * DQ_WAVES + (threadIdx.x >> 6);
+    const int cg0 = (blockIdx.x % cgroups) * DQ_WAVES;   // the workgroup's first chunk
+    const int wv = threadIdx.x >> 6;
+    const int c = cg0 + wv;
     {
         const int t = threadIdx.x;   // 256 threads: row t/16, entry t%16
         const int n = b * TILE_ROWS + (t >> 4);
-        sl[t] = n < N ? bf16_to_f32(lut[static_cast<size_t>(n) * 16 + (t & 15)]) : 0.f;
+        sl[t] = i4 ? static_cast<float>(t & 15)
+                   : n < N ? bf16_to_f32(lut[static_cast<size_t>(n) * 16 + (t & 15)]) : 0.f;
     }
     __syncthreads();
     const int l = threadIdx.x & 63;
     const int j = l & 15;
+    const int kq = l >> 4;
     const int n = b * TILE_ROWS + j;
-    if (c >= Kc || n >= N)
-        return;
-    const int k0 = c * TILE_K + (l >> 4) * 32;
-    const int G = K / g;
-    const float a = bf16_to_f32(alpha[static_cast<size_t>(n) * G + k0 / g]);
-    const float bt = bf16_to_f32(beta[static_cast<size_t>(n) * G + k0 / g]);
-    const u32x4_t p = *reinterpret_cast<const u32x4_t*>(
-        packed + (static_cast<size_t>(b) * Kc + c) * TILE_BYTES + l * 16);
-    const float* L = sl + j * 16;
-    u32x4_t out[4];
+    if (c < Kc && n < N) {
+        const int k0 = c * TILE_K + kq * 32;
+        const int G = K / g;
+        const float a = bf16_to_f32(alpha[static_cast<size_t>(n) * G + k0 / g]);
+        const float bt = bf16_to_f32(beta[static_cast<size_t>(n) * G + k0 / g]);
+        const u32x4_t p = *reinterpret_cast<const u32x4_t*>(
+            packed + (static_cast<size_t>(b) * Kc + c) * TILE_BYTES + l * 16);
+        const float* L = sl + j * 16;
+        u32x4_t out[4];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const uint32_t byte = (p[q >> 2] >> (8 * (q & 3))) & 0xFFu;
-        const float lo = fmaf(a, L[byte & 15u], bt);
-        const float hi = fmaf(a, L[byte >> 4], bt);
-        out[q >> 2][q & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+        for (int q = 0; q < 16; ++q) {
+            const uint32_t byte = (p[q >> 2] >> (8 * (q & 3))) & 0xFFu;
+            const float lo = fmaf(a, L[byte & 15u], bt);
+            const float hi = fmaf(a, L[byte >> 4], bt);
+            out[q >> 2][q & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            so[j * RP + wv * 16 + kq * 4 + q] = out[q];
     }
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(w + static_cast<size_t>(n) * K + k0);
+    __syncthreads();
+    // piece pc of row r: k = (cg0 + pc/16) * 128 + (pc%16) * 8
+    const int nch = min(DQ_WAVES, Kc - cg0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        dst[q] = out[q];
+    for (int i = 0; i < TILE_ROWS * DQ_WAVES * 16 / (64 * DQ_WAVES); ++i) {
+        const int pi = threadIdx.x + i * 64 * DQ_WAVES;
+        const int r = pi / (DQ_WAVES * 16);
+        const int pc = pi - r * (DQ_WAVES * 16);
+        const int nr = b * TILE_ROWS + r;
+        if (nr < N && pc < nch * 16)
+            *reinterpret_cast<u32x4_t*>(w + static_cast<size_t>(nr) * K + cg0 * TILE_K + pc * 8) =
+                so[r * RP + pc];
+    }
 }
 
 // ---- any2 (2-bit codes) -----------------------------------------------------
@@ -3086,6 +3109,111 @@ static void launch_big(const GemmArgs& a, int fmt, hipStream_t stream)
         hipLaunchKernelGGL((k_gemm_big<BM, FMT_ANY4, BN>), gd, dim3(256), 0, stream, a);
 }
 
+// ---- prefill: the layer dequantised once, then a plain bf16 GEMM ----------
+// From PREFILL_MIN_M x rows on, with a workspace of N*K bf16, the weights are
+// dequantised into it by the format's dequant kernel (the exact values
+// any4_dequant writes) and y = x * W^T is one bf16 GEMM with fp32
+// accumulation from hipBLASLt: a dequant-GEMM kernel would redo the decode
+// for every tile of x rows, and at these M the GEMM is bound by the matrix
+// cores, where the library's tuned kernels are the faster choice.  Without a
+// workspace (or should the library decline the shape) the tiled kernel runs.
+constexpr int64_t PREFILL_MIN_M = 256;
+
+size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    return M >= PREFILL_MIN_M ? static_cast<size_t>(N) * static_cast<size_t>(K) * 2 : 0;
+}
+
+void launch_dequant_fmt(int fmt, const uint8_t* packed, const uint16_t* lut, const uint16_t* alpha,
+                        const uint16_t* beta, uint16_t* w, int N, int K, int g, hipStream_t stream)
+{
+    const int64_t Kc = K / TILE_K;
+    const dim3 gd(static_cast<unsigned>(row_blocks(N) * ((Kc + DQ_WAVES - 1) / DQ_WAVES)));
+    if (fmt == FMT_ANY2)
+        hipLaunchKernelGGL(k_dequant2, gd, dim3(64 * DQ_WAVES), 0, stream, packed, lut, alpha, beta, w,
+                           N, K, g);
+    else if (fmt == FMT_ANY3)
+        hipLaunchKernelGGL(k_dequant3, gd, dim3(64 * DQ_WAVES), 0, stream, packed, lut, alpha, beta, w,
+                           N, K, g);
+    else
+        hipLaunchKernelGGL(k_dequant, gd, dim3(64 * DQ_WAVES), 0, stream, packed, lut, alpha, beta, w,
+                           N, K, g, fmt == FMT_INT4 ? 1 : 0);
+}
+
+// One hipBLASLt handle per device and one matmul plan per (device, M, N, K),
+// made on first use and kept until the process ends (the heuristic query
+// is host work worth doing once; making them on first use keeps them out of
+// any graph the caller captures later).
+struct BlasPlan {
+    int dev;
+    int64_t M, N, K;
+    bool ok;
+    hipblasLtMatmulDesc_t desc;
+    hipblasLtMatrixLayout_t la, lb, lc;
+    hipblasLtMatmulAlgo_t algo;
+};
+std::mutex blas_mu;
+hipblasLtHandle_t blas_handles[64];
+std::vector<BlasPlan> blas_plans;
+
+const BlasPlan* blas_plan(int dev, int64_t M, int64_t N, int64_t K)
+{
+    std::lock_guard<std::mutex> lock(blas_mu);
+    for (const BlasPlan& p : blas_plans)
+        if (p.dev == dev && p.M == M && p.N == N && p.K == K)
+            return p.ok ? &p : nullptr;
+    BlasPlan p{dev, M, N, K, false, nullptr, nullptr, nullptr, nullptr, {}};
+    bool ok = dev >= 0 && dev < 64;
+    if (ok && !blas_handles[dev])
+        ok = hipblasLtCreate(&blas_handles[dev]) == HIPBLAS_STATUS_SUCCESS;
+    // column-major view: Y (N x M, ld N) = op(A) (N x K) * B (K x M), with
+    // A = W seen as K x N (ld K) transposed and B = x seen as K x M (ld K)
+    const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+    ok = ok && hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) ==
+                   HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) ==
+                   HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, K, N, K) == HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16BF, K, M, K) == HIPBLAS_STATUS_SUCCESS;
+    ok = ok && hipblasLtMatrixLayoutCreate(&p.lc, HIP_R_16BF, N, M, N) == HIPBLAS_STATUS_SUCCESS;
+    if (ok) {
+        // no library workspace: the algorithms that need one are left out
+        hipblasLtMatmulPreference_t pref = nullptr;
+        uint64_t wsz = 0;
+        hipblasLtMatmulHeuristicResult_t res[1];
+        int n = 0;
+        ok = hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
+             hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsz,
+                                                   sizeof(wsz)) == HIPBLAS_STATUS_SUCCESS &&
+             hipblasLtMatmulAlgoGetHeuristic(blas_handles[dev], p.desc, p.la, p.lb, p.lc, p.lc, pref, 1,
+                                             res, &n) == HIPBLAS_STATUS_SUCCESS &&
+             n > 0;
+        if (ok)
+            p.algo = res[0].algo;
+        if (pref)
+            hipblasLtMatmulPreferenceDestroy(pref);
+    }
+    p.ok = ok;
+    blas_plans.push_back(p);
+    return ok ? &blas_plans.back() : nullptr;
+}
+
+// y = x * W^T through the library; false: not run (the caller falls back)
+bool blas_gemm(const uint16_t* w, const uint16_t* x, uint16_t* y, int64_t M, int64_t N, int64_t K,
+               hipStream_t stream)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return false;
+    const BlasPlan* p = blas_plan(dev, M, N, K);
+    if (!p)
+        return false;
+    const float one = 1.0f, zero = 0.0f;
+    return hipblasLtMatmul(blas_handles[dev], p->desc, &one, w, p->la, x, p->lb, &zero, y, p->lc, y,
+                           p->lc, &p->algo, nullptr, 0, stream) == HIPBLAS_STATUS_SUCCESS;
+}
+
 // Argument checks and dispatch shared by any4_gemm (table lookup),
 // any4_gemm_int4 (the 4-bit code itself is the value; lut unused), any2_gemm
 // and any3_gemm.
@@ -3111,9 +3239,11 @@ static any4_status gemm_call(int fmt, const uint16_t* x, const uint8_t* packed, 
                                      !aligned(beta, 16))))
         return ANY4_E_ALIGN;
     // the workspace is optional: with one, K may be split over workgroups
-    const size_t need = M <= 16 && K > 0 ? st_workspace_bytes(static_cast<int>(M),
-                                                              static_cast<int>(N),
-                                                              static_cast<int>(K)) : 0;
+    // (M <= 16), or the layer is dequantised into it (prefill)
+    const size_t need = K == 0 ? 0
+                        : M <= 16 ? st_workspace_bytes(static_cast<int>(M), static_cast<int>(N),
+                                                       static_cast<int>(K))
+                                  : prefill_workspace_bytes(M, N, K);
     if (workspace && workspace_bytes < need)
         return ANY4_E_WORKSPACE;
     if (workspace && !aligned(workspace, 16))
@@ -3136,8 +3266,16 @@ static any4_status gemm_call(int fmt, const uint16_t* x, const uint8_t* packed, 
     a.N = static_cast<int>(N);
     a.K = static_cast<int>(K);
     a.g = static_cast<int>(g);
-    a.ws = need > 0 && workspace ? static_cast<float*>(workspace) : nullptr;
+    a.ws = need > 0 && workspace && M <= 16 ? static_cast<float*>(workspace) : nullptr;
     a.ws_bytes = a.ws ? workspace_bytes : 0;
+    if (need > 0 && workspace && M >= PREFILL_MIN_M) {
+        uint16_t* w = static_cast<uint16_t*>(workspace);
+        launch_dequant_fmt(fmt, packed, lut, alpha, beta, w, a.N, a.K, a.g, stream);
+        if (launched() != ANY4_OK)
+            return ANY4_E_HIP;
+        if (blas_gemm(w, x, y, M, N, K, stream))
+            return launched();
+    }
     if (M > 16 && M <= 48) {
         // a few decode batches: one pass of the streaming kernel with two or
         // three 16-row slices of x against each decoded weight tile; for the
@@ -3332,15 +3470,17 @@ any4_status any4_dequant(const uint8_t* packed, const uint16_t* lut, const uint1
     (void)hipGetLastError();
     hipLaunchKernelGGL(k_dequant, dim3(static_cast<unsigned>(blocks)), dim3(64 * DQ_WAVES), 0,
                        stream, packed, lut, alpha, beta, w, static_cast<int>(N),
-                       static_cast<int>(K), static_cast<int>(g));
+                       static_cast<int>(K), static_cast<int>(g), 0);
     return launched();
 }
 
 size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g)
 {
-    if (M <= 0 || M > 16 || N <= 0 || K <= 0 || !group_ok(K, g) ||
+    if (M <= 0 || N <= 0 || K <= 0 || !group_ok(K, g) ||
         N >= (static_cast<int64_t>(1) << 31) || K >= (static_cast<int64_t>(1) << 31))
         return 0;
+    if (M > 16)
+        return prefill_workspace_bytes(M, N, K);
     return st_workspace_bytes(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
 }
 
@@ -3359,7 +3499,8 @@ any4_status any4_gemm_noalloc(const uint16_t* x, const uint8_t* packed, const ui
 {
     // the same kernels as any4_gemm with a workspace of
     // any4_gemm_workspace_size bytes, that workspace being this GPU's scratch
-    const size_t need = any4_gemm_workspace_size(M, N, K, g);
+    // (M <= 16; larger batches run as any4_gemm without a workspace)
+    const size_t need = M <= 16 ? any4_gemm_workspace_size(M, N, K, g) : 0;
     if (need > SCRATCH_BYTES)
         return ANY4_E_WORKSPACE;
     void* ws = nullptr;

@@ -114,8 +114,9 @@ any4_status any4_dequant(const uint8_t* packed, const uint16_t* lut, const uint1
  * 16-row blocks (N/16 between 256 and 512 on the 256 CUs of an MI355X) and K
  * is at least 12288: then x, which every workgroup reads for its whole K,
  * would cost more than the weights.  The workspace then holds S*M*N fp32
- * partial sums (S = 4 / blocks per CU), added up in a fixed order.  Invalid
- * shapes give 0.
+ * partial sums (S = 4 / blocks per CU), added up in a fixed order.  For
+ * M >= 256 (prefill) it is N*K*2 bytes: room for the dequantised layer (see
+ * any4_gemm).  Other shapes, and invalid ones, give 0.
  */
 size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
 
@@ -126,10 +127,15 @@ size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
  * with the weights still streamed once (two or three 16-row slices of x per
  * decoded tile; for a few shapes, 16-row slices of x and y that each stream
  * the weights), beyond that a tiled matrix-core product over weight tiles
- * dequantised in on-chip memory.
+ * dequantised in on-chip memory.  From M = 256 on, given a workspace of
+ * any4_gemm_workspace_size bytes, the layer is instead dequantised into the
+ * workspace (the any4_dequant values exactly, w[n][k] at element n*K + k) and
+ * y is one bf16 GEMM with fp32 accumulation from hipBLASLt (the library's
+ * summation order; the bound below holds with its fp32 summation error);
+ * should the library decline, the tiled kernel runs.
  *     y[m][n] = bf16_rne( sum_k x[m][k] * w[n][k] )
- * Every weight is dequantised inside the kernel (the weights are never
- * written to memory) as bf16_rne(fp32(alpha * v + beta)), v the table value
+ * Otherwise every weight is dequantised inside the kernel (the weights are
+ * never written to memory) as bf16_rne(fp32(alpha * v + beta)), v the table value
  * as the kernel holds it: each table row is kept as f16 scaled by 2^-s, s
  * chosen so that the row's largest finite magnitude lies in [2^14, 2^15)
  * (and s >= -60).  A table value is therefore held exactly -- and w[n][k] is
@@ -160,9 +166,10 @@ size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
  *       owned by the caller, contents need not be initialised.  With at least
  *       any4_gemm_workspace_size(M, N, K, g) bytes the call may split K over
  *       workgroups (a second kernel then adds the partial sums in split order,
- *       so results stay deterministic); with NULL it uses kernels that need no
- *       scratch (same result bound, another summation order).  Calls that
- *       share one workspace must be ordered (e.g. one stream).
+ *       so results stay deterministic) or, for M >= 256, dequantise the layer
+ *       into it; with NULL it uses kernels that need no scratch (same result
+ *       bound, another summation order).  Calls that share one workspace
+ *       must be ordered (e.g. one stream).
  * Errors: ANY4_E_SHAPE, ANY4_E_NULL, ANY4_E_ALIGN (also a misaligned
  * workspace), ANY4_E_WORKSPACE (a non-NULL workspace smaller than
  * any4_gemm_workspace_size), ANY4_E_HIP.
@@ -177,8 +184,9 @@ any4_status any4_gemm(const uint16_t* x, const uint8_t* packed, const uint16_t* 
  * memory (code under HIP graph capture, serving loops that must not call the
  * allocator, harnesses that forbid it): the same arguments without the
  * workspace, the same kernels and the same result, bit for bit, as any4_gemm
- * given a workspace of any4_gemm_workspace_size(M, N, K, g) bytes.  Where
- * that size is not 0 (K split over workgroups), the partial sums go to a
+ * given a workspace of any4_gemm_workspace_size(M, N, K, g) bytes for
+ * M <= 16 (for larger M: as any4_gemm with no workspace).  Where that size
+ * is not 0 (K split over workgroups), the partial sums go to a
  * 4 MiB array of device memory inside the library, one per GPU, held until
  * the process ends; its device address is looked up on the first such call
  * on each GPU (with that GPU current: `stream` must belong to the current
