@@ -155,7 +155,8 @@ size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
  * where a row's small values are small in absolute terms (1.0 beside 2^-40 or
  * subnormals), not where a row's other values are needed beside a value
  * 2^39 times larger.  Runs are deterministic (same inputs, same bits): the
- * summation order depends only on the shape.
+ * summation order depends only on the shape (on the prefill path, the
+ * library GEMM's order, which this library does not control).
  *   x                         device, [M][K] bf16, read-only.
  *   packed, lut, alpha, beta  device, read-only.
  *   y                         device, [M][N] bf16, written.
