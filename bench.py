@@ -329,7 +329,7 @@ def decoder_layer(torch, any4, workloads, steps: int) -> dict:
 
 def prefill(torch, any4, workloads, Ms) -> dict:
     """µs and TFLOP/s of any4_gemm at prefill batches M > 16 on the up/gate
-    layer (the tiled MFMA kernel below 256 rows; from 256 on the layer
+    layer (the tiled MFMA kernel below 128 rows; from 128 on the layer
     dequantised into the workspace, then one library bf16 GEMM), graph-timed
     over rotating weight sets."""
     import numpy as np
@@ -719,7 +719,7 @@ def main() -> int:
         progress("gemv")
         out["wide_batch"] = wide_batch(torch, any4, workloads, (24, 32, 48))
         progress("wide batch")
-        out["prefill"] = prefill(torch, any4, workloads, (64, 256, 512, 1024))
+        out["prefill"] = prefill(torch, any4, workloads, (64, 128, 256, 512, 1024))
         progress("prefill")
         out["decoder_layer_70b"] = decoder_layer(torch, any4, workloads, min(K, 50))
         progress("70B decoder layer")

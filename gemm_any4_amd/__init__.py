@@ -278,7 +278,7 @@ def gemm(x: torch.Tensor, packed: torch.Tensor, lut: torch.Tensor, alpha: torch.
 
     workspace: optional uint8 device tensor of at least workspace_size(M, N, K, g)
     bytes (contents need not be initialised); with it, K may be split over
-    workgroups, their fp32 partial sums kept there, or (M >= 256) the layer is
+    workgroups, their fp32 partial sums kept there, or (M >= 128) the layer is
     dequantised into it for one library bf16 GEMM.  An empty tensor runs the
     kernels that need no workspace.  By default a workspace kept per device
     and stream is used."""

@@ -41,7 +41,7 @@
 
 #include <hipblaslt/hipblaslt.h>
 #include <mutex>
-#include <vector>
+#include <deque>
 
 #include "any4.h"
 
@@ -149,6 +149,36 @@ __global__ __launch_bounds__(PACK_THREADS) void k_pack(const uint8_t* __restrict
 // ---------------------------------------------------------------------------
 constexpr int DQ_WAVES = 4;   // one tile per wave; a workgroup covers 4 chunks of one row block
 
+// The decoded weights of a dequant workgroup (16 rows x DQ_WAVES chunks; the
+// lane's 32 of row j, k-quarter kq of chunk wave wv, in out) go through LDS
+// and are stored as whole rows: a wave's 16-byte stores then cover 1 KB of
+// one row instead of 16 rows' 16-byte pieces.  Called by every thread (it
+// holds a barrier); `live`: the lane decoded something.
+constexpr int DQ_RP = DQ_WAVES * 16 + 1;   // 16-byte pieces per staged row (+1: banks)
+__device__ __forceinline__ void dq_store_rows(u32x4_t* so, const u32x4_t (&out)[4], bool live,
+                                              int wv, int j, int kq, int b, int cg0, int Kc,
+                                              int N, int K, uint16_t* __restrict__ w)
+{
+    if (live) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            so[j * DQ_RP + wv * 16 + kq * 4 + q] = out[q];
+    }
+    __syncthreads();
+    // piece pc of row r: k = (cg0 + pc/16) * 128 + (pc%16) * 8
+    const int nch = min(DQ_WAVES, Kc - cg0);
+#pragma unroll
+    for (int i = 0; i < TILE_ROWS * 16 / 64; ++i) {
+        const int pi = threadIdx.x + i * 64 * DQ_WAVES;
+        const int r = pi / (DQ_WAVES * 16);
+        const int pc = pi - r * (DQ_WAVES * 16);
+        const int nr = b * TILE_ROWS + r;
+        if (nr < N && pc < nch * 16)
+            *reinterpret_cast<u32x4_t*>(w + static_cast<size_t>(nr) * K + cg0 * TILE_K + pc * 8) =
+                so[r * DQ_RP + pc];
+    }
+}
+
 // w[n][k] = bf16(fma(alpha, LUT[idx], beta)).  The workgroup's 16 table rows
 // are widened to fp32 in LDS; each lane decodes the 32 weights of its tile
 // slot (a row's quarter of the wave's 128 k).  The decoded rows go through
@@ -162,9 +192,8 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void k_dequant(const uint8_t* __rest
                                                           uint16_t* __restrict__ w, int N, int K,
                                                           int g, int i4)
 {
-    constexpr int RP = DQ_WAVES * 16 + 1;   // 16-byte pieces per staged row (+1: banks)
     __shared__ float sl[TILE_ROWS * 16];
-    __shared__ u32x4_t so[TILE_ROWS * RP];
+    __shared__ u32x4_t so[TILE_ROWS * DQ_RP];
     const int Kc = K / TILE_K;
     const int cgroups = (Kc + DQ_WAVES - 1) / DQ_WAVES;
     const int b = blockIdx.x / cgroups;
@@ -182,7 +211,9 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void k_dequant(const uint8_t* __rest
     const int j = l & 15;
     const int kq = l >> 4;
     const int n = b * TILE_ROWS + j;
-    if (c < Kc && n < N) {
+    const bool live = c < Kc && n < N;
+    u32x4_t out[4];
+    if (live) {
         const int k0 = c * TILE_K + kq * 32;
         const int G = K / g;
         const float a = bf16_to_f32(alpha[static_cast<size_t>(n) * G + k0 / g]);
@@ -190,7 +221,6 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void k_dequant(const uint8_t* __rest
         const u32x4_t p = *reinterpret_cast<const u32x4_t*>(
             packed + (static_cast<size_t>(b) * Kc + c) * TILE_BYTES + l * 16);
         const float* L = sl + j * 16;
-        u32x4_t out[4];
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const uint32_t byte = (p[q >> 2] >> (8 * (q & 3))) & 0xFFu;
@@ -198,23 +228,8 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void k_dequant(const uint8_t* __rest
             const float hi = fmaf(a, L[byte >> 4], bt);
             out[q >> 2][q & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            so[j * RP + wv * 16 + kq * 4 + q] = out[q];
     }
-    __syncthreads();
-    // piece pc of row r: k = (cg0 + pc/16) * 128 + (pc%16) * 8
-    const int nch = min(DQ_WAVES, Kc - cg0);
-#pragma unroll
-    for (int i = 0; i < TILE_ROWS * DQ_WAVES * 16 / (64 * DQ_WAVES); ++i) {
-        const int pi = threadIdx.x + i * 64 * DQ_WAVES;
-        const int r = pi / (DQ_WAVES * 16);
-        const int pc = pi - r * (DQ_WAVES * 16);
-        const int nr = b * TILE_ROWS + r;
-        if (nr < N && pc < nch * 16)
-            *reinterpret_cast<u32x4_t*>(w + static_cast<size_t>(nr) * K + cg0 * TILE_K + pc * 8) =
-                so[r * RP + pc];
-    }
+    dq_store_rows(so, out, live, wv, j, kq, b, cg0, Kc, N, K, w);
 }
 
 // ---- any2 (2-bit codes) -----------------------------------------------------
@@ -263,10 +278,13 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void k_dequant2(const uint8_t* __res
                                                            int g)
 {
     __shared__ float sl[TILE_ROWS * 4];
+    __shared__ u32x4_t so[TILE_ROWS * DQ_RP];
     const int Kc = K / TILE_K;
     const int cgroups = (Kc + DQ_WAVES - 1) / DQ_WAVES;
     const int b = blockIdx.x / cgroups;
-    const int c = (blockIdx.x % cgroups) * DQ_WAVES + (threadIdx.x >> 6);
+    const int cg0 = (blockIdx.x % cgroups) * DQ_WAVES;
+    const int wv = threadIdx.x >> 6;
+    const int c = cg0 + wv;
     if (threadIdx.x < TILE_ROWS * 4) {   // row t/4, entry t%4
         const int t = threadIdx.x;
         const int n = b * TILE_ROWS + (t >> 2);
@@ -276,32 +294,30 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void k_dequant2(const uint8_t* __res
     const int l = threadIdx.x & 63;
     const int j = l & 15;
     const int n = b * TILE_ROWS + j;
-    if (c >= Kc || n >= N)
-        return;
-    const int k0 = c * TILE_K + (l >> 4) * 32;
-    const int G = K / g;
-    const float a = bf16_to_f32(alpha[static_cast<size_t>(n) * G + k0 / g]);
-    const float bt = bf16_to_f32(beta[static_cast<size_t>(n) * G + k0 / g]);
-    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-    const u32x2_t p = *reinterpret_cast<const u32x2_t*>(
-        packed + (static_cast<size_t>(b) * Kc + c) * (TILE_BYTES / 2) + l * 8);
-    const float* L = sl + j * 4;
+    const bool live = c < Kc && n < N;
     u32x4_t out[4];
+    if (live) {
+        const int k0 = c * TILE_K + (l >> 4) * 32;
+        const int G = K / g;
+        const float a = bf16_to_f32(alpha[static_cast<size_t>(n) * G + k0 / g]);
+        const float bt = bf16_to_f32(beta[static_cast<size_t>(n) * G + k0 / g]);
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t p = *reinterpret_cast<const u32x2_t*>(
+            packed + (static_cast<size_t>(b) * Kc + c) * (TILE_BYTES / 2) + l * 8);
+        const float* L = sl + j * 4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {   // byte i: codes 4i .. 4i+3
-        const uint32_t byte = (p[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+        for (int i = 0; i < 8; ++i) {   // byte i: codes 4i .. 4i+3
+            const uint32_t byte = (p[i >> 2] >> (8 * (i & 3))) & 0xFFu;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const float lo = fmaf(a, L[(byte >> (4 * t)) & 3u], bt);
-            const float hi = fmaf(a, L[(byte >> (4 * t + 2)) & 3u], bt);
-            const int d = 2 * i + t;
-            out[d >> 2][d & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+            for (int t = 0; t < 2; ++t) {
+                const float lo = fmaf(a, L[(byte >> (4 * t)) & 3u], bt);
+                const float hi = fmaf(a, L[(byte >> (4 * t + 2)) & 3u], bt);
+                const int d = 2 * i + t;
+                out[d >> 2][d & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+            }
         }
     }
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(w + static_cast<size_t>(n) * K + k0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        dst[q] = out[q];
+    dq_store_rows(so, out, live, wv, j, l >> 4, b, cg0, Kc, N, K, w);
 }
 
 // ---- any3 (3-bit codes) -----------------------------------------------------
@@ -379,10 +395,13 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void k_dequant3(const uint8_t* __res
                                                            int g)
 {
     __shared__ float sl[TILE_ROWS * 8];
+    __shared__ u32x4_t so[TILE_ROWS * DQ_RP];
     const int Kc = K / TILE_K;
     const int cgroups = (Kc + DQ_WAVES - 1) / DQ_WAVES;
     const int b = blockIdx.x / cgroups;
-    const int c = (blockIdx.x % cgroups) * DQ_WAVES + (threadIdx.x >> 6);
+    const int cg0 = (blockIdx.x % cgroups) * DQ_WAVES;
+    const int wv = threadIdx.x >> 6;
+    const int c = cg0 + wv;
     if (threadIdx.x < TILE_ROWS * 8) {   // row t/8, entry t%8
         const int t = threadIdx.x;
         const int n = b * TILE_ROWS + (t >> 3);
@@ -392,30 +411,28 @@ __global__ __launch_bounds__(64 * DQ_WAVES) void k_dequant3(const uint8_t* __res
     const int l = threadIdx.x & 63;
     const int j = l & 15;
     const int n = b * TILE_ROWS + j;
-    if (c >= Kc || n >= N)
-        return;
-    const int k0 = c * TILE_K + (l >> 4) * 32;
-    const int G = K / g;
-    const float a = bf16_to_f32(alpha[static_cast<size_t>(n) * G + k0 / g]);
-    const float bt = bf16_to_f32(beta[static_cast<size_t>(n) * G + k0 / g]);
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(
-        packed + (static_cast<size_t>(b) * Kc + c) * (TILE_BYTES * 3 / 4) + l * 12);
-    const u32x4_t p = {src[0], src[1], src[2], 0u};
-    const uint32_t top = any3_top_pairs(p);
-    const float* L = sl + j * 8;
+    const bool live = c < Kc && n < N;
     u32x4_t out[4];
+    if (live) {
+        const int k0 = c * TILE_K + (l >> 4) * 32;
+        const int G = K / g;
+        const float a = bf16_to_f32(alpha[static_cast<size_t>(n) * G + k0 / g]);
+        const float bt = bf16_to_f32(beta[static_cast<size_t>(n) * G + k0 / g]);
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(
+            packed + (static_cast<size_t>(b) * Kc + c) * (TILE_BYTES * 3 / 4) + l * 12);
+        const u32x4_t p = {src[0], src[1], src[2], 0u};
+        const uint32_t top = any3_top_pairs(p);
+        const float* L = sl + j * 8;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {   // pair i: codes 2i, 2i+1
-        const uint32_t d = i < 12 ? p[i >> 2] : top;
-        const uint32_t P = (d >> (8 * (i & 3))) & 0x3Fu;
-        const float lo = fmaf(a, L[P & 7u], bt);
-        const float hi = fmaf(a, L[P >> 3], bt);
-        out[i >> 2][i & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+        for (int i = 0; i < 16; ++i) {   // pair i: codes 2i, 2i+1
+            const uint32_t d = i < 12 ? p[i >> 2] : top;
+            const uint32_t P = (d >> (8 * (i & 3))) & 0x3Fu;
+            const float lo = fmaf(a, L[P & 7u], bt);
+            const float hi = fmaf(a, L[P >> 3], bt);
+            out[i >> 2][i & 3] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+        }
     }
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(w + static_cast<size_t>(n) * K + k0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        dst[q] = out[q];
+    dq_store_rows(so, out, live, wv, j, l >> 4, b, cg0, Kc, N, K, w);
 }
 
 // ---------------------------------------------------------------------------
@@ -3117,7 +3134,10 @@ static void launch_big(const GemmArgs& a, int fmt, hipStream_t stream)
 // for every tile of x rows, and at these M the GEMM is bound by the matrix
 // cores, where the library's tuned kernels are the faster choice.  Without a
 // workspace (or should the library decline the shape) the tiled kernel runs.
-constexpr int64_t PREFILL_MIN_M = 256;
+#ifndef ANY4_PREFILL_MIN_M
+#define ANY4_PREFILL_MIN_M 128
+#endif
+constexpr int64_t PREFILL_MIN_M = ANY4_PREFILL_MIN_M;
 
 size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
@@ -3154,7 +3174,7 @@ struct BlasPlan {
 };
 std::mutex blas_mu;
 hipblasLtHandle_t blas_handles[64];
-std::vector<BlasPlan> blas_plans;
+std::deque<BlasPlan> blas_plans;   // a deque: a plan stays put while others are added
 
 const BlasPlan* blas_plan(int dev, int64_t M, int64_t N, int64_t K)
 {

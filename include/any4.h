@@ -115,7 +115,7 @@ any4_status any4_dequant(const uint8_t* packed, const uint16_t* lut, const uint1
  * is at least 12288: then x, which every workgroup reads for its whole K,
  * would cost more than the weights.  The workspace then holds S*M*N fp32
  * partial sums (S = 4 / blocks per CU), added up in a fixed order.  For
- * M >= 256 (prefill) it is N*K*2 bytes: room for the dequantised layer (see
+ * M >= 128 (prefill) it is N*K*2 bytes: room for the dequantised layer (see
  * any4_gemm).  Other shapes, and invalid ones, give 0.
  */
 size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
@@ -127,7 +127,7 @@ size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
  * with the weights still streamed once (two or three 16-row slices of x per
  * decoded tile; for a few shapes, 16-row slices of x and y that each stream
  * the weights), beyond that a tiled matrix-core product over weight tiles
- * dequantised in on-chip memory.  From M = 256 on, given a workspace of
+ * dequantised in on-chip memory.  From M = 128 on, given a workspace of
  * any4_gemm_workspace_size bytes, the layer is instead dequantised into the
  * workspace (the any4_dequant values exactly, w[n][k] at element n*K + k) and
  * y is one bf16 GEMM with fp32 accumulation from hipBLASLt (the library's
@@ -167,7 +167,7 @@ size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
  *       owned by the caller, contents need not be initialised.  With at least
  *       any4_gemm_workspace_size(M, N, K, g) bytes the call may split K over
  *       workgroups (a second kernel then adds the partial sums in split order,
- *       so results stay deterministic) or, for M >= 256, dequantise the layer
+ *       so results stay deterministic) or, for M >= 128, dequantise the layer
  *       into it; with NULL it uses kernels that need no scratch (same result
  *       bound, another summation order).  Calls that share one workspace
  *       must be ordered (e.g. one stream).

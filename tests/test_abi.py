@@ -100,9 +100,9 @@ def test_workspace_size_is_defined_for_all_shapes():
     for M in (1, 2, 4, 8, 16):
         assert any4.workspace_size(M, 14336, 4096, 128) >= 0
     assert any4.workspace_size(17, 16, 128, 128) == 0
-    # prefill (M >= 256): the layer dequantised into the workspace, N*K bf16
-    assert any4.workspace_size(255, 14336, 4096, 128) == 0
-    assert any4.workspace_size(256, 14336, 4096, 128) == 14336 * 4096 * 2
+    # prefill (M >= 128): the layer dequantised into the workspace, N*K bf16
+    assert any4.workspace_size(127, 14336, 4096, 128) == 0
+    assert any4.workspace_size(128, 14336, 4096, 128) == 14336 * 4096 * 2
     assert any4.workspace_size(1024, 17, 384, 128) == 17 * 384 * 2
     assert any4.workspace_size(256, 17, 384, 96) == 0   # g not a multiple of 128
 

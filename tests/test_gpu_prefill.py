@@ -1,4 +1,4 @@
-"""GPU parity of the prefill path (M >= 256 with a workspace of N*K bf16): the
+"""GPU parity of the prefill path (M >= 128 with a workspace of N*K bf16): the
 layer is dequantised into the workspace by the format's dequant kernel, then
 multiplied by a library bf16 GEMM with fp32 accumulation.  Checked against
 the CPU oracle (every output), against the tiled kernel that runs without a
@@ -25,7 +25,7 @@ def _gpu():
     any4.lib()
 
 
-SHAPES = [(256, 300, 1024, 128), (257, 17, 128, 128), (300, 16 * 40 + 3, 768, 256),
+SHAPES = [(128, 200, 512, 128), (256, 300, 1024, 128), (257, 17, 128, 128), (300, 16 * 40 + 3, 768, 256),
           (512, 1000, 2048, 1024), (1024, 64, 384, 128)]
 
 
