@@ -2716,15 +2716,16 @@ bool launch_st(const GemmArgs& a, hipStream_t stream, unsigned long long* ts);
 bool st_disable = false;   // probe builds: time the older kernels
 #endif
 
-// k_gemm_st where it measured faster than k_gemm_km / k_gemm_kb:
-// up to four row blocks per workgroup (one group), with more than one block
-// or K past 4096.
+// k_gemm_st where it measured faster than k_gemm_km / k_gemm_kb: up to four
+// row blocks per workgroup (one group).  (One block with K <= 4096 went to
+// k_gemm_km until the streaming kernel's early table build: now 6.3 -> 6.0 us
+// on 4096x4096 at M = 1, 7.9 -> 6.3 us on 4096x2048 at M = 16.)
 bool use_st(const GemmArgs& a)
 {
     const int64_t NB = row_blocks(a.N);
     const int64_t grid = NB < KM_GRID ? NB : KM_GRID;
     const int64_t nb = grid > 0 ? (NB + grid - 1) / grid : 0;
-    return nb >= 1 && nb <= 4 && (nb >= 2 || a.K > KM_MAX_K);
+    return nb >= 1 && nb <= 4;
 }
 
 template <int MT, int FMT>
