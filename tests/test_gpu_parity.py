@@ -172,6 +172,25 @@ def test_gemm_ragged(M, N, K, g):
     gu.assert_within_bound(y, y_ref, ad, f"ragged {M}x{N}x{K} g{g}")
 
 
+# The streaming kernel's two prologue orders: with a build item per thread
+# (NBG * 256 threads or more) each wave stages its own blocks' table rows
+# (one block, or the two blocks of a table region); K of 33 chunks makes the
+# plan take fewer waves, so the first 32 * NBG threads stage every block and
+# the workgroup meets at a barrier before the build.  Both against the
+# oracle, at one, two and four blocks per group, M = 1 (x in LDS) and 16.
+@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("N,K", [(16 * 200 + 3, 4096), (16 * 500, 4096), (16 * 900 + 9, 4096),
+                                 (16 * 200 + 3, 33 * 128), (16 * 500, 33 * 128),
+                                 (16 * 900 + 9, 33 * 128)])
+def test_gemm_streaming_prologues(M, N, K):
+    inp = workloads.generic(M * 13 + N + K, M, N, K, 128)
+    L = gu.Layer(inp)
+    y = any4.gemm(L.x, L.packed, L.lut, L.alpha, L.beta, 128)
+    torch.cuda.synchronize()
+    y_ref, ad = oracle.gemm(inp.x, L.w_ref(), nthreads=oracle.default_threads())
+    gu.assert_within_bound(y, y_ref, ad, f"prologue {M}x{N}x{K}")
+
+
 # Large K (> 4096): x staged in LDS (M <= 2, x <= 56 KB) or carried with the
 # tiles; one or two row blocks decoded together, one or two groups of them.
 @pytest.mark.parametrize("M,N,K,g", [(1, 64, 16384, 128), (16, 100, 8192, 1024),
