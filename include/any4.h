@@ -132,7 +132,9 @@ size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
  * workspace (the any4_dequant values exactly, w[n][k] at element n*K + k) and
  * y is one bf16 GEMM with fp32 accumulation from hipBLASLt (the library's
  * summation order; the bound below holds with its fp32 summation error);
- * should the library decline, the tiled kernel runs.
+ * should the library decline, the tiled kernel runs.  (That path uses the
+ * library handle of the calling thread's current device: `stream` must belong
+ * to it.)
  *     y[m][n] = bf16_rne( sum_k x[m][k] * w[n][k] )
  * Otherwise every weight is dequantised inside the kernel (the weights are
  * never written to memory) as bf16_rne(fp32(alpha * v + beta)), v the table value
