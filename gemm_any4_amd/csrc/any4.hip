@@ -23,15 +23,18 @@
 // Kernels
 //   k_pack, k_pack2, k_pack3        idx[N][K] u8 -> tiles, one tile slot per thread.
 //   k_dequant, k_dequant2, k_dequant3  w = bf16(fma(alpha, LUT[idx], beta)), one slot
-//                          per thread.
+//                          per thread, rows stored whole through LDS.
 //   k_gemm_st              y = x * W^T for M <= 16 with one to four row blocks
 //                          per CU: the weights stream once, decoded through
 //                          table lookups in LDS into v_mfma_f32_16x16x32_bf16
 //                          operands; K optionally split over workgroups.
+//                          M = 17..48: two or three 16-row slices of x.
 //   k_split_sum            y from the split partial sums, in split order.
-//   k_gemm_km, k_gemm_kb   the same decode for the other M <= 16 shapes (one
-//                          block per CU with K <= 4096, more than four).
-//   k_gemm_big             M > 48: tiles dequantised into LDS, then MFMAs.
+//   k_gemm_km, k_gemm_kb   the same decode for more than four row blocks per CU.
+//   k_gemm_big             M > 48 without a workspace: tiles dequantised into
+//                          LDS, then MFMAs.  From M = 128 with a workspace the
+//                          layer is dequantised into it (k_dequant*) and y is
+//                          one hipBLASLt bf16 GEMM.
 //   k_quantize_w           group scale + weighted k-means, one wave per row
 //                          (k_quantize, one thread per row, for rows of more
 //                          than 1024 groups).
