@@ -2895,7 +2895,12 @@ inline bool st_plan(int M, int N, int K, int g, bool split_ok, StPlan& P)
                         continue;
                     const int cw = r * ((Kc + nw * r - 1) / (nw * r));
                     const int waste = nw * cw - Kc;
-                    const int score = waste * 4096 + (max_waves - nw) * 64 + cw / r;
+                    // x in LDS, one block per group: bodies of a single tile
+                    // (a ring of one tile, no falling priority) measured slow,
+                    // 11.4 against 9.8 us on 4096x14336 at M = 1 for 16 waves x
+                    // 7 one-tile bodies against 14 waves x one 8-tile body
+                    const int one_tile = xl && nbg * r == 1 && cw > 1 ? 2048 : 0;
+                    const int score = waste * 4096 + one_tile + (max_waves - nw) * 64 + cw / r;
                     if (best < 0 || score < best) {
                         best = score;
                         P.nw = nw;
