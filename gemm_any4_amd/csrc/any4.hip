@@ -2784,19 +2784,61 @@ void launch_gemm(const GemmArgs& a, hipStream_t stream)
 }
 
 // ---- k_split_sum: y = bf16(sum over splits of the partial sums) ------------
-// The partial sums of the S workgroups that split K, added in split order
-// (so the result does not depend on which workgroup finished first), then
-// rounded once to bf16.  ws is [S][M][N] fp32.
+// The partial sums of the S <= 4 workgroups that split K, added in split
+// order (so the result does not depend on which workgroup finished first),
+// then rounded once to bf16.  ws is [S][M][N] fp32.  Each thread takes four
+// consecutive outputs and issues the loads of every split before the first
+// add: the partial sums come from other XCDs' writes, so each load is a trip
+// past L2, and S dependent trips cost S latencies.  vec: 16-byte loads and
+// 8-byte stores (mn a multiple of 4, ws 16-byte and y 8-byte aligned).
+constexpr int SPLIT_MAX = 4;
+
 __global__ __launch_bounds__(256) void k_split_sum(const float* __restrict__ ws,
-                                                   uint16_t* __restrict__ y, int S, size_t mn)
+                                                   uint16_t* __restrict__ y, int S, size_t mn,
+                                                   int vec)
 {
-    const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    const size_t i = (static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
     if (i >= mn)
         return;
-    float t = ws[i];
-    for (int s = 1; s < S; ++s)
-        t += ws[static_cast<size_t>(s) * mn + i];
-    y[i] = static_cast<uint16_t>(f32_to_bf16(t));
+    if (vec) {
+        float4 v[SPLIT_MAX] = {};
+#pragma unroll
+        for (int s = 0; s < SPLIT_MAX; ++s)
+            if (s < S)
+                v[s] = *reinterpret_cast<const float4*>(ws + static_cast<size_t>(s) * mn + i);
+        float4 t = v[0];
+#pragma unroll
+        for (int s = 1; s < SPLIT_MAX; ++s)
+            if (s < S) {
+                t.x += v[s].x;
+                t.y += v[s].y;
+                t.z += v[s].z;
+                t.w += v[s].w;
+            }
+        uint2 o;
+        o.x = f32_to_bf16(t.x) | (f32_to_bf16(t.y) << 16);
+        o.y = f32_to_bf16(t.z) | (f32_to_bf16(t.w) << 16);
+        *reinterpret_cast<uint2*>(y + i) = o;
+        return;
+    }
+    const int n = mn - i < 4 ? static_cast<int>(mn - i) : 4;
+    float v[SPLIT_MAX][4] = {};
+#pragma unroll
+    for (int s = 0; s < SPLIT_MAX; ++s)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (s < S && j < n)
+                v[s][j] = ws[static_cast<size_t>(s) * mn + i + j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float t = v[0][j];
+#pragma unroll
+        for (int s = 1; s < SPLIT_MAX; ++s)
+            if (s < S)
+                t += v[s][j];
+        if (j < n)
+            y[i + j] = static_cast<uint16_t>(f32_to_bf16(t));
+    }
 }
 
 // ---- k_gemm_st launch: the shape decides waves, blocks per group and ring --
@@ -3062,8 +3104,10 @@ bool launch_st(const GemmArgs& a, hipStream_t stream, unsigned long long* ts)
     }
     if (P.splits > 1) {
         const size_t mn = static_cast<size_t>(a.M) * a.N;
-        hipLaunchKernelGGL(k_split_sum, dim3(static_cast<unsigned>((mn + 255) / 256)), dim3(256), 0,
-                           stream, a.ws, a.y, P.splits, mn);
+        const int vec = mn % 4 == 0 && (reinterpret_cast<uintptr_t>(a.ws) & 15) == 0 &&
+                        (reinterpret_cast<uintptr_t>(a.y) & 7) == 0;
+        hipLaunchKernelGGL(k_split_sum, dim3(static_cast<unsigned>((mn + 1023) / 1024)), dim3(256),
+                           0, stream, a.ws, a.y, P.splits, mn, vec);
     }
     return true;
 }
