@@ -2849,17 +2849,23 @@ struct StPlan {
 };
 
 // Split K over S workgroups when x, read once per workgroup for all of the
-// workgroup's K, would cost more than the weights: M > 2 (the x loads are
-// full-width whatever M) with one or two row blocks per CU and K of 12288 or
-// more; then each workgroup takes four row blocks over K/S.  Needs a
-// workspace of S*M*N fp32 partial sums.  (Measured at M = 16: 4096x14336
-// 20.4 -> 16.8 us, 8192x28672 45.7 -> 37.4 us; 8192x8192 gained nothing.)
+// workgroup's K, would cost more than the weights: the x rows the kernel
+// loads (M rounded up to the instantiated 1, 2, 4, 8 or 16; the loads are
+// full-width whatever M) times K times 2 bytes against the nb * 16 rows x K
+// half-bytes of its row blocks, i.e. more than 4 * nb x rows, with one or two
+// row blocks per CU and K of 12288 or more; then each workgroup takes four
+// row blocks over K/S.  Needs a workspace of S*M*N fp32 partial sums.
+// (Measured at M = 16: 4096x14336 20.4 -> 16.8 us, 8192x28672 45.7 -> 37.4
+// us; 8192x8192 gained nothing.  At the threshold, split against unsplit:
+// 4096x14336 M = 4 12.9 / 12.4 us, M = 8 13.1 / 15.1; 8192x28672 M = 4
+// 33.6 / 29.2, M = 8 32.9 / 31.9, M = 16 35.4 / 44.7.)
 inline int st_splits(int M, int N, int K)
 {
     const int NB = static_cast<int>(row_blocks(N));
     const int grid = NB < KM_GRID ? NB : KM_GRID;
     const int nb = grid > 0 ? (NB + grid - 1) / grid : 0;
-    if (M <= 2 || nb < 1 || nb > 2 || K / TILE_K < 96 || NB < KM_GRID)
+    const int mt = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+    if (mt <= 4 * nb || nb < 1 || nb > 2 || K / TILE_K < 96 || NB < KM_GRID)
         return 1;
     return 4 / nb;
 }

@@ -128,8 +128,8 @@ def test_traffic_summary_counts_the_split_sum_apart(tmp_path, monkeypatch):
             rows_f.append((name, [100.0 * M]))
             rows_w.append((name, [2.0]))
             if M > 2:
-                rows_f.append(("void (anonymous namespace)::k_split_sum(float const*, unsigned short*, int, unsigned long)", [8.0]))
-                rows_w.append(("void (anonymous namespace)::k_split_sum(float const*, unsigned short*, int, unsigned long)", [4.0]))
+                rows_f.append(("void (anonymous namespace)::k_split_sum(float const*, unsigned short*, int, unsigned long, int)", [8.0]))
+                rows_w.append(("void (anonymous namespace)::k_split_sum(float const*, unsigned short*, int, unsigned long, int)", [4.0]))
     rows_f.append(("__amd_rocclr_copyBuffer", [copy_kib / 2]))
     rows_w.append(("__amd_rocclr_copyBuffer", [copy_kib]))
     _write_csv(tmp_path / "f.csv", "FETCH_SIZE", rows_f)

@@ -602,9 +602,10 @@ def test_inf_in_one_x_row_stays_in_that_row(N, K):
 
 # --------------------------------------------------------------------------
 # K split over workgroups (with a workspace): long K, one or two row blocks
-# per CU, M > 2; partial sums added in split order by a second kernel
+# per CU, more x rows than 4 per row block of a CU (M > 4 with one block,
+# M > 8 with two); partial sums added in split order by a second kernel
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("cfg,M", [(3, 4), (3, 8), (3, 16)])
+@pytest.mark.parametrize("cfg,M", [(3, 5), (3, 8), (3, 16)])
 def test_split_k_config3(cfg, M):
     L = gu.config_layer(cfg)
     need = any4.workspace_size(M, L.N, L.K, L.g)
@@ -621,8 +622,8 @@ def test_split_k_config3(cfg, M):
     print(f"config {cfg} M={M}: split max err/tol {r1:.3e}, unsplit {r0:.3e}", flush=True)
 
 
-@pytest.mark.parametrize("M,N,K,g", [(3, 16 * 256, 12288, 128), (16, 16 * 512, 28672, 128),
-                                     (5, 16 * 300, 16384 + 128, 128), (9, 16 * 256 + 3, 12800, 256)])
+@pytest.mark.parametrize("M,N,K,g", [(5, 16 * 256, 12288, 128), (16, 16 * 512, 28672, 128),
+                                     (11, 16 * 300, 16384 + 128, 128), (9, 16 * 256 + 3, 12800, 256)])
 def test_split_k_ragged(M, N, K, g):
     inp = workloads.generic(M * 19 + N + K, M, N, K, g)
     L = gu.Layer(inp)
@@ -646,6 +647,9 @@ def test_split_k_workspace_errors():
     torch.cuda.synchronize()
     assert torch.count_nonzero(y.float()) == 0
     assert any4.workspace_size(1, L.N, L.K, L.g) == 0       # M <= 2: never split
+    assert any4.workspace_size(4, L.N, L.K, L.g) == 0       # 4 x rows, one block per CU
+    assert any4.workspace_size(8, 8192, 28672, 128) == 0    # 8 x rows, two blocks per CU
+    assert any4.workspace_size(9, 8192, 28672, 128) == 2 * 9 * 8192 * 4
     assert any4.workspace_size(16, 14336, 4096, 128) == 0   # short K: never split
     assert any4.workspace_size(16, 8192, 8192, 128) == 0
 
