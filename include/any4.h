@@ -158,7 +158,10 @@ size_t any4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int64_t g);
  * subnormals), not where a row's other values are needed beside a value
  * 2^39 times larger.  Runs are deterministic (same inputs, same bits): the
  * summation order depends only on the shape (on the prefill path, the
- * library GEMM's order, which this library does not control).
+ * library GEMM's order, which this library does not control: its algorithm
+ * is picked once per shape and process by timing the library's candidates
+ * on the first eager call, so two processes may round differently;
+ * environment ANY4_BLAS_TUNE=0 keeps the library's first choice).
  *   x                         device, [M][K] bf16, read-only.
  *   packed, lut, alpha, beta  device, read-only.
  *   y                         device, [M][N] bf16, written.
