@@ -110,10 +110,12 @@ any4_status any4_dequant(const uint8_t* packed, const uint16_t* lut, const uint1
 /*
  * any4_gemm_workspace_size -- bytes of device workspace with which any4_gemm
  * may split K over several workgroups for this shape, or 0 when it does not
- * split.  It splits for M = 3..16 when the weights give each CU one or two
- * 16-row blocks (N/16 between 256 and 512 on the 256 CUs of an MI355X) and K
- * is at least 12288: then x, which every workgroup reads for its whole K,
- * would cost more than the weights.  The workspace then holds S*M*N fp32
+ * split.  It splits when the weights give each CU one or two 16-row blocks
+ * (N/16 between 256 and 512 on the 256 CUs of an MI355X), K is at least
+ * 12288, and the x rows the kernel loads (M rounded up to 1, 2, 4, 8 or 16)
+ * exceed four per block of a CU (M = 5..16 with one block, M = 9..16 with
+ * two): then x, which every workgroup reads for its whole K, would cost more
+ * than the weights.  The workspace then holds S*M*N fp32
  * partial sums (S = 4 / blocks per CU), added up in a fixed order.  For
  * M >= 128 (prefill) it is N*K*2 bytes: room for the dequantised layer (see
  * any4_gemm).  Other shapes, and invalid ones, give 0.
